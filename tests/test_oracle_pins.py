@@ -1,0 +1,352 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties one oracle step to a closed form, a brute-force enumeration, a
+library routine for a special case, a hand-worked value, an invariant, or a
+figure the pages print (tests/golden/pages_figures.json).  The cases are
+chosen so a plausible slip (dropped term, wrong sign or index, transposed
+operand, swapped W1/W3, missing scale) fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import moe_synth
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_figures.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _route_inputs(T, H, E, seed, scale=0.3):
+    r = _rng(seed)
+    return r.standard_normal((T, H)), r.standard_normal((E, H)) * scale
+
+
+# ----------------------------------------------------------------- router
+def test_softmax_matches_library():
+    x, wg = _route_inputs(50, 16, 12, 1)
+    l = oracle.gate_logits(x, wg)
+    np.testing.assert_allclose(oracle.softmax_rows(l), scipy.special.softmax(l, axis=1), rtol=0, atol=1e-15)
+
+
+def test_gate_is_x_times_wg_transposed():
+    # one-hot gate rows: logits[t, e] = x[t, e] exactly, so the routing is known
+    T, E, H = 9, 5, 7
+    x = _rng(2).standard_normal((T, H))
+    wg = np.zeros((E, H))
+    wg[np.arange(E), np.arange(E)] = 1.0
+    l = oracle.gate_logits(x, wg)
+    np.testing.assert_array_equal(l, x[:, :E])
+    r = oracle.route(x, wg, 2)
+    expect = np.argsort(-x[:, :E], axis=1)[:, :2]
+    np.testing.assert_array_equal(r["ids"], expect)
+
+
+def test_bias_enters_with_plus_sign():
+    E, H, k = 6, 4, 3
+    bias = np.array([0.1, 2.0, -1.0, 1.5, 0.0, 3.0])
+    r = oracle.route(np.zeros((2, H)), _rng(3).standard_normal((E, H)), k, bias)
+    np.testing.assert_array_equal(r["ids"], [[5, 1, 3]] * 2)
+    sel = bias[[5, 1, 3]]
+    np.testing.assert_allclose(r["w"][0], np.exp(sel) / np.exp(sel).sum(), atol=1e-15)
+
+
+def test_selected_weights_sum_to_one():
+    x, wg = _route_inputs(200, 32, 16, 4)
+    for k in (1, 2, 5, 16):
+        r = oracle.route(x, wg, k)
+        np.testing.assert_allclose(r["w"].sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_k2_weight_is_sigmoid_of_logit_gap():
+    x, wg = _route_inputs(100, 24, 8, 5)
+    r = oracle.route(x, wg, 2)
+    l = np.take_along_axis(r["logits"], r["ids"].astype(np.int64), axis=1)
+    np.testing.assert_allclose(r["w"][:, 0], 1.0 / (1.0 + np.exp(l[:, 1] - l[:, 0])), atol=1e-14)
+
+
+def test_weights_are_softmax_of_selected_logits():
+    x, wg = _route_inputs(64, 24, 32, 6)
+    r = oracle.route(x, wg, 6)
+    l = np.take_along_axis(r["logits"], r["ids"].astype(np.int64), axis=1)
+    np.testing.assert_allclose(r["w"], scipy.special.softmax(l, axis=1), atol=1e-14)
+    # p_sel is the full softmax at the selected experts, descending
+    assert np.all(np.diff(r["p_sel"], axis=1) <= 0)
+
+
+def test_topk_brute_force_with_ties():
+    T, H, E, k = 24, 6, 6, 3
+    x, wg = _route_inputs(T, H, E, 7, scale=1.0)
+    x[3] = 0.0                 # exact ties across all experts
+    x[10] = 0.0
+    wg[4] = wg[2]              # experts 2 and 4 always tie
+    r = oracle.route(x, wg, k)
+    p = r["p"]
+    for t in range(T):
+        best, best_key = None, None
+        for sub in itertools.combinations(range(E), k):
+            key = (-sum(p[t, list(sub)]), sub)       # max total p, then lexicographic
+            if best_key is None or key < best_key:
+                best, best_key = sub, key
+        got = list(r["ids"][t])
+        assert sorted(got) == list(best), (t, got, best)
+        pv = p[t, got]
+        assert np.all(np.diff(pv) <= 0)
+        for a in range(k - 1):                          # equal p -> lower id first
+            if pv[a] == pv[a + 1]:
+                assert got[a] < got[a + 1]
+
+
+def test_zero_row_routes_to_first_k_experts():
+    for E, k in ((8, 2), (256, 8), (64, 6)):
+        r = oracle.route(np.zeros((3, 16)), _rng(8).standard_normal((E, 16)), k)
+        np.testing.assert_array_equal(r["ids"], np.tile(np.arange(k), (3, 1)))
+        np.testing.assert_allclose(r["w"], 1.0 / k, atol=1e-15)
+
+
+# ----------------------------------------------------------------- quantisation
+def test_quant_rounding_half_even_and_scale():
+    x = np.array([[2.5, 1.5, 0.5, -0.5, -63.5, 127.0],
+                  [0.0, 0.0, 0.0, 0.0, 0.0, 0.0],
+                  [-254.0, 1.0, 3.0, 0.0, 0.0, 2.0]], dtype=np.float32)
+    q, s = oracle.quant_per_token_int8(x)
+    np.testing.assert_array_equal(q[0], [2, 2, 0, 0, -64, 127])
+    np.testing.assert_array_equal(q[1], 0)
+    assert s[0] == np.float32(1.0) and s[1] == np.float32(1.0) and s[2] == np.float32(2.0)
+    np.testing.assert_array_equal(q[2], [-127, 0, 2, 0, 0, 1])      # 0.5 -> 0, 1.5 -> 2, 1.0 -> 1
+    assert q.dtype == np.int8 and s.dtype == np.float32
+
+
+def test_quant_error_bound_and_range():
+    x = (_rng(9).standard_normal((300, 257)) * _rng(10).uniform(0.01, 30, (300, 1))).astype(np.float32)
+    q, s = oracle.quant_per_token_int8(x)
+    err = np.abs(x.astype(np.float64) - q.astype(np.float64) * s[:, None])
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    np.testing.assert_array_equal(np.abs(q.astype(np.int32)).max(axis=1), 127)
+    assert q.min() >= -127
+
+
+# ----------------------------------------------------------------- align
+def _align_brute(ids, E, C):
+    """The definition, slot by slot: rank = earlier slots on the same expert."""
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    n = len(flat)
+    rank = [sum(1 for s2 in range(s) if flat[s2] == flat[s]) for s in range(n)]
+    counts = [flat.count(e) for e in range(E)]
+    kept = [c if C is None else min(c, C) for c in counts]
+    pos, sorted_slot = [], [-1] * n
+    for s in range(n):
+        if C is not None and rank[s] >= C:
+            pos.append(-1)
+        else:
+            p = sum(kept[:flat[s]]) + rank[s]
+            pos.append(p)
+            sorted_slot[p] = s
+    return counts, kept, pos, sorted_slot, n - sum(kept)
+
+
+@pytest.mark.parametrize("T,E,k,C", [(30, 5, 2, None), (30, 5, 2, 7), (40, 9, 3, 4), (17, 4, 4, 3), (1, 3, 1, None)])
+def test_align_brute_force(T, E, k, C):
+    r = _rng(T * 100 + E)
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    a = oracle.align(ids, E, C)
+    counts, kept, pos, sorted_slot, nd = _align_brute(ids, E, C)
+    np.testing.assert_array_equal(a["counts"], counts)
+    np.testing.assert_array_equal(a["kept"], kept)
+    np.testing.assert_array_equal(a["pos"].reshape(-1), pos)
+    np.testing.assert_array_equal(a["sorted_slot"], sorted_slot)
+    assert a["num_dropped"] == nd
+    assert a["counts"].sum() == T * k
+    assert a["kept"].sum() == T * k - a["num_dropped"]
+    np.testing.assert_array_equal(a["offsets"], np.concatenate([[0], np.cumsum(kept)]))
+
+
+def test_drop_rule_first_come_first_served():
+    # every token routes to experts {0, 1}: exactly the first C tokens are kept
+    T, E, k, C = 50, 4, 2, 13
+    ids = np.tile([0, 1], (T, 1))
+    a = oracle.align(ids, E, C)
+    kept = a["pos"] >= 0
+    np.testing.assert_array_equal(kept[:, 0], np.arange(T) < C)
+    np.testing.assert_array_equal(kept[:, 1], np.arange(T) < C)
+    np.testing.assert_array_equal(a["pos"][:C, 0], np.arange(C))
+    np.testing.assert_array_equal(a["pos"][:C, 1], C + np.arange(C))
+    assert a["num_dropped"] == 2 * (T - C)
+
+
+def test_kept_counts_invariant_under_token_permutation():
+    T, E, k = 300, 16, 4
+    r = _rng(11)
+    ids = np.stack([r.permutation(E)[:k] for _ in range(T)])
+    C = oracle.capacity(T, k, E, 0.8)
+    a = oracle.align(ids, E, C)
+    b = oracle.align(ids[r.permutation(T)], E, C)
+    np.testing.assert_array_equal(a["kept"], b["kept"])
+    assert a["num_dropped"] == b["num_dropped"] > 0
+
+
+def test_capacity_closed_forms():
+    assert oracle.capacity(4096, 8, 256, 1.25) == 160
+    assert oracle.capacity(16384, 6, 64, 1.25) == 1920
+    assert oracle.capacity(10, 3, 4, 1.25) == 10          # 9.375 rounds up
+    assert oracle.capacity(64, 2, 8, 0.0) is None
+
+
+def test_tiles_cover_rows():
+    offsets = np.array([0, 0, 5, 5, 300, 301])
+    t = oracle.tiles(offsets, 128)
+    assert t == [(1, 0, 5), (3, 5, 128), (3, 133, 128), (3, 261, 39), (4, 300, 1)]
+
+
+# ----------------------------------------------------------------- FFN / combine
+def test_swiglu_hand_worked():
+    a = np.array([[1.0, 2.0]])
+    out = oracle.swiglu_ffn(a, np.array([[1.0, 0.0]]), np.array([[0.0, 1.0]]), np.array([[1.0], [-1.0]]))
+    h = 2.0 / (1.0 + math.exp(-1.0))          # silu(1) * 2
+    np.testing.assert_allclose(out, [[h, -h]], atol=1e-15)
+
+
+def test_swiglu_gate_and_up_roles():
+    r = _rng(12)
+    a = np.abs(r.standard_normal((4, 8))) + 0.1
+    w3 = r.standard_normal((5, 8))
+    w2 = r.standard_normal((8, 5))
+    w1_neg = -np.ones((5, 8)) * 10.0       # gate far negative: silu ~ 0
+    assert np.abs(oracle.swiglu_ffn(a, w1_neg, w3, w2)).max() < 1e-6
+    w1_pos = np.ones((5, 8)) * 10.0        # gate far positive: silu(g) ~ g
+    ref = ((a @ w1_pos.T) * (a @ w3.T)) @ w2.T
+    np.testing.assert_allclose(oracle.swiglu_ffn(a, w1_pos, w3, w2), ref, rtol=1e-9)
+    z = np.linspace(-5, 5, 11)
+    np.testing.assert_allclose(oracle.silu(-z), oracle.silu(z) - z, atol=1e-14)
+
+
+def _small_inputs(T, H, E, k, I, w_dtype="f32", cap=0.0, seed=77, x_dtype="f32", wg_dtype="f32"):
+    spec = moe_synth.Spec("t", T, H, E, k, I, x_dtype=x_dtype, wg_dtype=wg_dtype, w_dtype=w_dtype,
+                          out_dtype="f32", capacity_factor=cap)
+    return moe_synth.make_inputs(spec, seed, threads=2)
+
+
+def _layer(inp, **kw):
+    s = inp.spec
+    args = dict(x=inp.x, x_dtype=s.x_dtype, wg=inp.wg, wg_dtype=s.wg_dtype, bias=inp.bias, w13=inp.w13,
+                w2=inp.w2, w_dtype=s.w_dtype, k=s.k, capacity_factor=s.capacity_factor, s13=inp.s13, s2=inp.s2)
+    args.update(kw)
+    return args
+
+
+def test_single_expert_is_dense_ffn():
+    inp = _small_inputs(20, 16, 1, 1, 24)
+    out = oracle.layer(**_layer(inp))["out"]
+    x = inp.x.astype(np.float64)
+    w1, w3 = inp.w13[0, :24].astype(np.float64), inp.w13[0, 24:].astype(np.float64)
+    g = np.einsum("th,ih->ti", x, w1)
+    u = np.einsum("th,ih->ti", x, w3)
+    ref = np.einsum("ti,hi->th", g * scipy.special.expit(g) * u, inp.w2[0].astype(np.float64))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_identical_experts_reduce_to_one_ffn():
+    inp = _small_inputs(40, 16, 6, 3, 8)
+    inp.w13[:] = inp.w13[0]
+    inp.w2[:] = inp.w2[0]
+    out = oracle.layer(**_layer(inp))["out"]
+    ref = oracle.swiglu_ffn(inp.x.astype(np.float64), inp.w13[0, :8].astype(np.float64),
+                            inp.w13[0, 8:].astype(np.float64), inp.w2[0].astype(np.float64))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-14)
+
+
+def test_k_equals_e_is_dense_soft_mixture():
+    T, H, E, I = 12, 8, 4, 6
+    inp = _small_inputs(T, H, E, E, I)
+    out = oracle.layer(**_layer(inp))["out"]
+    x = inp.x.astype(np.float64)
+    p = scipy.special.softmax(x @ inp.wg.astype(np.float64).T, axis=1)
+    ref = np.zeros((T, H))
+    for e in range(E):
+        w13 = inp.w13[e].astype(np.float64)
+        ref += p[:, e:e + 1] * oracle.swiglu_ffn(x, w13[:I], w13[I:], inp.w2[e].astype(np.float64))
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("w_dtype,cap", [("f32", 0.0), ("f32", 0.6), ("i8", 0.0), ("i8", 0.7), ("bf16", 1.0)])
+def test_expert_major_equals_token_major(w_dtype, cap):
+    inp = _small_inputs(48, 32, 8, 3, 16, w_dtype=w_dtype, cap=cap,
+                        x_dtype="bf16" if w_dtype != "f32" else "f32")
+    res = oracle.layer(**_layer(inp))
+    if cap > 0:
+        assert res["align"]["num_dropped"] > 0 or cap >= 1.0
+    ref = oracle.layer_token_major(**_layer(inp))
+    np.testing.assert_allclose(res["out"], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_fully_dropped_token_gives_zero_and_no_renormalisation():
+    T, H, E, k, I = 30, 8, 4, 2, 4
+    inp = _small_inputs(T, H, E, k, I)
+    inp.wg[:] = 0.0
+    inp.wg[0, 0] = inp.wg[1, 1] = 1.0
+    inp.x[:, 0] = 5.0 + np.arange(T)          # expert 0 first, expert 1 second for every token
+    inp.x[:, 1] = 4.0 + np.arange(T)
+    inp.x[:, 2:] = 0.0
+    res = oracle.layer(**_layer(inp, capacity_factor=0.5))          # C = ceil(0.5*60/4) = 8
+    assert res["capacity"] == 8
+    np.testing.assert_array_equal(res["out"][8:], 0.0)
+    y0 = oracle.swiglu_ffn(inp.x[:8].astype(np.float64), inp.w13[0, :I].astype(np.float64),
+                           inp.w13[0, I:].astype(np.float64), inp.w2[0].astype(np.float64))
+    y1 = oracle.swiglu_ffn(inp.x[:8].astype(np.float64), inp.w13[1, :I].astype(np.float64),
+                           inp.w13[1, I:].astype(np.float64), inp.w2[1].astype(np.float64))
+    w = res["route"]["w"][:8]
+    np.testing.assert_allclose(res["out"][:8], w[:, :1] * y0 + w[:, 1:] * y1, rtol=1e-12)
+
+
+def test_output_permutation_equivariant_without_drops():
+    inp = _small_inputs(32, 16, 8, 2, 8)
+    perm = _rng(13).permutation(32)
+    a = oracle.layer(**_layer(inp))["out"]
+    b = oracle.layer(**_layer(inp, x=inp.x[perm]))["out"]
+    np.testing.assert_allclose(b, a[perm], rtol=1e-13, atol=1e-15)
+
+
+# ----------------------------------------------------------------- W8A8
+def test_w8a8_integer_products_exact():
+    r = _rng(14)
+    a = r.integers(-128, 128, (64, 2048)).astype(np.int8)
+    b = r.integers(-127, 128, (96, 2048)).astype(np.int8)
+    exact = a.astype(np.int64) @ b.astype(np.int64).T
+    np.testing.assert_array_equal((a.astype(np.float64) @ b.astype(np.float64).T).astype(np.int64), exact)
+
+
+def test_w8a8_close_to_dequantised_fp64_layer():
+    T, H, E, k, I = 64, 64, 4, 2, 32
+    inp = _small_inputs(T, H, E, k, I, w_dtype="i8", x_dtype="bf16")
+    q = oracle.layer(**_layer(inp))["out"]
+    w13 = (inp.w13.astype(np.float64) * inp.s13[:, :, None]).astype(np.float32)
+    w2 = (inp.w2.astype(np.float64) * inp.s2[:, :, None]).astype(np.float32)
+    ref = oracle.layer(**_layer(inp, w13=w13, w2=w2, w_dtype="f32", s13=None, s2=None))["out"]
+    rel = np.linalg.norm(q - ref) / np.linalg.norm(ref)
+    assert 1e-4 < rel < 2e-2, rel
+
+
+# ----------------------------------------------------------------- the pages' figures
+def test_pages_figures():
+    g = json.load(open(GOLDEN))
+    d = g["dispatch_volume"]
+    ids = np.stack([np.arange(d["top_k"]) + (t % 32) * 8 for t in range(d["tokens"])])
+    a = oracle.align(ids, d["num_experts"], None)
+    n_rows = int(a["offsets"][-1])
+    assert n_rows == d["expert_accesses"] == d["tokens"] * d["top_k"]
+    assert d["hidden"] * 2 == d["bytes_per_row"]
+    assert n_rows * d["bytes_per_row"] == d["total_bytes_approx"]
+    r = g["router_params"]
+    assert abs(r["hidden"] * r["num_experts"] - r["params_approx"]) / r["params_approx"] < 0.05
+    h = g["unfused_hbm_passes"]
+    assert sum(v[0] for k, v in h.items() if isinstance(v, list)) == h["total_reads"]
+    assert sum(v[1] for k, v in h.items() if isinstance(v, list)) == h["total_writes"]
+    assert oracle.capacity(4096, 8, 256, g["capacity_factor"]["factor"]) == 160
