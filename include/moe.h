@@ -1,0 +1,223 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE layer hot path.
+ *
+ * The layer that follows attention in a Mixture-of-Experts transformer, in the
+ * five steps of the MoE FlashAttention page (http://www.framerc.cn/news/2508843/,
+ * section "FlashAttention 在 MoE 模型里的位置"): the attention output is given;
+ * each token is routed to its top-k experts, tokens are grouped by expert, each
+ * expert runs its FFN on its own tokens, and the expert outputs are merged
+ * weighted by the route weights.
+ *
+ * Page references used below:
+ *   [FA-MoE]  http://www.framerc.cn/news/2508843/  (MoE layer, fusions, fused call)
+ *   [Router]  https://2048ai.net/6a1268d0662f9a54cb76af71.html  (router, dispatch, capacity)
+ *   [LightOP] https://adg.csdn.net/6a3a2e8f10ee7a33f281154b.html (fused gate/top-k,
+ *             MoE Align, MoE Sum, W8A8)
+ *
+ * Conventions for every entry point
+ *   - Memory: every pointer argument is DEVICE memory owned by the caller
+ *     unless stated otherwise.  The library never allocates or frees device
+ *     memory; scratch comes from a caller-provided workspace whose minimum
+ *     size the matching *_workspace_size() returns (workspace pointers must be
+ *     256-byte aligned; tensor pointers 16-byte aligned).
+ *   - Layout: row-major, densely packed; bf16 is the IEEE bfloat16 bit pattern.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  Calls
+ *     enqueue kernels and return at once; they never synchronise the device and
+ *     never copy device data to the host.  Kernel faults surface at the
+ *     caller's next synchronisation, as usual in HIP.
+ *   - Errors: every call returns a moe_status and throws nothing.  Argument
+ *     checks run on the host before any launch, so an error return means
+ *     nothing was enqueued.  moe_last_error() gives a thread-local message.
+ *     An unsupported shape or dtype is an error, never a slower fallback.
+ *   - T == 0 is a valid no-op returning MOE_OK.
+ *   - Values: NaN/Inf inputs are not supported and not checked.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, negative size, k < 1, k > E, ... */
+  MOE_ERR_UNSUPPORTED = 2, /* dtype combination or shape the kernels do not implement */
+  MOE_ERR_WORKSPACE = 3,   /* workspace too small or misaligned */
+  MOE_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_I8 = 2
+} moe_dtype;
+
+/* Limits shared by all entry points: 1 <= E <= 256, 1 <= k <= min(E, 8),
+ * H % 64 == 0, I % 64 == 0, T * k < 2^31. */
+
+/* ---------------------------------------------------------------- route --
+ * Gate, softmax, top-k and renormalisation in one pass over x
+ * ([Router] section on the router as a small network; [LightOP] section 3.1,
+ * fused gate + softmax + top-k), optionally with the per-token int8
+ * quantisation of x ([LightOP] section 4.1, per-token int8 quantisation).
+ *
+ *   x        [T, H]  x_dtype (MOE_F32 or MOE_BF16): attention output
+ *   wg       [E, H]  wg_dtype (MOE_F32 or MOE_BF16): gate weight (Linear(H, E))
+ *   bias     [E] fp32 or NULL: added to the logits before the softmax
+ *   topk_ids [T, k] int32 out: expert ids, most probable first; equal
+ *            probabilities go to the lower id
+ *   topk_w   [T, k] fp32 out: selected probabilities divided by their sum
+ *   topk_p   [T, k] fp32 out or NULL: selected softmax probabilities
+ *   xq, xs   [T, H] int8 and [T] fp32 out, both or neither: per-token codes
+ *            round-half-even(x / s) clamped to [-128, 127] with
+ *            s = absmax(x row) / 127 (1 for an all-zero row); fp32 IEEE
+ *            arithmetic, bit-exact to that definition
+ * Logits, the softmax and the selection are fp32.  Supported: E <= 16 with
+ * any x/wg dtype; 16 < E <= 256 (E % 16 == 0) with bf16 x and bf16 wg.
+ */
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k);
+moe_status moe_route(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                     const float* bias, int64_t T, int32_t H, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_w, float* topk_p, int8_t* xq, float* xs,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------- capacity -----
+ * Per-expert capacity C = ceil(factor * T * k / E) ([Router] section on
+ * communication/computation overlap, capacity limit, with the load counted as
+ * the T*k assignments).  factor <= 0 means no limit and returns 0.
+ * factor = 1.25 is evaluated exactly as ceil(5*T*k / (4*E)).  Host only.
+ */
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor);
+
+/* ------------------------------------------------------------- align -----
+ * Group the T*k (token, choice) assignments by expert: per-expert histogram,
+ * capacity cut, exclusive prefix sum, expert-sorted slot list and the GEMM
+ * row-tile list ([Router] section on token dispatch, counting per
+ * destination; [LightOP] section 3.2, MoE Align: prefix sum, hierarchical
+ * atomics, fused map/mask/fill).
+ *
+ * Slot s = t*k + j is token t's j-th choice.  rank(s) = number of slots
+ * before s (in slot order) routed to the same expert.  s is kept iff
+ * capacity <= 0 or rank(s) < capacity; dropped slots take the residual path.
+ *   topk_ids    [T, k] int32 in, each in [0, E) (an id outside is dropped)
+ *   counts      [E] int32 out: assignments per expert before the cut
+ *   offsets     [E+1] int32 out: exclusive prefix sum of min(counts, C);
+ *               offsets[E] = N = kept assignments
+ *   sorted_slot [T*k] int32 out: sorted_slot[offsets[e] + rank] = slot for
+ *               kept slots, in slot order within each expert; -1 at [N, T*k)
+ *   pos         [T*k] int32 out: sorted row of each slot, -1 if dropped
+ *   tiles       [moe_align_max_tiles(...)][4] int32 out: (expert, first
+ *               sorted row, row count, 0) for row tiles of at most block_m
+ *               rows, one expert each, in expert order; unused entries are
+ *               (-1, 0, 0, 0)
+ *   num_tiles   [1] int32 out;  num_dropped [1] int32 out: T*k - N
+ * Every output is deterministic and bit-exact to that definition.
+ * block_m in {16, 32, 64, 128, 256}.
+ */
+size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E);
+int64_t moe_align_max_tiles(int64_t T, int32_t k, int32_t E, int32_t block_m);
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
+                     int64_t capacity, int32_t block_m, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_slot, int32_t* pos, int32_t* tiles, int32_t* num_tiles,
+                     int32_t* num_dropped, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ---------------------------------------------------------- expert FFN ---
+ * Per-expert SwiGLU on the expert-sorted rows as a grouped GEMM pair
+ * ([FA-MoE] step 4 and its fused call with stacked expert weights and
+ * activation "silu"; [LightOP] sections 4.1 and 4.3, W16A16 and W8A8 MoE):
+ *   for sorted row r of expert e with slot s = sorted_slot[r], t = s / k:
+ *     h[r]  = silu(W1[e] a_t) * (W3[e] a_t),    silu(z) = z / (1 + exp(-z))
+ *     Y[r]  = w * (W2[e] h[r]),  w = topk_w[s] (1 if topk_w is NULL)
+ *   act_dtype MOE_F32 / MOE_BF16: a_t = x[t] (w_dtype must equal act_dtype)
+ *   act_dtype MOE_I8 (W8A8, w_dtype MOE_I8): a_t = xq[t] with scale xs[t];
+ *     int32 accumulation, dequantised by xs[t] * s13[e][n]; h is quantised
+ *     per row with the per-token rule before the second GEMM, whose int32
+ *     result is scaled by that row scale * s2[e][n]  ([LightOP] section 4.1)
+ *   x        [T, H] act_dtype;  xs [T] fp32 (MOE_I8 only, else NULL)
+ *   w13      [E, 2I, H] w_dtype: rows 0..I-1 are W1[e], rows I..2I-1 W3[e]
+ *   w2       [E, H, I] w_dtype
+ *   s13, s2  [E, 2I], [E, H] fp32 per-output-channel scales (MOE_I8 only)
+ *   sorted_slot, tiles, num_tiles: from moe_align with the same block_m;
+ *   block_m must equal moe_ffn_block_m() for this shape
+ *   y_sorted [T*k, H] y_dtype out (MOE_F32 for f32 activations, else
+ *            MOE_BF16): rows >= N are not written
+ */
+int32_t moe_ffn_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype);
+size_t moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                              int32_t w_dtype);
+moe_status moe_expert_ffn(const void* x, int32_t act_dtype, const float* xs, const void* w13,
+                          const void* w2, int32_t w_dtype, const float* s13, const float* s2,
+                          const int32_t* sorted_slot, const int32_t* tiles,
+                          const int32_t* num_tiles, int32_t block_m, const float* topk_w,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted,
+                          int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------ combine ----
+ * Route-weighted merge of each token's kept expert rows ([FA-MoE] step 5 and
+ * its fusion of weighting into accumulation; [LightOP] section 3.2, MoE Sum):
+ *   out[t] = sum over j with pos[t*k+j] >= 0 of  w * y_sorted[pos[t*k+j]]
+ *   w = topk_w[t*k+j], or 1 when topk_w is NULL (rows already weighted)
+ * A token with every slot dropped gets 0.  fp32 accumulation in slot order.
+ *   y_sorted [*, H] y_dtype (MOE_F32 / MOE_BF16);  out [T, H] out_dtype.
+ */
+moe_status moe_combine(const void* y_sorted, int32_t y_dtype, const int32_t* pos,
+                       const float* topk_w, int64_t T, int32_t k, int32_t H, void* out,
+                       int32_t out_dtype, void* stream);
+
+/* -------------------------------------------------------------- layer ----
+ * The whole MoE branch (route, align, expert FFN, combine) enqueued on one
+ * stream with no host synchronisation ([FA-MoE] fused MoE call: attention
+ * output, router weight, stacked expert weights, expert count, top-k, silu).
+ *   x [T, H] (MOE_F32 or MOE_BF16), wg [E, H], bias [E] or NULL,
+ *   w13/w2/s13/s2 as in moe_expert_ffn, capacity as in moe_align
+ *   (<= 0: none), out [T, H] with out_dtype == x_dtype.
+ *   w_dtype MOE_I8 quantises x per token inside the route step (W8A8).
+ * aux (host struct, may be NULL; each member may be NULL) names device
+ * buffers the layer writes its intermediates to instead of the workspace:
+ * topk_ids/topk_w/topk_p [T,k], counts [E], offsets [E+1], sorted_slot and
+ * pos [T*k], num_dropped [1], xq [T,H] int8 and xs [T] (W8A8 only).
+ * The layer returns the MoE branch only: the caller adds the residual, which
+ * is where dropped assignments go.
+ */
+typedef struct moe_layer_aux {
+  int32_t* topk_ids;
+  float* topk_w;
+  float* topk_p;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_slot;
+  int32_t* pos;
+  int32_t* num_dropped;
+  int8_t* xq;
+  float* xs;
+} moe_layer_aux;
+
+size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                int32_t x_dtype, int32_t w_dtype);
+moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                     const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                     const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                     int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                     const moe_layer_aux* aux, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------- diagnostics -----
+ * moe_last_error: message of this thread's last failed call ("" if none).
+ * moe_last_dispatch: kernel variants this thread's last successful call
+ * enqueued (never a silent fallback: an unsupported case is an error).
+ * Both return thread-local storage valid until the thread's next call.
+ */
+const char* moe_last_error(void);
+const char* moe_last_dispatch(void);
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

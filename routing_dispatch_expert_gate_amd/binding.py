@@ -1,0 +1,224 @@
+"""ctypes binding of ``libmoe.so`` (argument marshalling only).
+
+Every function here passes device pointers, sizes and the current HIP stream
+to the C ABI declared in ``include/moe.h``; all computation happens in the
+HIP kernels.  PyTorch provides device memory (outputs and workspaces) and the
+stream.  A missing library raises at import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8}
+
+_vp, _i32, _i64, _sz, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+_st = ctypes.c_int
+
+# name -> (restype, argtypes); the same names and order as include/moe.h
+SIGNATURES = {
+    "moe_route_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_route": (_st, [_vp, _i32, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                        _vp, _sz, _vp]),
+    "moe_capacity": (_i64, [_i64, _i32, _i32, _f64]),
+    "moe_align_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "moe_align_max_tiles": (_i64, [_i64, _i32, _i32, _i32]),
+    "moe_align": (_st, [_vp, _i64, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                        _sz, _vp]),
+    "moe_ffn_block_m": (_i32, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "moe_ffn_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn": (_st, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                             _i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
+    "moe_layer_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_layer": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
+                        _i32, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_last_dispatch": (ctypes.c_char_p, []),
+    "moe_version": (ctypes.c_char_p, []),
+}
+
+
+class MoeLayerAux(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("topk_ids", "topk_w", "topk_p", "counts", "offsets", "sorted_slot",
+                                   "pos", "num_dropped", "xq", "xs")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"moe status {status}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run routing_dispatch_expert_gate_amd.build.build() "
+                          "(hipcc, gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, lib.moe_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ws(nbytes: int, device) -> torch.Tensor | None:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device) if nbytes else None
+
+
+def last_dispatch() -> str:
+    return lib.moe_last_dispatch().decode()
+
+
+def version() -> str:
+    return lib.moe_version().decode()
+
+
+def capacity(T: int, k: int, E: int, factor: float) -> int:
+    return int(lib.moe_capacity(T, k, E, float(factor)))
+
+
+def route(x: torch.Tensor, wg: torch.Tensor, k: int, bias: torch.Tensor | None = None,
+          want_p: bool = True, quant: bool = False) -> dict:
+    """moe_route: returns ids [T,k] int32, w [T,k] fp32, p [T,k] fp32 (or None),
+    and xq [T,H] int8 / xs [T] fp32 when ``quant``."""
+    _dev(x, "x"), _dev(wg, "wg")
+    T, H = x.shape
+    E = wg.shape[0]
+    dev = x.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = torch.empty((T, k), dtype=torch.float32, device=dev) if want_p else None
+    xq = torch.empty((T, H), dtype=torch.int8, device=dev) if quant else None
+    xs = torch.empty((T,), dtype=torch.float32, device=dev) if quant else None
+    if bias is not None:
+        _dev(bias, "bias")
+    nws = lib.moe_route_workspace_size(T, H, E, k)
+    ws = _ws(nws, dev)
+    _check(lib.moe_route(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), T, H, E, k, _p(ids),
+                         _p(w), _p(p), _p(xq), _p(xs), _p(ws), nws, _stream(dev)))
+    return {"ids": ids, "w": w, "p": p, "xq": xq, "xs": xs}
+
+
+def align(ids: torch.Tensor, E: int, capacity: int = 0, block_m: int = 128) -> dict:
+    """moe_align on device ids [T,k]."""
+    _dev(ids, "ids")
+    T, k = ids.shape
+    dev = ids.device
+    n = T * k
+    mt = int(lib.moe_align_max_tiles(T, k, E, block_m))
+    out = {
+        "counts": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "sorted_slot": torch.empty(n, dtype=torch.int32, device=dev),
+        "pos": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "tiles": torch.empty((max(mt, 1), 4), dtype=torch.int32, device=dev),
+        "num_tiles": torch.empty(1, dtype=torch.int32, device=dev),
+        "num_dropped": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    nws = lib.moe_align_workspace_size(T, k, E)
+    ws = _ws(nws, dev)
+    _check(lib.moe_align(_p(ids), T, k, E, int(capacity), block_m, _p(out["counts"]), _p(out["offsets"]),
+                         _p(out["sorted_slot"]), _p(out["pos"]), _p(out["tiles"]), _p(out["num_tiles"]),
+                         _p(out["num_dropped"]), _p(ws), nws, _stream(dev)))
+    return out
+
+
+def ffn_block_m(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype) -> int:
+    return int(lib.moe_ffn_block_m(T, H, I, E, k, _DT[w_dtype]))
+
+
+def expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, sorted_slot: torch.Tensor,
+               tiles: torch.Tensor, num_tiles: torch.Tensor, block_m: int, k: int,
+               topk_w: torch.Tensor | None = None, xs: torch.Tensor | None = None,
+               s13: torch.Tensor | None = None, s2: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_expert_ffn: returns y_sorted [T*k, H] (rows >= N unwritten)."""
+    for t, nme in ((x, "x"), (w13, "w13"), (w2, "w2"), (sorted_slot, "sorted_slot"), (tiles, "tiles")):
+        _dev(t, nme)
+    T, H = x.shape
+    E, I = w2.shape[0], w2.shape[2]
+    dev = x.device
+    ydt = torch.float32 if w13.dtype == torch.float32 else torch.bfloat16
+    y = torch.empty((T * k, H), dtype=ydt, device=dev)
+    nws = lib.moe_ffn_workspace_size(T, H, I, E, k, _DT[w13.dtype])
+    ws = _ws(nws, dev)
+    _check(lib.moe_expert_ffn(_p(x), _DT[x.dtype], _p(xs), _p(w13), _p(w2), _DT[w13.dtype], _p(s13), _p(s2),
+                              _p(sorted_slot), _p(tiles), _p(num_tiles), block_m, _p(topk_w), T, H, I, E, k,
+                              _p(y), _DT[ydt], _p(ws), nws, _stream(dev)))
+    return y
+
+
+def combine(y_sorted: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor | None, T: int, k: int,
+            out_dtype: torch.dtype) -> torch.Tensor:
+    """moe_combine: out [T, H]."""
+    _dev(y_sorted, "y_sorted"), _dev(pos, "pos")
+    H = y_sorted.shape[1]
+    out = torch.empty((T, H), dtype=out_dtype, device=y_sorted.device)
+    _check(lib.moe_combine(_p(y_sorted), _DT[y_sorted.dtype], _p(pos), _p(topk_w), T, k, H, _p(out),
+                           _DT[out_dtype], _stream(y_sorted.device)))
+    return out
+
+
+class Layer:
+    """moe_layer with a workspace allocated once and re-used across calls."""
+
+    def __init__(self, T: int, H: int, I: int, E: int, k: int, x_dtype: torch.dtype,
+                 w_dtype: torch.dtype, device="cuda"):
+        self.shape = (T, H, I, E, k)
+        self.x_dtype, self.w_dtype = x_dtype, w_dtype
+        self.nws = lib.moe_layer_workspace_size(T, H, I, E, k, _DT[x_dtype], _DT[w_dtype])
+        self.ws = _ws(self.nws, device)
+
+    def __call__(self, x, wg, w13, w2, capacity=0, bias=None, s13=None, s2=None, out=None, aux=None):
+        T, H, I, E, k = self.shape
+        if out is None:
+            out = torch.empty((T, H), dtype=x.dtype, device=x.device)
+        aux_s = None
+        if aux is not None:
+            aux_s = MoeLayerAux(**{n: (aux[n].data_ptr() if aux.get(n) is not None else None)
+                                   for n, _ in MoeLayerAux._fields_})
+        _check(lib.moe_layer(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), _p(w13), _p(w2),
+                             _DT[w13.dtype], _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out),
+                             _DT[out.dtype], ctypes.byref(aux_s) if aux_s is not None else None,
+                             _p(self.ws), self.nws, _stream(x.device)))
+        return out
+
+
+def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None):
+    """One moe_layer call (allocates its workspace); ``aux`` maps moe_layer_aux
+    member names to device tensors that receive the intermediates."""
+    T, H = x.shape
+    E, I = w2.shape[0], w2.shape[2]
+    return Layer(T, H, I, E, k, x.dtype, w13.dtype, x.device)(x, wg, w13, w2, capacity, bias, s13, s2,
+                                                             aux=aux)

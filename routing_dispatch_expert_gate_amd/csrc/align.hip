@@ -1,0 +1,194 @@
+// Align / dispatch: group the T*k (token, choice) slots by expert.
+//
+// Definition (MoE Router page, 2048ai.net: the token-dispatch section counts
+// assignments per destination; the overlap section caps each expert at C and
+// sends the excess to the residual path): rank(s) = number of earlier slots
+// routed to the same expert; slot s is kept iff rank(s) < C; the kept slots of
+// expert e occupy sorted rows offsets[e] .. offsets[e+1)-1 in slot order.
+//
+// Technique (LightOP page, section 3.2, MoE Align: parallel prefix sum,
+// hierarchical atomics, fused map/mask/fill), three launches and no host sync:
+//   1. align_hist: each block histograms a contiguous slot range in LDS
+//      (LDS atomics only; the counts do not depend on their order).
+//   2. align_scan: one block turns the block histograms into per-block
+//      exclusive bases (column scan), applies the capacity, scans the kept
+//      counts into offsets, and writes the GEMM row-tile list.
+//   3. align_scatter: each block re-reads its range; four waves take
+//      contiguous quarters, count per wave (LDS atomics), scan over waves, and
+//      then rank their slots 64 at a time in slot order: the lanes holding
+//      the same expert are found with a ballot loop and ranked by popcount of
+//      the lower lanes.  Ranks therefore come from an ordered scan, never from
+//      the order atomics return in, so every output is deterministic.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kAlignThreads = 256;
+
+__global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t* __restrict__ ids,
+                                                                 int64_t n, int E, int spb,
+                                                                 int32_t* __restrict__ bhist) {
+  __shared__ int32_t h[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kAlignThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * spb;
+  const int64_t s1 = s0 + spb < n ? s0 + spb : n;
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += kAlignThreads) {
+    const int e = ids[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kAlignThreads) bhist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Exclusive scan of one value per thread over the 256-thread block.
+__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < kAlignThreads; o <<= 1) {
+    const int add = tid >= o ? tmp[tid - o] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int incl = tmp[tid];
+  *total = tmp[kAlignThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
+    int32_t* __restrict__ bhist, int nb, int E, int64_t n, int64_t cap, int bm, int64_t max_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles, int32_t* __restrict__ num_dropped) {
+  __shared__ int tmp[kAlignThreads];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int v = bhist[(size_t)b * E + e];
+      bhist[(size_t)b * E + e] = total;
+      total += v;
+    }
+    counts[e] = total;
+  }
+  const int kept = e < E ? (cap > 0 && total > cap ? (int)cap : total) : 0;
+  const int ntile = (kept + bm - 1) / bm;
+  int n_kept = 0, n_tiles = 0;
+  const int off = block_exclusive_scan(kept, tmp, &n_kept);
+  const int tbase = block_exclusive_scan(ntile, tmp, &n_tiles);
+  if (e < E) offsets[e] = off;
+  if (e == 0) {
+    offsets[E] = n_kept;
+    *num_dropped = (int32_t)(n - n_kept);
+    *num_tiles = n_tiles;
+  }
+  for (int i = 0; i < ntile; ++i) {
+    const int rows = kept - i * bm < bm ? kept - i * bm : bm;
+    *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tbase + i)) = make_int4(e, off + i * bm, rows, 0);
+  }
+  for (int64_t q = n_tiles + e; q < max_tiles; q += kAlignThreads)
+    *reinterpret_cast<int4*>(tiles + 4 * q) = make_int4(-1, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int spb, const int32_t* __restrict__ bbase,
+    const int32_t* __restrict__ offsets, int64_t cap, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ pos) {
+  __shared__ int32_t wh[4 * kMaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  for (int i = tid; i < 4 * kMaxE; i += kAlignThreads) wh[i] = 0;
+  __syncthreads();
+
+  const int64_t s0 = (int64_t)blockIdx.x * spb;
+  const int64_t s1 = s0 + spb < n ? s0 + spb : n;
+  const int64_t sub = (((s1 - s0) + 3) / 4 + 63) / 64 * 64;
+  const int64_t w0 = s0 + wv * sub < s1 ? s0 + wv * sub : s1;
+  const int64_t w1 = w0 + sub < s1 ? w0 + sub : s1;
+  int32_t* my = wh + wv * kMaxE;
+
+  for (int64_t s = w0 + lane; s < w1; s += 64) {
+    const int e = ids[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&my[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = bbase[(size_t)blockIdx.x * E + e];
+    for (int q = 0; q < 4; ++q) {
+      const int v = wh[q * kMaxE + e];
+      wh[q * kMaxE + e] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = w0; base < w1; base += 64) {
+    const int64_t s = base + lane;
+    const bool in_range = s < w1;
+    const int e = in_range ? ids[s] : -1;
+    const bool valid = in_range && (unsigned)e < (unsigned)E;   // out-of-range ids are dropped
+    uint64_t active = __ballot(valid);
+    int rank = 0;
+    while (active) {
+      const int leader = __ffsll((unsigned long long)active) - 1;
+      const int ev = __shfl(e, leader, kWave);
+      const uint64_t m = __ballot(valid && e == ev);
+      if (valid && e == ev) rank = my[ev] + __popcll(m & lt);
+      if (lane == leader) my[ev] += __popcll(m);
+      active &= ~m;
+    }
+    if (in_range) {
+      const bool kept = valid && (cap <= 0 || rank < cap);
+      const int p = kept ? offsets[e] + rank : -1;
+      pos[s] = p;
+      if (kept) sorted_slot[p] = (int32_t)s;
+    }
+  }
+
+  // sentinel fill of the unused tail [N, n) of sorted_slot, split over blocks
+  const int64_t N = offsets[E];
+  const int64_t f1 = N + s1 < n ? N + s1 : n;
+  for (int64_t i = N + s0 + tid; i < f1; i += kAlignThreads) sorted_slot[i] = -1;
+}
+
+}  // namespace
+
+int64_t align_max_tiles(int64_t T, int k, int E, int block_m) {
+  const int64_t n = T * k;
+  return (n + block_m - 1) / block_m + (E < n ? E : n);
+}
+
+AlignPlan plan_align(int64_t T, int k, int E) {
+  AlignPlan p;
+  const int64_t n = T * k;
+  p.slots_per_block = 1024;
+  p.nblocks = (int)((n + p.slots_per_block - 1) / p.slots_per_block);
+  if (p.nblocks < 1) p.nblocks = 1;
+  p.ws_bytes = (size_t)p.nblocks * (size_t)E * sizeof(int32_t);
+  return p;
+}
+
+hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k, int E, int64_t cap,
+                        int block_m, int64_t max_tiles, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* pos, int32_t* tiles, int32_t* num_tiles,
+                        int32_t* num_dropped, void* ws, hipStream_t s) {
+  const int64_t n = T * k;
+  int32_t* bhist = (int32_t*)ws;
+  align_hist_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, p.slots_per_block, bhist);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  align_scan_kernel<<<1, kAlignThreads, 0, s>>>(bhist, p.nblocks, E, n, cap, block_m, max_tiles,
+                                                counts, offsets, tiles, num_tiles, num_dropped);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  align_scatter_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, p.slots_per_block, bhist,
+                                                          offsets, cap, sorted_slot, pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

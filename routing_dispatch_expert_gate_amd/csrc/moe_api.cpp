@@ -1,0 +1,414 @@
+// C ABI of the MoE layer hot path: argument validation, workspace carving and
+// kernel dispatch.  Every check runs on the host before the first launch, so
+// an error return means nothing was enqueued; unsupported cases are errors,
+// never a slower path.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local std::string g_dispatch;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+moe_status ok(const std::string& d) {
+  g_err.clear();
+  g_dispatch = d;
+  return MOE_OK;
+}
+
+bool al(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
+bool is_act(int d) { return d == MOE_F32 || d == MOE_BF16; }
+
+// Shape checks shared by every entry point.
+moe_status check_dims(int64_t T, int32_t H, int32_t E, int32_t k) {
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "T must be >= 0 (got %lld)", (long long)T);
+  if (E < 1) return fail(MOE_ERR_INVALID_ARG, "E must be >= 1 (got %d)", E);
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "k must be >= 1 (got %d)", k);
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k (%d) must be <= E (%d)", k, E);
+  if (H < 1) return fail(MOE_ERR_INVALID_ARG, "H must be >= 1 (got %d)", H);
+  if (E > moe::kMaxE) return fail(MOE_ERR_UNSUPPORTED, "E > %d is not supported (got %d)", moe::kMaxE, E);
+  if (k > moe::kMaxK) return fail(MOE_ERR_UNSUPPORTED, "k > %d is not supported (got %d)", moe::kMaxK, k);
+  if (H % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "H must be a multiple of 64 (got %d)", H);
+  if (T * (int64_t)k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T*k must be < 2^31");
+  return MOE_OK;
+}
+
+moe_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL; %zu bytes needed", need);
+  if (!al(ws, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)              \
+  do {                             \
+    moe_status st_ = (expr);       \
+    if (st_ != MOE_OK) return st_; \
+  } while (0)
+
+#define MOE_NONNULL(p)                                                            \
+  do {                                                                            \
+    if (!(p)) return fail(MOE_ERR_INVALID_ARG, "required pointer " #p " is NULL"); \
+  } while (0)
+
+#define MOE_ALIGNED(p, a)                                                              \
+  do {                                                                                 \
+    if ((p) && !al((p), (a)))                                                          \
+      return fail(MOE_ERR_INVALID_ARG, "pointer " #p " must be %d-byte aligned", (int)(a)); \
+  } while (0)
+
+moe_status route_checks(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, int64_t T,
+                        int32_t H, int32_t E, int32_t k, int32_t* ids, float* w, int8_t* xq,
+                        float* xs, moe::RoutePlan* plan) {
+  MOE_TRY(check_dims(T, H, E, k));
+  if (!is_act(x_dtype)) return fail(MOE_ERR_UNSUPPORTED, "x dtype must be MOE_F32 or MOE_BF16");
+  if (!is_act(wg_dtype)) return fail(MOE_ERR_UNSUPPORTED, "wg dtype must be MOE_F32 or MOE_BF16");
+  if ((xq == nullptr) != (xs == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "xq and xs must both be given or both be NULL");
+  *plan = moe::plan_route(T, H, E, k, x_dtype, wg_dtype);
+  if (plan->kind < 0)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "route: E=%d with x/wg dtypes %d/%d and H=%d is not implemented (E<=8 with H<=8192 or "
+                "E<=16 with H<=4096, any dtype; or E%%16==0, E<=256 with bf16 x and bf16 wg)",
+                E, x_dtype, wg_dtype, H);
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(x);
+  MOE_NONNULL(wg);
+  MOE_NONNULL(ids);
+  MOE_NONNULL(w);
+  MOE_ALIGNED(x, 16);
+  MOE_ALIGNED(wg, 16);
+  MOE_ALIGNED(xq, 8);
+  return MOE_OK;
+}
+
+std::string route_name(const moe::RoutePlan& p) {
+  char b[160];
+  if (p.kind == 0)
+    snprintf(b, sizeof b, "route_fma_kernel(tokens/wg=%d,waves=%d)", p.bt, p.nw);
+  else if (p.kind == 1)
+    snprintf(b, sizeof b, "route_mfma_kernel<fused>(tokens/wg=%d)", p.bt);
+  else
+    snprintf(b, sizeof b, "route_mfma_kernel<logits>(tokens/wg=%d,ksplit=%d)+route_topk_kernel", p.bt, p.ks);
+  return b;
+}
+
+moe_status ffn_checks(int32_t act_dtype, int32_t w_dtype, int32_t y_dtype, int64_t T, int32_t H,
+                      int32_t I, int32_t E, int32_t k) {
+  MOE_TRY(check_dims(T, H, E, k));
+  if (I < 1) return fail(MOE_ERR_INVALID_ARG, "I must be >= 1 (got %d)", I);
+  if (I % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "I must be a multiple of 64 (got %d)", I);
+  const bool ok_combo = (act_dtype == MOE_F32 && w_dtype == MOE_F32 && y_dtype == MOE_F32) ||
+                        (act_dtype == MOE_BF16 && w_dtype == MOE_BF16 && y_dtype == MOE_BF16) ||
+                        (act_dtype == MOE_I8 && w_dtype == MOE_I8 && y_dtype == MOE_BF16);
+  if (!ok_combo)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "expert FFN dtypes (act %d, w %d, y %d) not implemented: use f32/f32/f32, "
+                "bf16/bf16/bf16 or i8/i8/bf16",
+                act_dtype, w_dtype, y_dtype);
+  if (w_dtype == MOE_I8 && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "W8A8 needs H and I multiples of 128 (got %d, %d)", H, I);
+  return MOE_OK;
+}
+
+bool valid_block_m(int32_t b) { return b == 16 || b == 32 || b == 64 || b == 128 || b == 256; }
+
+// Layout of the fused layer's workspace.
+struct LayerCarve {
+  size_t ids, w, p, counts, offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, xq, xs, y,
+      scratch, total;
+  moe::RoutePlan rp;
+  moe::AlignPlan ap;
+  moe::FfnPlan fp;
+};
+
+LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t x_dtype,
+                       int32_t wg_dtype, int32_t w_dtype) {
+  LayerCarve c{};
+  const int64_t n = T * k;
+  c.rp = moe::plan_route(T, H, E, k, x_dtype, wg_dtype);
+  c.ap = moe::plan_align(T, k, E);
+  c.fp = moe::plan_ffn(T, H, I, E, k, w_dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += a256(bytes);
+    return o;
+  };
+  c.ids = take(n * 4);
+  c.w = take(n * 4);
+  c.p = take(n * 4);
+  c.counts = take((size_t)E * 4);
+  c.offsets = take((size_t)(E + 1) * 4);
+  c.sorted_slot = take(n * 4);
+  c.pos = take(n * 4);
+  c.tiles = take((size_t)c.fp.max_tiles * 16);
+  c.num_tiles = take(4);
+  c.num_dropped = take(4);
+  c.xq = take(w_dtype == MOE_I8 ? (size_t)T * H : 0);
+  c.xs = take(w_dtype == MOE_I8 ? (size_t)T * 4 : 0);
+  c.y = take(n * (size_t)H * (w_dtype == MOE_F32 ? 4 : 2));
+  size_t scratch = c.rp.ws_bytes;
+  if (c.ap.ws_bytes > scratch) scratch = c.ap.ws_bytes;
+  if (c.fp.ws_bytes > scratch) scratch = c.fp.ws_bytes;
+  c.scratch = take(scratch);
+  c.total = off;
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+const char* moe_last_dispatch(void) { return g_dispatch.c_str(); }
+const char* moe_version(void) { return "moe-gfx950 0.1.0"; }
+
+int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor) {
+  if (!(factor > 0.0) || E < 1 || T < 0 || k < 1) return 0;
+  const int64_t load = T * (int64_t)k;
+  const double f4 = factor * 4.0;
+  if (f4 == (double)(int64_t)f4) {   // quarter steps (1.25 included): exact integer ceil
+    const int64_t num = (int64_t)f4 * load, den = 4 * (int64_t)E;
+    return (num + den - 1) / den;
+  }
+  const long double q = (long double)factor * (long double)load / (long double)E;
+  int64_t c = (int64_t)q;
+  if ((long double)c < q) ++c;
+  return c;
+}
+
+size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k) {
+  return moe::plan_route(T, H, E, k, MOE_BF16, MOE_BF16).ws_bytes;
+}
+
+moe_status moe_route(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                     const float* bias, int64_t T, int32_t H, int32_t E, int32_t k,
+                     int32_t* topk_ids, float* topk_w, float* topk_p, int8_t* xq, float* xs,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  moe::RoutePlan plan;
+  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, topk_ids, topk_w, xq, xs, &plan));
+  if (T == 0) return ok("none (T=0)");
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  hipError_t e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w,
+                                   topk_p, xq, xs, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route launch");
+  return ok(route_name(plan));
+}
+
+size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E) {
+  return moe::plan_align(T, k, E).ws_bytes;
+}
+
+int64_t moe_align_max_tiles(int64_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || block_m < 1) return 0;
+  return moe::align_max_tiles(T, k, E, block_m);
+}
+
+moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int64_t capacity,
+                     int32_t block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                     int32_t* pos, int32_t* tiles, int32_t* num_tiles, int32_t* num_dropped,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(T, 64, E, k));
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_INVALID_ARG, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(topk_ids);
+  MOE_NONNULL(counts);
+  MOE_NONNULL(offsets);
+  MOE_NONNULL(sorted_slot);
+  MOE_NONNULL(pos);
+  MOE_NONNULL(tiles);
+  MOE_NONNULL(num_tiles);
+  MOE_NONNULL(num_dropped);
+  MOE_ALIGNED(tiles, 16);
+  const moe::AlignPlan plan = moe::plan_align(T, k, E);
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  const int64_t mt = moe::align_max_tiles(T, k, E, block_m);
+  hipError_t e = moe::launch_align(plan, topk_ids, T, k, E, capacity, block_m, mt, counts, offsets,
+                                   sorted_slot, pos, tiles, num_tiles, num_dropped, workspace,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_align launch");
+  char b[128];
+  snprintf(b, sizeof b, "align_hist+align_scan+align_scatter(blocks=%d,slots/block=%d)", plan.nblocks,
+           plan.slots_per_block);
+  return ok(b);
+}
+
+int32_t moe_ffn_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_I8) return -1;
+  return moe::plan_ffn(T, H, I, E, k, w_dtype).block_m;
+}
+
+size_t moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_I8) return 0;
+  return moe::plan_ffn(T, H, I, E, k, w_dtype).ws_bytes;
+}
+
+moe_status moe_expert_ffn(const void* x, int32_t act_dtype, const float* xs, const void* w13,
+                          const void* w2, int32_t w_dtype, const float* s13, const float* s2,
+                          const int32_t* sorted_slot, const int32_t* tiles,
+                          const int32_t* num_tiles, int32_t block_m, const float* topk_w,
+                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted,
+                          int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(ffn_checks(act_dtype, w_dtype, y_dtype, T, H, I, E, k));
+  const moe::FfnPlan plan = moe::plan_ffn(T, H, I, E, k, w_dtype);
+  if (block_m != plan.block_m)
+    return fail(MOE_ERR_INVALID_ARG,
+                "block_m %d does not match the FFN tile height %d for this shape "
+                "(use moe_ffn_block_m)",
+                block_m, plan.block_m);
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(x);
+  MOE_NONNULL(w13);
+  MOE_NONNULL(w2);
+  MOE_NONNULL(sorted_slot);
+  MOE_NONNULL(tiles);
+  MOE_NONNULL(num_tiles);
+  MOE_NONNULL(y_sorted);
+  if (w_dtype == MOE_I8) {
+    MOE_NONNULL(xs);
+    MOE_NONNULL(s13);
+    MOE_NONNULL(s2);
+  }
+  MOE_ALIGNED(x, 16);
+  MOE_ALIGNED(w13, 16);
+  MOE_ALIGNED(w2, 16);
+  MOE_ALIGNED(tiles, 16);
+  MOE_ALIGNED(y_sorted, 16);
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  hipError_t e = moe::launch_ffn(plan, x, act_dtype, xs, w13, w2, w_dtype, s13, s2, sorted_slot,
+                                 tiles, num_tiles, topk_w, T, H, I, E, k, y_sorted, workspace,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn launch");
+  return ok(std::string(plan.up_name) + "+" + plan.down_name);
+}
+
+moe_status moe_combine(const void* y_sorted, int32_t y_dtype, const int32_t* pos,
+                       const float* topk_w, int64_t T, int32_t k, int32_t H, void* out,
+                       int32_t out_dtype, void* stream) {
+  MOE_TRY(check_dims(T, H, moe::kMaxE, k));
+  if (!is_act(y_dtype) || !is_act(out_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "combine dtypes must be MOE_F32 or MOE_BF16");
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(y_sorted);
+  MOE_NONNULL(pos);
+  MOE_NONNULL(out);
+  MOE_ALIGNED(y_sorted, 16);
+  MOE_ALIGNED(out, 16);
+  hipError_t e = moe::launch_combine(y_sorted, y_dtype, pos, topk_w, T, k, H, out, out_dtype,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine launch");
+  return ok(topk_w ? "combine_kernel<weighted>" : "combine_kernel<pre-weighted>");
+}
+
+size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                int32_t x_dtype, int32_t w_dtype) {
+  if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return 0;
+  const int32_t wgd = E <= 16 ? x_dtype : MOE_BF16;
+  return carve_layer(T, H, I, E, k, x_dtype, wgd, w_dtype).total;
+}
+
+moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                     const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                     const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                     int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                     const moe_layer_aux* aux, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  if (!is_act(x_dtype)) return fail(MOE_ERR_UNSUPPORTED, "x dtype must be MOE_F32 or MOE_BF16");
+  if (out_dtype != x_dtype) return fail(MOE_ERR_UNSUPPORTED, "out dtype must equal x dtype");
+  int32_t act;
+  if (w_dtype == MOE_F32 && x_dtype == MOE_F32)
+    act = MOE_F32;
+  else if (w_dtype == MOE_BF16 && x_dtype == MOE_BF16)
+    act = MOE_BF16;
+  else if (w_dtype == MOE_I8)
+    act = MOE_I8;
+  else
+    return fail(MOE_ERR_UNSUPPORTED,
+                "layer dtypes (x %d, w %d) not implemented: f32/f32, bf16/bf16 or W8A8 (any x, i8 w)",
+                x_dtype, w_dtype);
+  const int32_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
+  MOE_TRY(ffn_checks(act, w_dtype, ydt, T, H, I, E, k));
+  int8_t dummy_q = 0;
+  float dummy_s = 0.f;
+  moe::RoutePlan rp;
+  MOE_TRY(route_checks(T ? x : nullptr, x_dtype, wg, wg_dtype, T, H, E, k, (int32_t*)&dummy_s,
+                       &dummy_s, act == MOE_I8 ? &dummy_q : nullptr, act == MOE_I8 ? &dummy_s : nullptr,
+                       &rp));
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(w13);
+  MOE_NONNULL(w2);
+  MOE_NONNULL(out);
+  if (w_dtype == MOE_I8) {
+    MOE_NONNULL(s13);
+    MOE_NONNULL(s2);
+  }
+  MOE_ALIGNED(w13, 16);
+  MOE_ALIGNED(w2, 16);
+  MOE_ALIGNED(out, 16);
+  const LayerCarve c = carve_layer(T, H, I, E, k, x_dtype, wg_dtype, w_dtype);
+  MOE_TRY(check_ws(workspace, workspace_bytes, c.total));
+
+  uint8_t* base = (uint8_t*)workspace;
+  auto pick = [&](auto* user, size_t off) {
+    typedef decltype(user) P;
+    return user ? user : (P)(base + off);
+  };
+  const moe_layer_aux none{};
+  const moe_layer_aux& a = aux ? *aux : none;
+  int32_t* ids = pick(a.topk_ids, c.ids);
+  float* w = pick(a.topk_w, c.w);
+  float* p = a.topk_p;
+  int32_t* counts = pick(a.counts, c.counts);
+  int32_t* offsets = pick(a.offsets, c.offsets);
+  int32_t* sorted_slot = pick(a.sorted_slot, c.sorted_slot);
+  int32_t* pos = pick(a.pos, c.pos);
+  int32_t* num_dropped = pick(a.num_dropped, c.num_dropped);
+  int8_t* xq = act == MOE_I8 ? pick(a.xq, c.xq) : nullptr;
+  float* xs = act == MOE_I8 ? pick(a.xs, c.xs) : nullptr;
+  int32_t* tiles = (int32_t*)(base + c.tiles);
+  int32_t* num_tiles = (int32_t*)(base + c.num_tiles);
+  void* y = base + c.y;
+  void* scratch = base + c.scratch;
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq,
+                                   xs, scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
+  e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m,
+                        c.fp.max_tiles, counts, offsets, sorted_slot, pos, tiles, num_tiles,
+                        num_dropped, scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
+  e = moe::launch_ffn(c.fp, act == MOE_I8 ? (const void*)xq : x, act, xs, w13, w2, w_dtype, s13, s2,
+                      sorted_slot, tiles, num_tiles, w, T, H, I, E, k, y, scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer ffn launch");
+  e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
+  return ok(route_name(c.rp) + " | align(blocks=" + std::to_string(c.ap.nblocks) + ") | " +
+            c.fp.up_name + "+" + c.fp.down_name + "(block_m=" + std::to_string(c.fp.block_m) +
+            ") | combine_kernel<pre-weighted>");
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA bf16/int8, 160 KiB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr int kMaxE = 256;
+constexpr int kMaxK = 8;
+
+// ---------------------------------------------------------------- numerics
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// silu(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// 8 consecutive values <-> fp32 registers (16-byte aligned rows)
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(u[i] << 16);
+    v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
+
+// ------------------------------------------------------------- wave utils
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// ------------------------------------------------------------- launchers
+// route.hip
+struct RoutePlan {
+  int kind;      // 0 = fused FMA (E <= 16), 1 = fused MFMA (E <= 64), 2 = MFMA logits + top-k
+  int bt;        // tokens per workgroup
+  int ks;        // K splits (kind 2)
+  int nw;        // waves per workgroup (kind 0)
+  size_t ws_bytes;
+};
+RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype);
+hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
+                        const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
+                        float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s);
+
+// align.hip
+struct AlignPlan {
+  int slots_per_block;
+  int nblocks;
+  size_t ws_bytes;
+};
+AlignPlan plan_align(int64_t T, int k, int E);
+hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k, int E, int64_t cap,
+                        int block_m, int64_t max_tiles, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_slot, int32_t* pos, int32_t* tiles, int32_t* num_tiles,
+                        int32_t* num_dropped, void* ws, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pos, const float* w, int64_t T,
+                          int k, int H, void* out, int out_dtype, hipStream_t s);
+
+// ffn_*.hip
+struct FfnPlan {
+  int block_m;
+  int64_t max_tiles;
+  size_t ws_bytes;   // h (+ row maxima for W8A8)
+  const char* up_name;
+  const char* down_name;
+};
+FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype);
+hipError_t launch_ffn(const FfnPlan& p, const void* x, int act_dtype, const float* xs,
+                      const void* w13, const void* w2, int w_dtype, const float* s13,
+                      const float* s2, const int32_t* sorted_slot, const int32_t* tiles,
+                      const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
+                      int E, int k, void* y, void* ws, hipStream_t s);
+
+int64_t align_max_tiles(int64_t T, int k, int E, int block_m);
+
+}  // namespace moe

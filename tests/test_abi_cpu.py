@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and its host-side validation returns the documented
+status before any launch (every call here fails validation or has T == 0)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16, I8 = 0, 1, 2
+P = ctypes.c_void_p(256)   # a non-null, aligned dummy pointer: never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def moe():
+    lib_path = os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "libmoe.so")
+    if not os.path.exists(lib_path):
+        import __graft_entry__
+        __graft_entry__._build_module().build()
+    import routing_dispatch_expert_gate_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported(moe):
+    names = declared_functions()
+    assert len(names) == 15, names
+    for n in names:
+        assert hasattr(moe.lib, n), n
+        assert n in moe.SIGNATURES, n
+
+
+def test_capacity_and_sizes(moe):
+    L = moe.lib
+    assert L.moe_capacity(4096, 8, 256, 1.25) == 160
+    assert L.moe_capacity(16384, 6, 64, 1.25) == 1920
+    assert L.moe_capacity(10, 3, 4, 1.25) == 10
+    assert L.moe_capacity(64, 2, 8, 0.0) == 0
+    assert L.moe_capacity(7, 1, 3, 1.1) == 3          # ceil(2.566..)
+    assert L.moe_align_max_tiles(4096, 2, 8, 128) == 64 + 8
+    assert L.moe_align_max_tiles(16, 8, 256, 128) == 1 + 128
+    assert L.moe_ffn_block_m(4096, 4096, 14336, 8, 2, BF16) in (16, 32, 64, 128, 256)
+    assert L.moe_ffn_block_m(4096, 4096, 14336, 8, 2, 7) == -1
+    small = L.moe_layer_workspace_size(64, 128, 256, 8, 2, F32, F32)
+    big = L.moe_layer_workspace_size(4096, 4096, 14336, 8, 2, BF16, BF16)
+    assert 0 < small < big
+    assert big >= 4096 * 2 * 4096 * 2        # the expert-sorted output rows at least
+    assert L.moe_route_workspace_size(4096, 4096, 256, 8) == 4096 * 256 * 4
+    assert L.moe_route_workspace_size(4096, 4096, 8, 2) == 0
+
+
+def _route(moe, **kw):
+    a = dict(x=P, xd=BF16, wg=P, wd=BF16, bias=None, T=64, H=128, E=8, k=2, ids=P, w=P, p=None,
+             xq=None, xs=None, ws=None, nws=0)
+    a.update(kw)
+    return moe.lib.moe_route(a["x"], a["xd"], a["wg"], a["wd"], a["bias"], a["T"], a["H"], a["E"], a["k"],
+                             a["ids"], a["w"], a["p"], a["xq"], a["xs"], a["ws"], a["nws"], None)
+
+
+def test_route_validation(moe):
+    msg = lambda: moe.lib.moe_last_error().decode()   # noqa: E731
+    assert _route(moe, k=9, E=8) == INVALID and "k (9)" in msg()
+    assert _route(moe, k=0) == INVALID
+    assert _route(moe, T=-1) == INVALID
+    assert _route(moe, E=300, k=2) == UNSUPPORTED
+    assert _route(moe, E=16, k=9) == UNSUPPORTED           # k > 8
+    assert _route(moe, H=100) == UNSUPPORTED
+    assert _route(moe, E=24, k=2) == UNSUPPORTED           # E > 16 must be a multiple of 16
+    assert _route(moe, E=64, wd=F32) == UNSUPPORTED        # E > 16 needs bf16 wg
+    assert _route(moe, E=8, H=4096 * 4) == UNSUPPORTED     # beyond the register-resident slice
+    assert _route(moe, x=None) == INVALID and "x" in msg()
+    assert _route(moe, ids=None) == INVALID
+    assert _route(moe, xq=P) == INVALID                    # xq without xs
+    assert _route(moe, xd=I8) == UNSUPPORTED
+    assert _route(moe, x=ctypes.c_void_p(258)) == INVALID  # misaligned
+    assert _route(moe, E=256, k=8, H=512) == WORKSPACE     # logits workspace needed
+    assert _route(moe, E=256, k=8, H=512, ws=ctypes.c_void_p(4096 + 8), nws=1 << 30) == WORKSPACE
+    assert _route(moe, T=0) == OK
+    assert moe.lib.moe_last_dispatch().decode() == "none (T=0)"
+
+
+def test_align_validation(moe):
+    L = moe.lib
+
+    def call(**kw):
+        a = dict(ids=P, T=64, k=2, E=8, C=0, bm=128, out=P, ws=None, nws=0)
+        a.update(kw)
+        o = a["out"]
+        return L.moe_align(a["ids"], a["T"], a["k"], a["E"], a["C"], a["bm"], o, o, o, o, o, o, o,
+                           a["ws"], a["nws"], None)
+
+    assert call(bm=100) == INVALID
+    assert call(k=3, E=2) == INVALID
+    assert call(ids=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call() == WORKSPACE
+    assert call(T=0) == OK
+
+
+def test_ffn_validation(moe):
+    L = moe.lib
+
+    def call(ad=BF16, wd=BF16, yd=BF16, bm=None, T=64, H=128, I=128, E=8, k=2, xs=None, s=None, ws=None, nws=0):
+        if bm is None:
+            bm = L.moe_ffn_block_m(T, H, I, E, k, wd)
+        return L.moe_expert_ffn(P, ad, xs, P, P, wd, s, s, P, P, P, bm, None, T, H, I, E, k, P, yd, ws, nws,
+                                None)
+
+    assert call(ad=F32, wd=BF16) == UNSUPPORTED
+    assert call(yd=F32) == UNSUPPORTED
+    assert call(I=96) == UNSUPPORTED
+    assert call(ad=I8, wd=I8, H=192, xs=P, s=P) == UNSUPPORTED     # W8A8 needs multiples of 128
+    assert call(ad=I8, wd=I8, xs=None, s=P) == INVALID
+    assert call(bm=64 if L.moe_ffn_block_m(64, 128, 128, 8, 2, BF16) != 64 else 32) == INVALID
+    assert call() == WORKSPACE
+    assert call(T=0) == OK
+
+
+def test_combine_and_layer_validation(moe):
+    L = moe.lib
+    assert L.moe_combine(P, I8, P, None, 64, 2, 128, P, BF16, None) == UNSUPPORTED
+    assert L.moe_combine(None, BF16, P, None, 64, 2, 128, P, BF16, None) == INVALID
+    assert L.moe_combine(P, BF16, P, None, 0, 2, 128, P, BF16, None) == OK
+
+    def layer(xd=BF16, wd=BF16, od=BF16, T=64, H=128, I=128, E=8, k=2, ws=None, nws=0, s=None):
+        return L.moe_layer(P, xd, P, BF16, None, P, P, wd, s, s, T, H, I, E, k, 0, P, od, None, ws, nws, None)
+
+    assert layer(od=F32) == UNSUPPORTED
+    assert layer(xd=F32, wd=BF16, od=F32) == UNSUPPORTED
+    assert layer(wd=I8) == INVALID                     # scales missing
+    assert layer() == WORKSPACE
+    assert layer(T=0) == OK
