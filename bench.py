@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path (route -> align -> SwiGLU grouped GEMM
+-> combine) on one MI355X.
+
+A step is one whole-layer call (moe_layer) over one batch of seeded synthetic
+inputs already resident in HBM.  The default workload is the Mixtral-8x7B
+shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  After the K
+timed steps, a staged pass runs the same layer through the per-step entry
+points with HIP events recorded between the launches on the stream the
+library launches on, to get each kernel's average duration; the dominant
+kernel's roofline is computed from those durations and its algorithmic
+flops/bytes.  The CPU oracle is timed on a bounded token sample of the same
+workload on the host cores (a baseline, not the target).
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; grouped-GEMM % MFMA peak; route+combine % HBM BW"
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3}
+RIDGE = {k: v * 1e12 / (PEAK_HBM_GBPS * 1e9) for k, v in PEAK_TFLOPS.items()}   # flop per byte
+CPU_SAMPLE = {1: 64, 2: 1024, 3: 64, 4: 16, 5: 512}
+BYTES = {"f32": 4, "bf16": 2, "i8": 1}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse() -> argparse.Namespace:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, Mixtral-shaped prefill)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+class Staged:
+    """The layer as its separate launches with preallocated buffers, for
+    per-kernel timing with events between launches."""
+
+    def __init__(self, moe, torch, spec, d, C):
+        import ctypes
+        self.moe, self.torch, self.spec, self.d, self.C = moe, torch, spec, d, C
+        L = moe.lib
+        T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
+        n = T * k
+        dev = "cuda"
+        i32, f32 = torch.int32, torch.float32
+        wdt = d["w13"].dtype
+        self.quant = spec.w_dtype == "i8"
+        self.ids = torch.empty((T, k), dtype=i32, device=dev)
+        self.w = torch.empty((T, k), dtype=f32, device=dev)
+        self.xq = torch.empty((T, H), dtype=torch.int8, device=dev) if self.quant else None
+        self.xs = torch.empty(T, dtype=f32, device=dev) if self.quant else None
+        self.bm = moe.ffn_block_m(T, H, I, E, k, wdt)
+        mt = int(L.moe_align_max_tiles(T, k, E, self.bm))
+        self.counts = torch.empty(E, dtype=i32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=dev)
+        self.sorted_slot = torch.empty(n, dtype=i32, device=dev)
+        self.pos = torch.empty(n, dtype=i32, device=dev)
+        self.tiles = torch.empty((mt, 4), dtype=i32, device=dev)
+        self.num_tiles = torch.empty(1, dtype=i32, device=dev)
+        self.num_dropped = torch.empty(1, dtype=i32, device=dev)
+        ydt = torch.float32 if spec.w_dtype == "f32" else torch.bfloat16
+        self.y = torch.empty((n, H), dtype=ydt, device=dev)
+        self.out = torch.empty((T, H), dtype=d["x"].dtype, device=dev)
+        self.n_route = int(L.moe_route_workspace_size(T, H, E, k))
+        self.n_align = int(L.moe_align_workspace_size(T, k, E))
+        self.n_ffn = int(L.moe_ffn_workspace_size(T, H, I, E, k, moe.binding._DT[wdt]))
+        mx = max(self.n_route, self.n_align, self.n_ffn, 1)
+        self.ws = torch.empty(mx, dtype=torch.uint8, device=dev)
+        self.P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+        self.DT = moe.binding._DT
+
+    def run(self, events=None):
+        L, P, DT, s, d = self.moe.lib, self.P, self.DT, self.spec, self.d
+        T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
+        st = self.moe.binding._stream(d["x"].device)
+        ev = events or [None] * 6
+        chk = self.moe.binding._check
+        ws = P(self.ws)
+        act = self.xq if self.quant else d["x"]
+
+        def rec(i):
+            if ev[i] is not None:
+                ev[i].record()
+
+        rec(0)
+        chk(L.moe_route(P(d["x"]), DT[d["x"].dtype], P(d["wg"]), DT[d["wg"].dtype], P(d["bias"]), T, H, E, k,
+                        P(self.ids), P(self.w), None, P(self.xq), P(self.xs), ws, self.n_route, st))
+        rec(1)
+        chk(L.moe_align(P(self.ids), T, k, E, self.C, self.bm, P(self.counts), P(self.offsets),
+                        P(self.sorted_slot), P(self.pos), P(self.tiles), P(self.num_tiles),
+                        P(self.num_dropped), ws, self.n_align, st))
+        rec(2)
+        chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), DT[d["w13"].dtype], P(d["s13"]),
+                         P(self.sorted_slot), P(self.tiles), P(self.num_tiles), self.bm, T, H, I, E, k, ws,
+                         self.n_ffn, st))
+        rec(3)
+        chk(L.moe_ffn_down(P(d["w2"]), DT[d["w2"].dtype], P(d["s2"]), P(self.sorted_slot), P(self.tiles),
+                           P(self.num_tiles), self.bm, P(self.w), T, H, I, E, k, P(self.y), DT[self.y.dtype],
+                           ws, self.n_ffn, st))
+        rec(4)
+        chk(L.moe_combine(P(self.y), DT[self.y.dtype], P(self.pos), None, T, k, H, P(self.out),
+                          DT[self.out.dtype], st))
+        rec(5)
+
+
+def traffic_for(workload: str, kernel_src: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg: int, sample_n: int) -> dict:
+    import moe_synth
+    import oracle
+    inp = moe_synth.config_inputs(cfg)
+    T = inp.spec.T
+    S = min(sample_n, T)
+    sample = np.sort(np.random.default_rng(7).choice(T, size=S, replace=False))
+    threads = os.cpu_count() or 1
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
+        if blas:
+            threads = max(blas)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.layer_from_inputs(inp, sample_tokens=sample)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{S} of {T} tokens of {inp.spec.name} (routing and align over all {T} tokens, "
+                      f"expert FFN and combine for the sample; fp64 NumPy/OpenBLAS), {dt:.1f} s"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import moe_synth
+    import routing_dispatch_expert_gate_amd as moe
+
+    cfg = args.config
+    spec = moe_synth.CONFIGS[cfg]
+    T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
+    log(f"workload {cfg}: {spec.name}; generating inputs")
+    inp = moe_synth.config_inputs(cfg)
+    d = {n: to_dev(getattr(inp, n), torch) for n in ("x", "wg", "bias", "w13", "w2", "s13", "s2")}
+    C = moe.capacity(T, k, E, spec.capacity_factor) if spec.capacity_factor > 0 else 0
+    layer = moe.Layer(T, H, I, E, k, d["x"].dtype, d["w13"].dtype)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((T, H), dtype=d["x"].dtype, device="cuda")
+    aux = {"counts": counts, "offsets": offsets}
+
+    def step(with_aux=False):
+        layer(d["x"], d["wg"], d["w13"], d["w2"], C, d["bias"], d["s13"], d["s2"], out=out,
+              aux=aux if with_aux else None)
+
+    step(True)
+    torch.cuda.synchronize()
+    dispatch = moe.last_dispatch()
+    off = offsets.cpu().numpy()
+    kept = np.diff(off)
+    N, D = int(off[-1]), int((kept > 0).sum())
+    log(f"dispatch: {dispatch}; N={N} D={D}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+    log(f"layer: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on the stream")
+
+    # staged pass: per-kernel durations from events between launches
+    st = Staged(moe, torch, spec, d, C)
+    names = ["route", "align", "ffn_up", "ffn_down", "combine"]
+    acc = np.zeros(5)
+    for _ in range(max(2, args.warmup)):
+        st.run()
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        st.run(evs)
+        torch.cuda.synchronize()
+        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
+    stage_ms = dict(zip(names, (acc / args.steps).tolist()))
+    log("stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
+
+    # algorithmic work (bytes / flops the method must move or do)
+    bx, bg, bw = BYTES[spec.x_dtype], BYTES[spec.wg_dtype], BYTES[spec.w_dtype]
+    by = 4 if spec.w_dtype == "f32" else 2
+    bo = BYTES[spec.out_dtype]
+    ba = 1 if spec.w_dtype == "i8" else bx                  # activation bytes the up GEMM reads
+    bh = 1 if spec.w_dtype == "i8" else by                  # h bytes the down GEMM reads
+    up_flops = 4.0 * N * H * I
+    down_flops = 2.0 * N * H * I
+    up_bytes = D * 2 * I * H * bw + N * H * ba + N * I * (4 if spec.w_dtype == "i8" else by)
+    down_bytes = D * H * I * bw + N * I * bh + N * H * by
+    route_bytes = T * H * bx + E * H * bg + 8 * T * k + (T * H + 4 * T if spec.w_dtype == "i8" else 0)
+    align_bytes = 12 * T * k
+    combine_bytes = N * H * by + T * H * bo + 4 * T * k
+    dt = spec.w_dtype
+    up_s = stage_ms["ffn_up"] * 1e-3
+    ai = up_flops / up_bytes
+    if ai >= RIDGE[dt]:
+        roof = {"bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s" if dt != "i8" else "TOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": up_bytes / up_s / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "ffn_up_kernel (" + dispatch.split("|")[2].strip().split("+")[0] + ")" \
+        if dispatch.count("|") >= 3 else "ffn_up_kernel"
+    roof["per_launch"] = {"flops": up_flops, "bytes": up_bytes, "ms": stage_ms["ffn_up"]}
+    roof["traffic"] = traffic_for(spec.name, os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "csrc",
+                                                          "ffn.hip"))
+    gemm_s = (stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e-3
+    rac_s = (stage_ms["route"] + stage_ms["align"] + stage_ms["combine"]) * 1e-3
+    rac_bytes = route_bytes + align_bytes + combine_bytes
+    extra = {
+        "grouped_gemm": {"flops": up_flops + down_flops, "ms": gemm_s * 1e3,
+                         "tflops": (up_flops + down_flops) / gemm_s / 1e12,
+                         "frac_of_peak": (up_flops + down_flops) / gemm_s / 1e12 / PEAK_TFLOPS[dt],
+                         "peak_dtype": dt,
+                         "hbm_GBps_alg": (up_bytes + down_bytes) / gemm_s / 1e9},
+        "route_align_combine": {"bytes": rac_bytes, "ms": rac_s * 1e3,
+                                "GBps": rac_bytes / rac_s / 1e9,
+                                "frac_of_hbm": rac_bytes / rac_s / 1e9 / PEAK_HBM_GBPS},
+        "stages_ms": stage_ms,
+        "kept_rows_N": N, "active_experts_D": D, "capacity": C,
+        "layer_gpu_ms": gpu_ms,
+        "dispatch": dispatch,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample or CPU_SAMPLE[cfg]
+        log(f"timing the CPU oracle on {n} tokens")
+        cpu = cpu_baseline(cfg, n)
+
+    rec = {
+        "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "i8": "int8 (W8A8)", "f32": "f32"}[spec.w_dtype],
+        "data": "synthetic (seeded; random-init weights of the workload's shapes)",
+        "config": {"workload": spec.name, "T": T, "H": H, "E": E, "top_k": k, "I": I,
+                   "capacity": C, "x_dtype": spec.x_dtype, "w_dtype": spec.w_dtype,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": extra,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

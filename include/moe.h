@@ -158,6 +158,23 @@ moe_status moe_expert_ffn(const void* x, int32_t act_dtype, const float* xs, con
                           int32_t y_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* The two halves of moe_expert_ffn as separate launches (the up GEMM with
+ * its SwiGLU epilogue, and the down GEMM with its route-weight epilogue, each
+ * one step of the layer).  The workspace (moe_ffn_workspace_size bytes)
+ * carries h from moe_ffn_up to moe_ffn_down: pass the same workspace, with
+ * nothing else writing it in between, on the same stream.  Arguments as in
+ * moe_expert_ffn; for W8A8 the down call quantises h per row first. */
+moe_status moe_ffn_up(const void* x, int32_t act_dtype, const float* xs, const void* w13,
+                      int32_t w_dtype, const float* s13, const int32_t* sorted_slot,
+                      const int32_t* tiles, const int32_t* num_tiles, int32_t block_m, int64_t T,
+                      int32_t H, int32_t I, int32_t E, int32_t k, void* workspace,
+                      size_t workspace_bytes, void* stream);
+moe_status moe_ffn_down(const void* w2, int32_t w_dtype, const float* s2,
+                        const int32_t* sorted_slot, const int32_t* tiles,
+                        const int32_t* num_tiles, int32_t block_m, const float* topk_w, int64_t T,
+                        int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted, int32_t y_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------ combine ----
  * Route-weighted merge of each token's kept expert rows ([FA-MoE] step 5 and
  * its fusion of weighting into accumulation; [LightOP] section 3.2, MoE Sum):

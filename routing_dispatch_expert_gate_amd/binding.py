@@ -36,6 +36,10 @@ SIGNATURES = {
     "moe_ffn_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn": (_st, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                              _i64, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "moe_ffn_up": (_st, [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
+                         _i32, _vp, _sz, _vp]),
+    "moe_ffn_down": (_st, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
+                           _i32, _vp, _sz, _vp]),
     "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "moe_layer_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_layer": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
@@ -177,6 +181,28 @@ def expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, sorted_slot
                               _p(sorted_slot), _p(tiles), _p(num_tiles), block_m, _p(topk_w), T, H, I, E, k,
                               _p(y), _DT[ydt], _p(ws), nws, _stream(dev)))
     return y
+
+
+def ffn_workspace(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype, device="cuda"):
+    """A workspace for moe_ffn_up / moe_ffn_down (it carries h between them)."""
+    n = int(lib.moe_ffn_workspace_size(T, H, I, E, k, _DT[w_dtype]))
+    return _ws(n, device), n
+
+
+def ffn_up(x, w13, sorted_slot, tiles, num_tiles, block_m, k, E, I, ws, xs=None, s13=None):
+    """moe_ffn_up into the workspace ``ws`` = (tensor, nbytes) from ffn_workspace."""
+    T, H = x.shape
+    _check(lib.moe_ffn_up(_p(x), _DT[x.dtype], _p(xs), _p(w13), _DT[w13.dtype], _p(s13), _p(sorted_slot),
+                          _p(tiles), _p(num_tiles), block_m, T, H, I, E, k, _p(ws[0]), ws[1],
+                          _stream(x.device)))
+
+
+def ffn_down(w2, sorted_slot, tiles, num_tiles, block_m, k, T, ws, y, topk_w=None, s2=None):
+    """moe_ffn_down from the workspace filled by ffn_up into ``y`` [T*k, H]."""
+    E, H, I = w2.shape
+    _check(lib.moe_ffn_down(_p(w2), _DT[w2.dtype], _p(s2), _p(sorted_slot), _p(tiles), _p(num_tiles),
+                            block_m, _p(topk_w), T, H, I, E, k, _p(y), _DT[y.dtype], _p(ws[0]), ws[1],
+                            _stream(y.device)))
 
 
 def combine(y_sorted: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor | None, T: int, k: int,

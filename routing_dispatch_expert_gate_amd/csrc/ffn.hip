@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
+constexpr int kI8 = 2;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
@@ -404,54 +405,67 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-template <bool I8>
-hipError_t launch_mfma_pair(const FfnPlan& p, const void* act, const float* xs, const void* w13,
-                            const void* w2, const float* s13, const float* s2,
-                            const int32_t* sorted_slot, const int32_t* tiles,
-                            const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
-                            int k, void* y, void* ws, hipStream_t s) {
-  const int64_t n = T * k;
+struct FfnBufs {
+  void* h;
+  uint32_t* rowmax;
+  int8_t* hq;
+  float* hs;
+};
+
+FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype) {
   uint8_t* wsb = (uint8_t*)ws;
-  void* h = wsb;
-  uint32_t* rowmax = nullptr;
-  int8_t* hq = nullptr;
-  float* hs = nullptr;
-  if (I8) {
+  FfnBufs b{wsb, nullptr, nullptr, nullptr};
+  if (w_dtype == kI8) {
     size_t off = align256((size_t)n * I * 4);
-    rowmax = (uint32_t*)(wsb + off);
+    b.rowmax = (uint32_t*)(wsb + off);
     off += align256((size_t)n * 4);
-    hq = (int8_t*)(wsb + off);
+    b.hq = (int8_t*)(wsb + off);
     off += align256((size_t)n * I);
-    hs = (float*)(wsb + off);
-    zero_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rowmax, n);
+    b.hs = (float*)(wsb + off);
   }
+  return b;
+}
+
+template <bool I8>
+hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const void* w13,
+                     const float* s13, const int32_t* sorted_slot, const int32_t* tiles,
+                     const int32_t* num_tiles, int64_t T, int H, int I, int k, const FfnBufs& b,
+                     hipStream_t s) {
+  const int64_t n = T * k;
+  if (I8) zero_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(b.rowmax, n);
   const unsigned mt = (unsigned)p.max_tiles;
   if (I % 128 == 0) {
     const int nbk = I / 128;
     ffn_up_kernel<I8, 128, 128, 2, 2><<<mt * nbk, 256, 0, s>>>(
         (const uint8_t*)act, xs, (const uint8_t*)w13, s13, sorted_slot, tiles, num_tiles, H, I, k,
-        nbk, h, rowmax);
+        nbk, b.h, b.rowmax);
   } else {
     const int nbk = I / 64;
     ffn_up_kernel<I8, 128, 64, 2, 2><<<mt * nbk, 256, 0, s>>>(
         (const uint8_t*)act, xs, (const uint8_t*)w13, s13, sorted_slot, tiles, num_tiles, H, I, k,
-        nbk, h, rowmax);
+        nbk, b.h, b.rowmax);
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const uint8_t* hin = (const uint8_t*)h;
+  return hipGetLastError();
+}
+
+template <bool I8>
+hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
+                       const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int H,
+                       int I, void* y, const FfnBufs& b, hipStream_t s) {
+  const unsigned mt = (unsigned)p.max_tiles;
+  const uint8_t* hin = (const uint8_t*)b.h;
   if (I8) {
-    quant_h_kernel<<<mt, 256, 0, s>>>((const float*)h, rowmax, tiles, num_tiles, I, hq, hs);
-    hin = (const uint8_t*)hq;
+    quant_h_kernel<<<mt, 256, 0, s>>>((const float*)b.h, b.rowmax, tiles, num_tiles, I, b.hq, b.hs);
+    hin = (const uint8_t*)b.hq;
   }
   if (H % 128 == 0) {
     const int nbk = H / 128;
     ffn_down_kernel<I8, 128, 128, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        hin, hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
+        hin, b.hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
   } else {
     const int nbk = H / 64;
     ffn_down_kernel<I8, 128, 64, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        hin, hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
+        hin, b.hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
   }
   return hipGetLastError();
 }
@@ -482,29 +496,38 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
   return p;
 }
 
-hipError_t launch_ffn(const FfnPlan& p, const void* x, int act_dtype, const float* xs,
-                      const void* w13, const void* w2, int w_dtype, const float* s13,
-                      const float* s2, const int32_t* sorted_slot, const int32_t* tiles,
-                      const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
-                      int E, int k, void* y, void* ws, hipStream_t s) {
-  (void)E;
-  (void)act_dtype;
+hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const void* w13,
+                         int w_dtype, const float* s13, const int32_t* sorted_slot,
+                         const int32_t* tiles, const int32_t* num_tiles, int64_t T, int H, int I,
+                         int k, void* ws, hipStream_t s) {
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype);
   if (w_dtype == kF32) {
     const unsigned mt = (unsigned)p.max_tiles;
-    float* h = (float*)ws;
     ffn_f32_kernel<true><<<mt * (I / 32), 256, 0, s>>>((const float*)x, (const float*)w13, sorted_slot,
-                                                        tiles, num_tiles, nullptr, H, I, k, I / 32, h);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    ffn_f32_kernel<false><<<mt * (H / 32), 256, 0, s>>>(h, (const float*)w2, sorted_slot, tiles,
-                                                         num_tiles, topk_w, H, I, k, H / 32, (float*)y);
+                                                        tiles, num_tiles, nullptr, H, I, k, I / 32,
+                                                        (float*)b.h);
     return hipGetLastError();
   }
   if (w_dtype == kBF16)
-    return launch_mfma_pair<false>(p, x, xs, w13, w2, s13, s2, sorted_slot, tiles, num_tiles, topk_w,
-                                   T, H, I, k, y, ws, s);
-  return launch_mfma_pair<true>(p, x, xs, w13, w2, s13, s2, sorted_slot, tiles, num_tiles, topk_w, T,
-                                H, I, k, y, ws, s);
+    return launch_up<false>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
+  return launch_up<true>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
+}
+
+hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const float* s2,
+                           const int32_t* sorted_slot, const int32_t* tiles,
+                           const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
+                           int k, void* y, void* ws, hipStream_t s) {
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype);
+  if (w_dtype == kF32) {
+    const unsigned mt = (unsigned)p.max_tiles;
+    ffn_f32_kernel<false><<<mt * (H / 32), 256, 0, s>>>((const float*)b.h, (const float*)w2,
+                                                         sorted_slot, tiles, num_tiles, topk_w, H, I,
+                                                         k, H / 32, (float*)y);
+    return hipGetLastError();
+  }
+  if (w_dtype == kBF16)
+    return launch_down<false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
+  return launch_down<true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
 }
 
 }  // namespace moe

@@ -266,42 +266,107 @@ size_t moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_
   return moe::plan_ffn(T, H, I, E, k, w_dtype).ws_bytes;
 }
 
+namespace {
+// Checks shared by the FFN entry points; fills the plan.
+moe_status ffn_prologue(int32_t act_dtype, int32_t w_dtype, int32_t y_dtype, int32_t block_m,
+                        int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                        const int32_t* sorted_slot, const int32_t* tiles,
+                        const int32_t* num_tiles, void* workspace, size_t workspace_bytes,
+                        moe::FfnPlan* plan) {
+  MOE_TRY(ffn_checks(act_dtype, w_dtype, y_dtype, T, H, I, E, k));
+  *plan = moe::plan_ffn(T, H, I, E, k, w_dtype);
+  if (block_m != plan->block_m)
+    return fail(MOE_ERR_INVALID_ARG,
+                "block_m %d does not match the FFN tile height %d for this shape "
+                "(use moe_ffn_block_m)",
+                block_m, plan->block_m);
+  if (T == 0) return MOE_OK;
+  MOE_NONNULL(sorted_slot);
+  MOE_NONNULL(tiles);
+  MOE_NONNULL(num_tiles);
+  MOE_ALIGNED(tiles, 16);
+  return MOE_OK;
+}
+
+moe_status up_checks(const void* x, const float* xs, const void* w13, int32_t w_dtype,
+                     const float* s13) {
+  MOE_NONNULL(x);
+  MOE_NONNULL(w13);
+  if (w_dtype == MOE_I8) {
+    MOE_NONNULL(xs);
+    MOE_NONNULL(s13);
+  }
+  MOE_ALIGNED(x, 16);
+  MOE_ALIGNED(w13, 16);
+  return MOE_OK;
+}
+
+moe_status down_checks(const void* w2, int32_t w_dtype, const float* s2, void* y) {
+  MOE_NONNULL(w2);
+  MOE_NONNULL(y);
+  if (w_dtype == MOE_I8) MOE_NONNULL(s2);
+  MOE_ALIGNED(w2, 16);
+  MOE_ALIGNED(y, 16);
+  return MOE_OK;
+}
+
+int32_t y_dtype_of(int32_t w_dtype) { return w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16; }
+}  // namespace
+
+moe_status moe_ffn_up(const void* x, int32_t act_dtype, const float* xs, const void* w13,
+                      int32_t w_dtype, const float* s13, const int32_t* sorted_slot,
+                      const int32_t* tiles, const int32_t* num_tiles, int32_t block_m, int64_t T,
+                      int32_t H, int32_t I, int32_t E, int32_t k, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  moe::FfnPlan plan;
+  MOE_TRY(ffn_prologue(act_dtype, w_dtype, y_dtype_of(w_dtype), block_m, T, H, I, E, k, sorted_slot,
+                       tiles, num_tiles, workspace, workspace_bytes, &plan));
+  if (T == 0) return ok("none (T=0)");
+  MOE_TRY(up_checks(x, xs, w13, w_dtype, s13));
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  hipError_t e = moe::launch_ffn_up(plan, x, xs, w13, w_dtype, s13, sorted_slot, tiles, num_tiles, T,
+                                    H, I, k, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn_up launch");
+  return ok(plan.up_name);
+}
+
+moe_status moe_ffn_down(const void* w2, int32_t w_dtype, const float* s2,
+                        const int32_t* sorted_slot, const int32_t* tiles,
+                        const int32_t* num_tiles, int32_t block_m, const float* topk_w, int64_t T,
+                        int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted, int32_t y_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  moe::FfnPlan plan;
+  const int32_t act = w_dtype;   // the activation dtype the up launch used
+  MOE_TRY(ffn_prologue(act, w_dtype, y_dtype, block_m, T, H, I, E, k, sorted_slot, tiles, num_tiles,
+                       workspace, workspace_bytes, &plan));
+  if (T == 0) return ok("none (T=0)");
+  MOE_TRY(down_checks(w2, w_dtype, s2, y_sorted));
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  hipError_t e = moe::launch_ffn_down(plan, w2, w_dtype, s2, sorted_slot, tiles, num_tiles, topk_w, T,
+                                      H, I, k, y_sorted, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn_down launch");
+  return ok(plan.down_name);
+}
+
 moe_status moe_expert_ffn(const void* x, int32_t act_dtype, const float* xs, const void* w13,
                           const void* w2, int32_t w_dtype, const float* s13, const float* s2,
                           const int32_t* sorted_slot, const int32_t* tiles,
                           const int32_t* num_tiles, int32_t block_m, const float* topk_w,
                           int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted,
                           int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  MOE_TRY(ffn_checks(act_dtype, w_dtype, y_dtype, T, H, I, E, k));
-  const moe::FfnPlan plan = moe::plan_ffn(T, H, I, E, k, w_dtype);
-  if (block_m != plan.block_m)
-    return fail(MOE_ERR_INVALID_ARG,
-                "block_m %d does not match the FFN tile height %d for this shape "
-                "(use moe_ffn_block_m)",
-                block_m, plan.block_m);
+  moe::FfnPlan plan;
+  MOE_TRY(ffn_prologue(act_dtype, w_dtype, y_dtype, block_m, T, H, I, E, k, sorted_slot, tiles,
+                       num_tiles, workspace, workspace_bytes, &plan));
   if (T == 0) return ok("none (T=0)");
-  MOE_NONNULL(x);
-  MOE_NONNULL(w13);
-  MOE_NONNULL(w2);
-  MOE_NONNULL(sorted_slot);
-  MOE_NONNULL(tiles);
-  MOE_NONNULL(num_tiles);
-  MOE_NONNULL(y_sorted);
-  if (w_dtype == MOE_I8) {
-    MOE_NONNULL(xs);
-    MOE_NONNULL(s13);
-    MOE_NONNULL(s2);
-  }
-  MOE_ALIGNED(x, 16);
-  MOE_ALIGNED(w13, 16);
-  MOE_ALIGNED(w2, 16);
-  MOE_ALIGNED(tiles, 16);
-  MOE_ALIGNED(y_sorted, 16);
+  MOE_TRY(up_checks(x, xs, w13, w_dtype, s13));
+  MOE_TRY(down_checks(w2, w_dtype, s2, y_sorted));
   MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
-  hipError_t e = moe::launch_ffn(plan, x, act_dtype, xs, w13, w2, w_dtype, s13, s2, sorted_slot,
-                                 tiles, num_tiles, topk_w, T, H, I, E, k, y_sorted, workspace,
-                                 (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn launch");
+  hipError_t e = moe::launch_ffn_up(plan, x, xs, w13, w_dtype, s13, sorted_slot, tiles, num_tiles, T,
+                                    H, I, k, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn up launch");
+  e = moe::launch_ffn_down(plan, w2, w_dtype, s2, sorted_slot, tiles, num_tiles, topk_w, T, H, I, k,
+                           y_sorted, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn down launch");
   return ok(std::string(plan.up_name) + "+" + plan.down_name);
 }
 
@@ -351,12 +416,13 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
                 x_dtype, w_dtype);
   const int32_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   MOE_TRY(ffn_checks(act, w_dtype, ydt, T, H, I, E, k));
-  int8_t dummy_q = 0;
-  float dummy_s = 0.f;
+  // the route outputs live in the workspace: validate the rest with aligned
+  // stand-ins for them (never dereferenced)
+  alignas(16) static int32_t stand_in[4];
+  int32_t* const si = stand_in;
   moe::RoutePlan rp;
-  MOE_TRY(route_checks(T ? x : nullptr, x_dtype, wg, wg_dtype, T, H, E, k, (int32_t*)&dummy_s,
-                       &dummy_s, act == MOE_I8 ? &dummy_q : nullptr, act == MOE_I8 ? &dummy_s : nullptr,
-                       &rp));
+  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, si, (float*)si,
+                       act == MOE_I8 ? (int8_t*)si : nullptr, act == MOE_I8 ? (float*)si : nullptr, &rp));
   if (T == 0) return ok("none (T=0)");
   MOE_NONNULL(w13);
   MOE_NONNULL(w2);
@@ -401,9 +467,12 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
                         c.fp.max_tiles, counts, offsets, sorted_slot, pos, tiles, num_tiles,
                         num_dropped, scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
-  e = moe::launch_ffn(c.fp, act == MOE_I8 ? (const void*)xq : x, act, xs, w13, w2, w_dtype, s13, s2,
-                      sorted_slot, tiles, num_tiles, w, T, H, I, E, k, y, scratch, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_layer ffn launch");
+  e = moe::launch_ffn_up(c.fp, act == MOE_I8 ? (const void*)xq : x, xs, w13, w_dtype, s13,
+                         sorted_slot, tiles, num_tiles, T, H, I, k, scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer ffn up launch");
+  e = moe::launch_ffn_down(c.fp, w2, w_dtype, s2, sorted_slot, tiles, num_tiles, w, T, H, I, k, y,
+                           scratch, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer ffn down launch");
   e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
   return ok(route_name(c.rp) + " | align(blocks=" + std::to_string(c.ap.nblocks) + ") | " +

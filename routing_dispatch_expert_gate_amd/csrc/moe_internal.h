@@ -109,11 +109,16 @@ struct FfnPlan {
   const char* down_name;
 };
 FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype);
-hipError_t launch_ffn(const FfnPlan& p, const void* x, int act_dtype, const float* xs,
-                      const void* w13, const void* w2, int w_dtype, const float* s13,
-                      const float* s2, const int32_t* sorted_slot, const int32_t* tiles,
-                      const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
-                      int E, int k, void* y, void* ws, hipStream_t s);
+// The FFN workspace carries h (and, for W8A8, row maxima, codes and scales)
+// from the up launch to the down launch.
+hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const void* w13,
+                         int w_dtype, const float* s13, const int32_t* sorted_slot,
+                         const int32_t* tiles, const int32_t* num_tiles, int64_t T, int H, int I,
+                         int k, void* ws, hipStream_t s);
+hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const float* s2,
+                           const int32_t* sorted_slot, const int32_t* tiles,
+                           const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
+                           int k, void* y, void* ws, hipStream_t s);
 
 int64_t align_max_tiles(int64_t T, int k, int E, int block_m);
 

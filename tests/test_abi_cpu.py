@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
