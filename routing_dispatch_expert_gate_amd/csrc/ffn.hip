@@ -34,6 +34,7 @@
 //    max (non-negative floats order like their bit patterns); a row pass then
 //    quantises h with the per-token rule, and the down GEMM runs int8 MFMA.
 #include <math.h>
+#include <stdio.h>
 
 #include "moe_internal.h"
 
@@ -51,7 +52,7 @@ struct Mma;
 template <>
 struct Mma<false> {
   typedef f32x16 Acc;
-  static __device__ __forceinline__ Acc run(const uint4& a, const uint4& b, const Acc& c) {
+  static __device__ __forceinline__ Acc run(const u32x4& a, const u32x4& b, const Acc& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
@@ -59,252 +60,339 @@ struct Mma<false> {
 template <>
 struct Mma<true> {
   typedef i32x16 Acc;
-  static __device__ __forceinline__ Acc run(const uint4& a, const uint4& b, const Acc& c) {
+  static __device__ __forceinline__ Acc run(const u32x4& a, const u32x4& b, const Acc& c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                  __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
   }
 };
 
-// acc[FM][NF] += A_tile * B_tile^T over nk steps of 128 bytes of K.
-// aload(p, kt) returns this thread's p-th A chunk of step kt; bptr[p] points
-// at this thread's p-th B chunk of step 0.  Chunk q = tid + p*NT is row q/8,
-// 16-byte column q%8.  wrow: first A row of this wave; brow_of(nf): first B
-// row of the wave's nf-th 32-column fragment.
-template <bool I8, int BM, int BNB, int NT, int FM, int NF, typename ALoad, typename BRow>
-__device__ __forceinline__ void gemm_mainloop(uint8_t* __restrict__ smem, ALoad&& aload,
-                                              const uint8_t* const* bptr, int nk, int wrow,
-                                              BRow&& brow_of, typename Mma<I8>::Acc (&acc)[FM][NF]) {
-  constexpr int APASS = BM * 8 / NT;
-  constexpr int BPASS = BNB * 8 / NT;
-  constexpr int STAGE = (BM + BNB) * 128;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  uint4 ar[APASS], br[BPASS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) ar[p] = aload(p, kt);
-#pragma unroll
-    for (int p = 0; p < BPASS; ++p) br[p] = *reinterpret_cast<const uint4*>(bptr[p] + (size_t)kt * 128);
-  };
-  auto sstore = [&](int st) {
-    uint8_t* base = smem + st * STAGE;
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      const int q = tid + p * NT;
-      *reinterpret_cast<uint4*>(base + swz(q >> 3, q & 7)) = ar[p];
-    }
-#pragma unroll
-    for (int p = 0; p < BPASS; ++p) {
-      const int q = tid + p * NT;
-      *reinterpret_cast<uint4*>(base + BM * 128 + swz(q >> 3, q & 7)) = br[p];
-    }
-  };
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* As = smem + cur * STAGE;
-    const uint8_t* Bs = As + BM * 128;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 2 * s + (lane >> 5);
-      uint4 a[FM], b[NF];
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        a[fm] = *reinterpret_cast<const uint4*>(As + swz(wrow + fm * 32 + (lane & 31), c));
-#pragma unroll
-      for (int nf = 0; nf < NF; ++nf)
-        b[nf] = *reinterpret_cast<const uint4*>(Bs + swz(brow_of(nf) + (lane & 31), c));
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int nf = 0; nf < NF; ++nf) acc[fm][nf] = Mma<I8>::run(a[fm], b[nf], acc[fm][nf]);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
-}
-
 // MFMA 32x32 accumulator element v of lane l sits at row 8*(v/4) + 4*(l/32) + v%4,
 // column l%32 of the fragment.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-// ------------------------------------------------------------- up GEMM ---
-template <bool I8, int BM, int BNH, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void ffn_up_kernel(
-    const uint8_t* __restrict__ act, const float* __restrict__ xs, const uint8_t* __restrict__ w13,
-    const float* __restrict__ s13, const int32_t* __restrict__ sorted_slot,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I, int k,
-    int n_blocks, void* __restrict__ hout, uint32_t* __restrict__ rowmax) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BNB = 2 * BNH;
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup P runs on
+// XCD P % 8).  Renumber them so that consecutive logical ids run on the same
+// XCD and share its L2.
+__device__ __forceinline__ int xcd_remap(int P, int G) {
+  const int q = G >> 3, r = G & 7, x = P & 7, j = P >> 3;
+  return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+constexpr int kGroupN = 8;   // N blocks per raster group
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+// Calls f(IntC<v>) for the runtime value v in [0, MAX] (v is wave-uniform).
+template <int MAX, typename F>
+__device__ __forceinline__ void dispatch_valid(int v, F&& f) {
+  if constexpr (MAX >= 0) {
+    if (v == MAX) {
+      f(IntC<MAX>{});
+      return;
+    }
+    if constexpr (MAX > 0) dispatch_valid<MAX - 1>(v, f);
+  }
+}
+
+struct GemmArgs {
+  const uint8_t* act;          // up: x or xq [T, H] (rows gathered); down: h or hq [rows, I]
+  const uint8_t* w;            // up: w13 [E, 2I, H]; down: w2 [E, H, I]
+  const int32_t* sorted_slot;
+  const int32_t* tiles;
+  const int32_t* num_tiles;
+  const float* xs;             // up, W8A8: per-token activation scale
+  const float* wscale;         // W8A8: per-output-channel weight scale, [E, 2I] up / [E, H] down
+  const float* hs;             // down, W8A8: per-row scale of h
+  const float* topk_w;         // down: route weight per slot (NULL: 1)
+  void* out;                   // up: h [rows, I] (bf16; fp32 for W8A8); down: y [rows, H] bf16
+  uint32_t* rowmax;            // up, W8A8: max |h| of each row (bit pattern of a non-negative float)
+  int H, I, k;
+  int n_blocks, max_tiles;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// LDS row swizzles: chunk c (16 bytes) of row r is stored at c ^ sw(r), so
+// that sixteen consecutive rows read at one chunk fall on sixteen distinct
+// 16-byte slots of a 256-byte bank row, and any eight consecutive rows on
+// eight distinct slots of a 128-byte one.
+//  64-byte rows (4 chunks): period 32;  128-byte rows (8 chunks): period 16.
+template <int ROWB>
+__device__ __forceinline__ int swr(int r) {
+  if constexpr (ROWB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
+  return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+}
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// wait until at most m*L of this wave's vector-memory ops are outstanding,
+// for a runtime m in [0, MMAX]
+template <int L, int MMAX>
+__device__ __forceinline__ void wait_vm_stages(int m) {
+  if constexpr (MMAX > 0) {
+    if (m >= MMAX) {
+      wait_vmcnt<MMAX * L>();
+      return;
+    }
+    wait_vm_stages<L, MMAX - 1>(m);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+// All of this wave's LDS reads have returned, then the workgroup barrier.
+// The memory clobber keeps every LDS access on its side of the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One BM x BN output tile of one row tile (one expert).  Waves form a WM x WN
+// grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments.
+//  up:   the B tile stacks BN/2 rows of W1 over the same BN/2 rows of W3, each
+//        wave holds matching G and U fragments, and the epilogue writes
+//        h = silu(G) * U;
+//  down: the B tile is BN rows of W2 and the epilogue writes w_r * acc.
+// K advances 64 bytes per stage (32 bf16 or 64 int8).  Stages are copied from
+// global memory straight into LDS (16 bytes per lane per instruction, lane i
+// landing at 16*i of a 1 KiB block), S stages deep: stage kt+S-1 is in flight
+// while stage kt computes, with no staging registers.  Each wave issues the
+// same number of copies per stage, waits for its own copies of stage kt with
+// an exact vmcnt, and a barrier then publishes them to the workgroup.
+// 32-row fragments wholly past the tile's valid rows skip their MFMAs (the
+// K loop is specialised on their number), and rows past the valid ones copy
+// the tile's first row: their accumulators are never stored (an MFMA output
+// row depends only on its A row).
+template <bool I8, bool UP, int BM, int BN, int WM, int WN, int S, int ROWB>
+__global__ __launch_bounds__(WM* WN * 64)
+__attribute__((amdgpu_waves_per_eu(
+    (BM / WM) * (BN / WN) <= 128 * 64 && 2 * S * (BM + BN) * ROWB <= 160 * 1024 ? 2 : 1)))
+void gg_kernel(const GemmArgs a) {
+  constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int WROWS = BM / WM, FM = WROWS / 32;
-  constexpr int WCOLS = BNH / WN, FN = WCOLS / 32, NF = 2 * FN;
-  constexpr int APASS = BM * 8 / NT, BPASS = BNB * 8 / NT;
+  constexpr int WCOLS = BN / WN, NF = WCOLS / 32;
+  constexpr int HB = BN / 2, HW = WCOLS / 2;
+  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int RPB = 1024 / ROWB;                   // rows per 1 KiB copy block
+  constexpr int SUB = ROWB / 32;                     // MFMA k-substeps per stage
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int NBLK = (BM + BN) / RPB;              // 1 KiB copy blocks per stage
+  constexpr int L = NBLK / NW;                       // copies per wave per stage
   constexpr int EB = I8 ? 1 : 2;
-  static_assert(APASS * NT == BM * 8 && BPASS * NT == BNB * 8, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BNB) * 128];
+  static_assert(L * NW == NBLK, "copies must split evenly over the waves");
+  static_assert(FM >= 1 && NF >= 1, "wave tile too small");
+  static_assert(!UP || (NF % 2 == 0), "up needs paired G/U fragments");
+  static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS stages");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
 
-  const int tile = blockIdx.x / n_blocks;
-  const int nb = blockIdx.x - tile * n_blocks;
-  if (tile >= *num_tiles) return;
-  const int4 td = reinterpret_cast<const int4*>(tiles)[tile];
-  const int e = td.x, r0 = td.y, rows = td.z;
-  const int n0 = nb * BNH;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int L0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_group = a.max_tiles * kGroupN;
+  const int g = L0 / per_group;
+  const int rem = L0 - g * per_group;
+  const int gs = min(kGroupN, a.n_blocks - g * kGroupN);
+  const int tile = rem / gs;
+  const int nb = g * kGroupN + (rem - tile * gs);
+  if (tile >= *a.num_tiles) return;
+  // the tile descriptor is uniform: keep it in scalar registers so every
+  // branch on it below is a scalar branch
+  const int4 td = reinterpret_cast<const int4*>(a.tiles)[tile];
+  const int e = __builtin_amdgcn_readfirstlane(td.x);
+  const int r0 = __builtin_amdgcn_readfirstlane(td.y);
+  const int rows = __builtin_amdgcn_readfirstlane(td.z);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / WN, wn = wv - (wv / WN) * WN;
-  const int64_t row_bytes = (int64_t)H * EB;
+  const int64_t kbytes = (int64_t)(UP ? a.H : a.I) * EB;
+  const int nk = (int)(kbytes / ROWB);
 
-  const uint8_t* aptr[APASS];
-  bool aval[APASS];
+  // This wave's copies: block q = wv*L + j; blocks [0, BM/RPB) are A rows,
+  // the rest B rows.  Lane i copies row RPB*blk + i/CPR into LDS chunk
+  // i%CPR, which holds logical chunk (i%CPR) ^ sw(row).
+  const uint8_t* abase = UP ? a.act : a.act + (int64_t)r0 * kbytes;
+  const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes;
+  uint32_t goff[L];
 #pragma unroll
-  for (int p = 0; p < APASS; ++p) {
-    const int q = tid + p * NT, r = q >> 3, c = q & 7;
-    aval[p] = r < rows;
-    const int tok = aval[p] ? sorted_slot[r0 + r] / k : 0;
-    aptr[p] = act + (int64_t)tok * row_bytes + c * 16;
+  for (int j = 0; j < L; ++j) {
+    const int q = wv * L + j;
+    const bool is_a = q < BM / RPB;                  // uniform
+    const int trow = (is_a ? q : q - BM / RPB) * RPB + lane / CPR;
+    const int c = (lane % CPR) ^ swr<ROWB>(trow);
+    uint32_t row;
+    if (is_a) {
+      const int r = trow < rows ? trow : 0;
+      row = UP ? (uint32_t)(a.sorted_slot[r0 + r] / a.k) : (uint32_t)r;
+    } else if (UP) {
+      row = (uint32_t)(trow < HB ? nb * HB + trow : a.I + nb * HB + (trow - HB));
+    } else {
+      row = (uint32_t)(nb * BN + trow);
+    }
+    goff[j] = row * (uint32_t)kbytes + c * 16;
   }
-  const uint8_t* bptr[BPASS];
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % S) * STAGE;
 #pragma unroll
-  for (int p = 0; p < BPASS; ++p) {
-    const int q = tid + p * NT, r = q >> 3, c = q & 7;
-    const int wrow = r < BNH ? n0 + r : I + n0 + (r - BNH);
-    bptr[p] = w13 + ((int64_t)e * 2 * I + wrow) * row_bytes + c * 16;
-  }
+    for (int j = 0; j < L; ++j) {
+      const int q = wv * L + j;
+      const uint8_t* src = (q < BM / RPB ? abase : bbase) + (size_t)kt * ROWB + goff[j];
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(st + q * 1024), 16, 0, 0);
+    }
+  };
+
+  // number of this wave's 32-row fragments that hold valid rows (uniform)
+  int fmv = (rows - wm * WROWS + 31) / 32;
+  fmv = fmv < 0 ? 0 : (fmv > FM ? FM : fmv);
+
   typename Mma<I8>::Acc acc[FM][NF];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int nf = 0; nf < NF; ++nf) acc[fm][nf] = typename Mma<I8>::Acc{};
 
-  auto aload = [&](int p, int kt) -> uint4 {
-    return aval[p] ? *reinterpret_cast<const uint4*>(aptr[p] + (size_t)kt * 128) : make_uint4(0, 0, 0, 0);
-  };
   auto brow_of = [&](int nf) -> int {
-    return nf < FN ? wn * WCOLS + nf * 32 : BNH + wn * WCOLS + (nf - FN) * 32;
+    if (UP) return nf < NF / 2 ? wn * HW + nf * 32 : HB + wn * HW + (nf - NF / 2) * 32;
+    return wn * WCOLS + nf * 32;
   };
-  gemm_mainloop<I8, BM, BNB, NT, FM, NF>(smem, aload, bptr, (int)(row_bytes / 128), wm * WROWS,
-                                         brow_of, acc);
-
-  if (!I8) {
-    uint16_t* h = reinterpret_cast<uint16_t*>(hout);
+  // fragment rows start at multiples of 32 (the swizzle period), so a lane's
+  // address within a fragment depends on the lane and the substep only
+  int lo[SUB];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+  for (int s = 0; s < SUB; ++s) {
+    const int r = lane & 31, c = 2 * s + (lane >> 5);
+    lo[s] = r * ROWB + ((c ^ swr<ROWB>(r)) << 4);
+  }
+
+  auto kloop = [&](auto vtag) {
+    constexpr int V = decltype(vtag)::value;
+#pragma unroll
+    for (int p = 0; p < S - 1; ++p)
+      if (p < nk) issue(p);
+    for (int kt = 0; kt < nk; ++kt) {
+      // stages issued after kt: min(S-2, nk-1-kt)
+      const int after = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
+      wait_vm_stages<L, S - 2>(after);
+      lds_barrier();
+      if (kt + S - 1 < nk) issue(kt + S - 1);
+      if constexpr (V > 0) {
+        const uint8_t* As = smem + (kt % S) * STAGE;
+        const uint8_t* Bs = As + BM * ROWB;
+        u32x4 af[SUB][V], bfr[SUB][NF];
+        // read order A0, B0..B(NF-1), A1..A(V-1): the first MFMA (A0 x B0)
+        // waits for two reads only
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+          af[s][0] = *reinterpret_cast<const u32x4*>(As + lo[s] + (wm * WROWS) * ROWB);
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            bfr[s][nf] = *reinterpret_cast<const u32x4*>(Bs + lo[s] + brow_of(nf) * ROWB);
+#pragma unroll
+          for (int fm = 1; fm < V; ++fm)
+            af[s][fm] = *reinterpret_cast<const u32x4*>(As + lo[s] + (wm * WROWS + fm * 32) * ROWB);
+        }
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+          for (int fm = 0; fm < V; ++fm)
+#pragma unroll
+            for (int nf = 0; nf < NF; ++nf)
+              acc[fm][nf] = Mma<I8>::run(af[s][fm], bfr[s][nf], acc[fm][nf]);
+        // schedule: substep-0 fragment reads, then each later substep's reads
+        // spread over the previous substep's MFMAs (LDS latency hidden behind
+        // matrix work), then the last substep's MFMAs
+        constexpr int R = V + NF, M = V * NF, PER = (M + R - 1) / R;
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+        for (int s = 1; s < SUB; ++s) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (M - R * PER > 0) __builtin_amdgcn_sched_group_barrier(0x008, M - R * PER, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+      }
+    }
+  };
+  dispatch_valid<FM>(fmv, kloop);
+  bool fv[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) fv[fm] = fm < fmv;
+
+  if constexpr (UP && !I8) {
+    uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (!fv[fm]) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
         if (row >= rows) continue;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int col = n0 + wn * WCOLS + f * 32 + (lane & 31);
-          const float g = (float)acc[fm][f][v], u = (float)acc[fm][FN + f][v];
-          h[(int64_t)(r0 + row) * I + col] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+        for (int f = 0; f < NF / 2; ++f) {
+          const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+          const float gv = (float)acc[fm][f][v], uv = (float)acc[fm][NF / 2 + f][v];
+          h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)f32_to_bf16_bits(silu_f32(gv) * uv);
         }
       }
-  } else {
-    float* h = reinterpret_cast<float*>(hout);
-    float sg[FN], su[FN];
+    }
+  } else if constexpr (UP) {
+    float* h = reinterpret_cast<float*>(a.out);
+    float sg[NF / 2], su[NF / 2];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int col = n0 + wn * WCOLS + f * 32 + (lane & 31);
-      sg[f] = s13[(int64_t)e * 2 * I + col];
-      su[f] = s13[(int64_t)e * 2 * I + I + col];
+    for (int f = 0; f < NF / 2; ++f) {
+      const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+      sg[f] = a.wscale[(int64_t)e * 2 * a.I + col];
+      su[f] = a.wscale[(int64_t)e * 2 * a.I + a.I + col];
     }
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+      if (!fv[fm]) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
         const bool valid = row < rows;
-        const float xsr = valid ? xs[sorted_slot[r0 + row] / k] : 0.f;
+        const float xsr = valid ? a.xs[a.sorted_slot[r0 + row] / a.k] : 0.f;
         float m = 0.f;
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          const int col = n0 + wn * WCOLS + f * 32 + (lane & 31);
-          const float g = (float)acc[fm][f][v] * xsr * sg[f];
-          const float u = (float)acc[fm][FN + f][v] * xsr * su[f];
-          const float hv = silu_f32(g) * u;
-          if (valid) h[(int64_t)(r0 + row) * I + col] = hv;
+        for (int f = 0; f < NF / 2; ++f) {
+          const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+          const float gv = (float)acc[fm][f][v] * xsr * sg[f];
+          const float uv = (float)acc[fm][NF / 2 + f][v] * xsr * su[f];
+          const float hv = silu_f32(gv) * uv;
+          if (valid) h[(int64_t)(r0 + row) * a.I + col] = hv;
           m = fmaxf(m, fabsf(hv));
         }
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        if (valid && (lane & 31) == 0) atomicMax(rowmax + r0 + row, __float_as_uint(m));
-      }
-  }
-}
-
-// ----------------------------------------------------------- down GEMM ---
-template <bool I8, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM* WN * 64) void ffn_down_kernel(
-    const uint8_t* __restrict__ hin, const float* __restrict__ hs, const uint8_t* __restrict__ w2,
-    const float* __restrict__ s2, const int32_t* __restrict__ sorted_slot,
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ num_tiles,
-    const float* __restrict__ topk_w, int H, int I, int n_blocks, uint16_t* __restrict__ y) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int WROWS = BM / WM, FM = WROWS / 32;
-  constexpr int WCOLS = BN / WN, NF = WCOLS / 32;
-  constexpr int APASS = BM * 8 / NT, BPASS = BN * 8 / NT;
-  constexpr int EB = I8 ? 1 : 2;
-  static_assert(APASS * NT == BM * 8 && BPASS * NT == BN * 8, "tile / thread mismatch");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (BM + BN) * 128];
-
-  const int tile = blockIdx.x / n_blocks;
-  const int nb = blockIdx.x - tile * n_blocks;
-  if (tile >= *num_tiles) return;
-  const int4 td = reinterpret_cast<const int4*>(tiles)[tile];
-  const int e = td.x, r0 = td.y, rows = td.z;
-  const int n0 = nb * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv / WN, wn = wv - (wv / WN) * WN;
-  const int64_t row_bytes = (int64_t)I * EB;
-
-  const uint8_t* aptr[APASS];
-  bool aval[APASS];
-#pragma unroll
-  for (int p = 0; p < APASS; ++p) {
-    const int q = tid + p * NT, r = q >> 3, c = q & 7;
-    aval[p] = r < rows;
-    aptr[p] = hin + (int64_t)(aval[p] ? r0 + r : 0) * row_bytes + c * 16;
-  }
-  const uint8_t* bptr[BPASS];
-#pragma unroll
-  for (int p = 0; p < BPASS; ++p) {
-    const int q = tid + p * NT, r = q >> 3, c = q & 7;
-    bptr[p] = w2 + ((int64_t)e * H + n0 + r) * row_bytes + c * 16;
-  }
-  typename Mma<I8>::Acc acc[FM][NF];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int nf = 0; nf < NF; ++nf) acc[fm][nf] = typename Mma<I8>::Acc{};
-  auto aload = [&](int p, int kt) -> uint4 {
-    return aval[p] ? *reinterpret_cast<const uint4*>(aptr[p] + (size_t)kt * 128) : make_uint4(0, 0, 0, 0);
-  };
-  auto brow_of = [&](int nf) -> int { return wn * WCOLS + nf * 32; };
-  gemm_mainloop<I8, BM, BN, NT, FM, NF>(smem, aload, bptr, (int)(row_bytes / 128), wm * WROWS,
-                                        brow_of, acc);
-
-  float sc[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f)
-    sc[f] = I8 ? s2[(int64_t)e * H + n0 + wn * WCOLS + f * 32 + (lane & 31)] : 1.f;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-      if (row >= rows) continue;
-      float wr = topk_w ? topk_w[sorted_slot[r0 + row]] : 1.f;
-      if (I8) wr *= hs[r0 + row];
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int col = n0 + wn * WCOLS + f * 32 + (lane & 31);
-        y[(int64_t)(r0 + row) * H + col] = (uint16_t)f32_to_bf16_bits((float)acc[fm][f][v] * sc[f] * wr);
+        if (valid && (lane & 31) == 0) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
       }
     }
+  } else {
+    uint16_t* y = reinterpret_cast<uint16_t*>(a.out);
+    float sc[NF];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      sc[f] = I8 ? a.wscale[(int64_t)e * a.H + nb * BN + wn * WCOLS + f * 32 + (lane & 31)] : 1.f;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (!fv[fm]) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
+        if (row >= rows) continue;
+        float wr = a.topk_w ? a.topk_w[a.sorted_slot[r0 + row]] : 1.f;
+        if (I8) wr *= a.hs[r0 + row];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int col = nb * BN + wn * WCOLS + f * 32 + (lane & 31);
+          y[(int64_t)(r0 + row) * a.H + col] = (uint16_t)f32_to_bf16_bits((float)acc[fm][f][v] * sc[f] * wr);
+        }
+      }
+    }
+  }
 }
 
 // ----------------------------------------------------- W8A8 h quantise ---
@@ -426,6 +514,56 @@ FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype) {
   return b;
 }
 
+struct Variant {
+  int bm, bn, wm, wn, stages, rowb;
+};
+// Rows: tile family (BN) by the divisibility of I (up) or H (down); columns:
+// prefill (256 x BN, 2 x 2 waves, 128-byte stage rows: every 1 KiB copy is 8
+// whole cache lines), mid (256 x BN, waves split N), decode (64 x BN, deeper
+// pipeline for weight streaming).  Where a family has no distinct mid tile
+// the prefill one is reused (entries 4 up, 7 down).
+constexpr Variant kUpVar[] = {{256, 256, 2, 2, 2, 128}, {256, 256, 1, 4, 4, 64}, {64, 256, 1, 4, 6, 64},
+                              {256, 128, 2, 2, 3, 128}, {256, 128, 2, 2, 3, 128}, {64, 128, 1, 2, 6, 64}};
+constexpr Variant kDownVar[] = {{256, 256, 2, 2, 2, 128}, {256, 256, 1, 4, 4, 64}, {64, 256, 1, 4, 6, 64},
+                                {256, 128, 2, 2, 3, 128}, {256, 128, 1, 4, 4, 64}, {64, 128, 1, 4, 6, 64},
+                                {256, 64, 2, 2, 3, 128},  {256, 64, 2, 2, 3, 128},  {64, 64, 1, 2, 6, 64}};
+
+#define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R) \
+  case IDX:                                    \
+    gg_kernel<I8, UP, BM, BN, WM, WN, S, R><<<grid, WM * WN * 64, 0, s>>>(a); \
+    break;
+
+template <bool I8, bool UP>
+hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
+  if constexpr (UP) {
+    switch (var) {
+      MOE_GG_CASE(0, 256, 256, 2, 2, 2, 128)
+      MOE_GG_CASE(1, 256, 256, 1, 4, 4, 64)
+      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64)
+      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128)
+      MOE_GG_CASE(5, 64, 128, 1, 2, 6, 64)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    switch (var) {
+      MOE_GG_CASE(0, 256, 256, 2, 2, 2, 128)
+      MOE_GG_CASE(1, 256, 256, 1, 4, 4, 64)
+      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64)
+      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128)
+      MOE_GG_CASE(4, 256, 128, 1, 4, 4, 64)
+      MOE_GG_CASE(5, 64, 128, 1, 4, 6, 64)
+      MOE_GG_CASE(6, 256, 64, 2, 2, 3, 128)
+      MOE_GG_CASE(8, 64, 64, 1, 2, 6, 64)
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+#undef MOE_GG_CASE
+
 template <bool I8>
 hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const void* w13,
                      const float* s13, const int32_t* sorted_slot, const int32_t* tiles,
@@ -433,41 +571,47 @@ hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const v
                      hipStream_t s) {
   const int64_t n = T * k;
   if (I8) zero_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(b.rowmax, n);
-  const unsigned mt = (unsigned)p.max_tiles;
-  if (I % 128 == 0) {
-    const int nbk = I / 128;
-    ffn_up_kernel<I8, 128, 128, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        (const uint8_t*)act, xs, (const uint8_t*)w13, s13, sorted_slot, tiles, num_tiles, H, I, k,
-        nbk, b.h, b.rowmax);
-  } else {
-    const int nbk = I / 64;
-    ffn_up_kernel<I8, 128, 64, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        (const uint8_t*)act, xs, (const uint8_t*)w13, s13, sorted_slot, tiles, num_tiles, H, I, k,
-        nbk, b.h, b.rowmax);
-  }
-  return hipGetLastError();
+  GemmArgs a{};
+  a.act = (const uint8_t*)act;
+  a.w = (const uint8_t*)w13;
+  a.sorted_slot = sorted_slot;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.xs = xs;
+  a.wscale = s13;
+  a.out = b.h;
+  a.rowmax = b.rowmax;
+  a.H = H;
+  a.I = I;
+  a.k = k;
+  a.n_blocks = I / (kUpVar[p.up_var].bn / 2);
+  a.max_tiles = (int)p.max_tiles;
+  return launch_gg<I8, true>(p.up_var, a, s);
 }
 
 template <bool I8>
 hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
                        const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int H,
                        int I, void* y, const FfnBufs& b, hipStream_t s) {
-  const unsigned mt = (unsigned)p.max_tiles;
-  const uint8_t* hin = (const uint8_t*)b.h;
-  if (I8) {
-    quant_h_kernel<<<mt, 256, 0, s>>>((const float*)b.h, b.rowmax, tiles, num_tiles, I, b.hq, b.hs);
-    hin = (const uint8_t*)b.hq;
-  }
-  if (H % 128 == 0) {
-    const int nbk = H / 128;
-    ffn_down_kernel<I8, 128, 128, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        hin, b.hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
-  } else {
-    const int nbk = H / 64;
-    ffn_down_kernel<I8, 128, 64, 2, 2><<<mt * nbk, 256, 0, s>>>(
-        hin, b.hs, (const uint8_t*)w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, nbk, (uint16_t*)y);
-  }
-  return hipGetLastError();
+  if (I8)
+    quant_h_kernel<<<(unsigned)p.max_tiles, 256, 0, s>>>((const float*)b.h, b.rowmax, tiles,
+                                                         num_tiles, I, b.hq, b.hs);
+  GemmArgs a{};
+  a.act = I8 ? (const uint8_t*)b.hq : (const uint8_t*)b.h;
+  a.w = (const uint8_t*)w2;
+  a.sorted_slot = sorted_slot;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.wscale = s2;
+  a.hs = b.hs;
+  a.topk_w = topk_w;
+  a.out = y;
+  a.H = H;
+  a.I = I;
+  a.k = 1;
+  a.n_blocks = H / kDownVar[p.down_var].bn;
+  a.max_tiles = (int)p.max_tiles;
+  return launch_gg<I8, false>(p.down_var, a, s);
 }
 
 }  // namespace
@@ -478,19 +622,30 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
   if (w_dtype == kF32) {
     p.block_m = 32;
     p.ws_bytes = align256((size_t)n * I * 4);
-    p.up_name = "ffn_f32_kernel<up>";
-    p.down_name = "ffn_f32_kernel<down>";
-  } else if (w_dtype == kBF16) {
-    p.block_m = 128;
-    p.ws_bytes = align256((size_t)n * I * 2);
-    p.up_name = I % 128 == 0 ? "ffn_up_kernel<bf16,128,128,2,2>" : "ffn_up_kernel<bf16,128,64,2,2>";
-    p.down_name = H % 128 == 0 ? "ffn_down_kernel<bf16,128,128,2,2>" : "ffn_down_kernel<bf16,128,64,2,2>";
+    snprintf(p.up_name, sizeof p.up_name, "ffn_f32_kernel<up>");
+    snprintf(p.down_name, sizeof p.down_name, "ffn_f32_kernel<down>");
   } else {
-    p.block_m = 128;
-    p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
-                 align256((size_t)n * 4);
-    p.up_name = I % 128 == 0 ? "ffn_up_kernel<i8,128,128,2,2>" : "ffn_up_kernel<i8,128,64,2,2>";
-    p.down_name = H % 128 == 0 ? "ffn_down_kernel<i8,128,128,2,2>" : "ffn_down_kernel<i8,128,64,2,2>";
+    // shape class from the mean rows per expert: decode-sized (weight
+    // streaming, short tiles), mid (one 256-row tile per expert, waves split
+    // N), prefill (256 x 256 tiles, 2 x 2 waves of 128 x 128)
+    const double mean_rows = (double)n / E;
+    const int cls = mean_rows <= 24.0 ? 2 : (mean_rows <= 192.0 ? 1 : 0);
+    p.up_var = (I % 128 == 0 ? 0 : 3) + cls;
+    p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 3 : 6)) + cls;
+    if (p.up_var == 4) p.up_var = 3;
+    if (p.down_var == 7) p.down_var = 6;
+    p.block_m = cls == 2 ? 64 : 256;
+    const char* t = w_dtype == kI8 ? "i8" : "bf16";
+    const Variant u = kUpVar[p.up_var], d = kDownVar[p.down_var];
+    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<%s,up,%dx%d,%dx%d,S%d,R%d>", t, u.bm, u.bn, u.wm,
+             u.wn, u.stages, u.rowb);
+    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<%s,down,%dx%d,%dx%d,S%d,R%d>", t, d.bm, d.bn,
+             d.wm, d.wn, d.stages, d.rowb);
+    if (w_dtype == kBF16)
+      p.ws_bytes = align256((size_t)n * I * 2);
+    else
+      p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
+                   align256((size_t)n * 4);
   }
   p.max_tiles = align_max_tiles(T, k, E, p.block_m);
   return p;

@@ -129,6 +129,11 @@ moe_status ffn_checks(int32_t act_dtype, int32_t w_dtype, int32_t y_dtype, int64
                 act_dtype, w_dtype, y_dtype);
   if (w_dtype == MOE_I8 && (H % 128 != 0 || I % 128 != 0))
     return fail(MOE_ERR_UNSUPPORTED, "W8A8 needs H and I multiples of 128 (got %d, %d)", H, I);
+  // the GEMM kernels address activations and one expert's weights with
+  // 32-bit byte offsets
+  const int64_t eb = act_dtype == MOE_F32 ? 4 : (act_dtype == MOE_BF16 ? 2 : 1);
+  if (T * H * eb >= ((int64_t)1 << 32) || 2 * (int64_t)I * H * eb >= ((int64_t)1 << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "activations (T*H) and each expert's weights (2*I*H) must be < 4 GiB");
   return MOE_OK;
 }
 

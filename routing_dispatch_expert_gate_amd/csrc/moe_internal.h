@@ -12,6 +12,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxE = 256;
@@ -30,8 +31,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// silu(z) = z / (1 + e^-z)
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp): the
+// result is rounded to bf16 or re-quantised to int8 afterwards
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // 8 consecutive values <-> fp32 registers (16-byte aligned rows)
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
@@ -102,11 +106,12 @@ hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pos, const 
 
 // ffn_*.hip
 struct FfnPlan {
-  int block_m;
-  int64_t max_tiles;
-  size_t ws_bytes;   // h (+ row maxima for W8A8)
-  const char* up_name;
-  const char* down_name;
+  int block_m;        // row-tile height the align step must use
+  int64_t max_tiles;  // host-side upper bound on the number of row tiles
+  size_t ws_bytes;    // h (+ row maxima, codes and scales for W8A8)
+  int up_var, down_var;
+  char up_name[64];
+  char down_name[64];
 };
 FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype);
 // The FFN workspace carries h (and, for W8A8, row maxima, codes and scales)
