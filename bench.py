@@ -49,6 +49,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, Mixtral-shaped prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (to calibrate HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -178,6 +180,17 @@ def main() -> int:
         return 2
     import torch
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return 0
+
     import moe_synth
     import routing_dispatch_expert_gate_amd as moe
 
@@ -258,8 +271,8 @@ def main() -> int:
     else:
         roof = {"bound": "hbm", "achieved": up_bytes / up_s / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "ffn_up_kernel (" + dispatch.split("|")[2].strip().split("+")[0] + ")" \
-        if dispatch.count("|") >= 3 else "ffn_up_kernel"
+    roof["kernel"] = "up GEMM: " + (dispatch.split("|")[2].strip().split("+")[0]
+                                     if dispatch.count("|") >= 3 else "gg_kernel")
     roof["per_launch"] = {"flops": up_flops, "bytes": up_bytes, "ms": stage_ms["ffn_up"]}
     roof["traffic"] = traffic_for(spec.name, os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "csrc",
                                                           "ffn.hip"))

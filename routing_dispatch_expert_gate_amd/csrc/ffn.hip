@@ -185,8 +185,17 @@ void gg_kernel(const GemmArgs a) {
   static_assert(L * NW == NBLK, "copies must split evenly over the waves");
   static_assert(FM >= 1 && NF >= 1, "wave tile too small");
   static_assert(!UP || (NF % 2 == 0), "up needs paired G/U fragments");
-  static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS stages");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
+  // per-row epilogue scale, loaded once before the K loop so the epilogue
+  // does no dependent global loads: up W8A8 the token's activation scale,
+  // down the route weight (times the row's h scale for W8A8).  It lives in
+  // the same LDS allocation as the stages: with a second LDS object the
+  // compiler can no longer tell the stage reads from the in-flight copies
+  // and drains every copy (vmcnt(0)) before each stage.
+  constexpr bool ROWSCALE = (UP && I8) || !UP;
+  constexpr int SCALE_BYTES = ROWSCALE ? BM * 4 : 0;
+  static_assert(S >= 2 && S * STAGE + SCALE_BYTES <= 160 * 1024, "LDS stages");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE + SCALE_BYTES];
+  float* row_scale = reinterpret_cast<float*>(smem + S * STAGE);
 
   const int L0 = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = a.max_tiles * kGroupN;
@@ -241,6 +250,21 @@ void gg_kernel(const GemmArgs a) {
     }
   };
 
+  if constexpr (ROWSCALE) {
+    for (int r = tid; r < BM; r += NT) {
+      float v = 0.f;
+      if (r < rows) {
+        const int slot = a.sorted_slot[r0 + r];
+        if constexpr (UP) {
+          v = a.xs[slot / a.k];
+        } else {
+          v = a.topk_w ? a.topk_w[slot] : 1.f;
+          if (I8) v *= a.hs[r0 + r];
+        }
+      }
+      row_scale[r] = v;   // published by the K loop's first barrier
+    }
+  }
   // number of this wave's 32-row fragments that hold valid rows (uniform)
   int fmv = (rows - wm * WROWS + 31) / 32;
   fmv = fmv < 0 ? 0 : (fmv > FM ? FM : fmv);
@@ -354,7 +378,7 @@ void gg_kernel(const GemmArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
         const bool valid = row < rows;
-        const float xsr = valid ? a.xs[a.sorted_slot[r0 + row] / a.k] : 0.f;
+        const float xsr = row_scale[row];
         float m = 0.f;
 #pragma unroll
         for (int f = 0; f < NF / 2; ++f) {
@@ -383,8 +407,7 @@ void gg_kernel(const GemmArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
         if (row >= rows) continue;
-        float wr = a.topk_w ? a.topk_w[a.sorted_slot[r0 + row]] : 1.f;
-        if (I8) wr *= a.hs[r0 + row];
+        const float wr = row_scale[row];
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
           const int col = nb * BN + wn * WCOLS + f * 32 + (lane & 31);
