@@ -11,15 +11,16 @@
 //
 // gfx950 design:
 //  * One workgroup computes a BM x BN output tile of one row tile (one
-//    expert, <= BM rows) from the tile list; the grid is the host-known upper
-//    bound on tiles times the N blocks, and workgroups past the device-side
-//    tile count exit at once (no host synchronisation).
-//  * K advances 128 bytes at a time (64 bf16 or 128 int8).  Tiles of A and B
-//    go global -> registers -> LDS, double buffered: the next k-step's global
-//    loads are in flight while the MFMAs consume the current LDS stage.  Each
-//    128-byte LDS row is split in eight 16-byte chunks stored at chunk
-//    c ^ (row & 7), so the 32-row column reads of the MFMA operands spread
-//    over all banks.
+//    expert, <= BM rows) from the tile list.  The grid is the host-known
+//    upper bound on tiles times the N blocks; the workgroups with work are
+//    renumbered over the device-side tile count so that they spread evenly
+//    over the eight XCDs, consecutive ones (the N blocks of a raster group,
+//    then the next row tile) sharing an XCD's L2.
+//  * K advances ROWB bytes per stage (64 or 128: 32/64 bf16, 64/128 int8).
+//    Stages are copied from global memory straight into LDS with 16-byte
+//    direct-to-LDS loads, S stages deep, so no registers stage the tiles;
+//    rows are stored with an XOR swizzle of their 16-byte chunks so the
+//    MFMA operand reads spread over all LDS banks.
 //  * MFMA 32x32x16 bf16 (fp32 accumulate) or 32x32x32 int8 (int32
 //    accumulate).  In both a lane supplies 16 contiguous bytes of K for row
 //    (lane % 32) at k-chunk (lane / 32); the byte layout of the mainloop is
@@ -45,7 +46,6 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kI8 = 2;
 
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
 
 template <bool I8>
 struct Mma;
@@ -156,7 +156,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 //        wave holds matching G and U fragments, and the epilogue writes
 //        h = silu(G) * U;
 //  down: the B tile is BN rows of W2 and the epilogue writes w_r * acc.
-// K advances 64 bytes per stage (32 bf16 or 64 int8).  Stages are copied from
+// K advances ROWB bytes per stage.  Stages are copied from
 // global memory straight into LDS (16 bytes per lane per instruction, lane i
 // landing at 16*i of a 1 KiB block), S stages deep: stage kt+S-1 is in flight
 // while stage kt computes, with no staging registers.  Each wave issues the
@@ -197,14 +197,21 @@ void gg_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE + SCALE_BYTES];
   float* row_scale = reinterpret_cast<float*>(smem + S * STAGE);
 
-  const int L0 = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = a.max_tiles * kGroupN;
+  // The grid covers the host's bound on tiles; only the first
+  // num_tiles * n_blocks workgroups have work.  Those are renumbered over
+  // exactly that count, so the real work spreads evenly over the XCDs
+  // (renumbering over the whole grid would pile it onto the first few)
+  // and the idle workgroups, dispatched last, exit at once.
+  const int nt = __builtin_amdgcn_readfirstlane(*a.num_tiles);
+  const int nwork = nt * a.n_blocks;
+  if ((int)blockIdx.x >= nwork) return;
+  const int L0 = xcd_remap(blockIdx.x, nwork);
+  const int per_group = nt * kGroupN;
   const int g = L0 / per_group;
   const int rem = L0 - g * per_group;
   const int gs = min(kGroupN, a.n_blocks - g * kGroupN);
   const int tile = rem / gs;
   const int nb = g * kGroupN + (rem - tile * gs);
-  if (tile >= *a.num_tiles) return;
   // the tile descriptor is uniform: keep it in scalar registers so every
   // branch on it below is a scalar branch
   const int4 td = reinterpret_cast<const int4*>(a.tiles)[tile];
@@ -419,35 +426,35 @@ void gg_kernel(const GemmArgs a) {
 }
 
 // ----------------------------------------------------- W8A8 h quantise ---
-// One wave per sorted row of a tile: s = max|h| / 127 (1 if 0),
-// q = round-half-even(h / s) clamped to [-128, 127]; fp32 IEEE arithmetic.
+// One wave per sorted row: s = max|h| / 127 (1 if 0), q = round-half-even(h / s)
+// clamped to [-128, 127]; fp32 IEEE arithmetic.  The tile list covers rows
+// [0, N) in order, so N is the end of the last tile; waves past it exit.
 __global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ h,
                                                       const uint32_t* __restrict__ rowmax,
                                                       const int32_t* __restrict__ tiles,
                                                       const int32_t* __restrict__ num_tiles, int I,
                                                       int8_t* __restrict__ hq, float* __restrict__ hs) {
-  const int tile = blockIdx.x;
-  if (tile >= *num_tiles) return;
-  const int4 td = reinterpret_cast<const int4*>(tiles)[tile];
+  const int nt = *num_tiles;
+  if (nt <= 0) return;
+  const int4 last = reinterpret_cast<const int4*>(tiles)[nt - 1];
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= (int64_t)last.y + last.z) return;
   const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x >> 6; i < td.z; i += 4) {
-    const int64_t r = td.y + i;
-    const float am = __uint_as_float(rowmax[r]);
-    const float s = am == 0.f ? 1.f : am / 127.f;
-    for (int c = lane * 8; c < I; c += 512) {
-      float v[8];
-      load8(h + r * I + c, v);
-      uint32_t b[2] = {0u, 0u};
+  const float am = __uint_as_float(rowmax[r]);
+  const float s = am == 0.f ? 1.f : am / 127.f;
+  for (int c = lane * 8; c < I; c += 512) {
+    float v[8];
+    load8(h + r * I + c, v);
+    uint32_t b[2] = {0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float z = rintf(v[q] / s);
-        z = fminf(fmaxf(z, -128.f), 127.f);
-        b[q >> 2] |= (uint32_t)((int)z & 0xFF) << (8 * (q & 3));
-      }
-      *reinterpret_cast<uint2*>(hq + r * I + c) = make_uint2(b[0], b[1]);
+    for (int q = 0; q < 8; ++q) {
+      float z = rintf(v[q] / s);
+      z = fminf(fmaxf(z, -128.f), 127.f);
+      b[q >> 2] |= (uint32_t)((int)z & 0xFF) << (8 * (q & 3));
     }
-    if (lane == 0) hs[r] = s;
+    *reinterpret_cast<uint2*>(hq + r * I + c) = make_uint2(b[0], b[1]);
   }
+  if (lane == 0) hs[r] = s;
 }
 
 __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -614,11 +621,11 @@ hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const v
 
 template <bool I8>
 hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
-                       const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int H,
-                       int I, void* y, const FfnBufs& b, hipStream_t s) {
+                       const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int64_t rows,
+                       int H, int I, void* y, const FfnBufs& b, hipStream_t s) {
   if (I8)
-    quant_h_kernel<<<(unsigned)p.max_tiles, 256, 0, s>>>((const float*)b.h, b.rowmax, tiles,
-                                                         num_tiles, I, b.hq, b.hs);
+    quant_h_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>((const float*)b.h, b.rowmax, tiles,
+                                                              num_tiles, I, b.hq, b.hs);
   GemmArgs a{};
   a.act = I8 ? (const uint8_t*)b.hq : (const uint8_t*)b.h;
   a.w = (const uint8_t*)w2;
@@ -704,8 +711,8 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
     return hipGetLastError();
   }
   if (w_dtype == kBF16)
-    return launch_down<false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
-  return launch_down<true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
+    return launch_down<false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
+  return launch_down<true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
 }
 
 }  // namespace moe
