@@ -10,15 +10,17 @@
 // hierarchical atomics, fused map/mask/fill), three launches and no host sync:
 //   1. align_hist: each block histograms a contiguous slot range in LDS
 //      (LDS atomics only; the counts do not depend on their order).
-//   2. align_scan: one block turns the block histograms into per-block
-//      exclusive bases (column scan), applies the capacity, scans the kept
-//      counts into offsets, and writes the GEMM row-tile list.
-//   3. align_scatter: each block re-reads its range; four waves take
-//      contiguous quarters, count per wave (LDS atomics), scan over waves, and
-//      then rank their slots 64 at a time in slot order: the lanes holding
-//      the same expert are found with a ballot loop and ranked by popcount of
-//      the lower lanes.  Ranks therefore come from an ordered scan, never from
-//      the order atomics return in, so every output is deterministic.
+//   2. align_scan: one block sums the block histograms into per-expert
+//      counts, applies the capacity, scans the kept counts into offsets, and
+//      writes the GEMM row-tile list.
+//   3. align_scatter: each block sums the histograms of the blocks before it
+//      (its per-expert base), re-reads its range; four waves take contiguous
+//      quarters, count per wave (LDS atomics), scan over waves, and then rank
+//      their slots 64 at a time in slot order: the lanes holding the same
+//      expert are found with one ballot per bit of the expert id and ranked
+//      by popcount of the lower lanes.  Ranks therefore come from an ordered
+//      scan, never from the order atomics return in, so every output is
+//      deterministic.
 #include "moe_internal.h"
 
 namespace moe {
@@ -60,18 +62,22 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
-    int32_t* __restrict__ bhist, int nb, int E, int64_t n, int64_t cap, int bm, int64_t max_tiles,
+    const int32_t* __restrict__ bhist, int nb, int E, int64_t n, int64_t cap, int bm, int64_t max_tiles,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tiles,
     int32_t* __restrict__ num_tiles, int32_t* __restrict__ num_dropped) {
   __shared__ int tmp[kAlignThreads];
   const int e = threadIdx.x;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int v = bhist[(size_t)b * E + e];
-      bhist[(size_t)b * E + e] = total;
-      total += v;
-    }
+    // independent loads: the sum is in a fixed order, the loads need not be
+    int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int b = 0;
+    for (; b + 8 <= nb; b += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part[u] += bhist[(size_t)(b + u) * E + e];
+    for (; b < nb; ++b) part[0] += bhist[(size_t)b * E + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) total += part[u];
     counts[e] = total;
   }
   const int kept = e < E ? (cap > 0 && total > cap ? (int)cap : total) : 0;
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
 }
 
 __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int spb, const int32_t* __restrict__ bbase,
+    const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int spb, const int32_t* __restrict__ bhist,
     const int32_t* __restrict__ offsets, int64_t cap, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ pos) {
   __shared__ int32_t wh[4 * kMaxE];
@@ -117,7 +123,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
-    int run = bbase[(size_t)blockIdx.x * E + e];
+    // this block's base for expert e: slots of e in all earlier blocks
+    int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int nbefore = blockIdx.x;
+    int b = 0;
+    for (; b + 8 <= nbefore; b += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part[u] += bhist[(size_t)(b + u) * E + e];
+    for (; b < nbefore; ++b) part[0] += bhist[(size_t)b * E + e];
+    int run = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) run += part[u];
     for (int q = 0; q < 4; ++q) {
       const int v = wh[q * kMaxE + e];
       wh[q * kMaxE + e] = run;
@@ -132,16 +148,16 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     const bool in_range = s < w1;
     const int e = in_range ? ids[s] : -1;
     const bool valid = in_range && (unsigned)e < (unsigned)E;   // out-of-range ids are dropped
-    uint64_t active = __ballot(valid);
-    int rank = 0;
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int ev = __shfl(e, leader, kWave);
-      const uint64_t m = __ballot(valid && e == ev);
-      if (valid && e == ev) rank = my[ev] + __popcll(m & lt);
-      if (lane == leader) my[ev] += __popcll(m);
-      active &= ~m;
+    // lanes holding the same expert: agree on every bit of the id
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
     }
+    int rank = 0;
+    if (valid) rank = my[e] + __popcll(same & lt);   // every lane reads before any leader adds
+    if (valid && (same & lt) == 0) my[e] += __popcll(same);
     if (in_range) {
       const bool kept = valid && (cap <= 0 || rank < cap);
       const int p = kept ? offsets[e] + rank : -1;
@@ -166,7 +182,9 @@ int64_t align_max_tiles(int64_t T, int k, int E, int block_m) {
 AlignPlan plan_align(int64_t T, int k, int E) {
   AlignPlan p;
   const int64_t n = T * k;
+  // at most 1024 blocks: each scatter block sums the histograms before it
   p.slots_per_block = 1024;
+  if (n > (int64_t)1024 * 1024) p.slots_per_block = (int)(((n + 1023) / 1024 + 255) / 256 * 256);
   p.nblocks = (int)((n + p.slots_per_block - 1) / p.slots_per_block);
   if (p.nblocks < 1) p.nblocks = 1;
   p.ws_bytes = (size_t)p.nblocks * (size_t)E * sizeof(int32_t);
@@ -186,7 +204,9 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
                                                 counts, offsets, tiles, num_tiles, num_dropped);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  align_scatter_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, p.slots_per_block, bhist,
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  align_scatter_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, ebits, p.slots_per_block, bhist,
                                                           offsets, cap, sorted_slot, pos);
   return hipGetLastError();
 }

@@ -112,44 +112,6 @@ struct GemmArgs {
   int n_blocks, max_tiles;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// LDS row swizzles: chunk c (16 bytes) of row r is stored at c ^ sw(r), so
-// that sixteen consecutive rows read at one chunk fall on sixteen distinct
-// 16-byte slots of a 256-byte bank row, and any eight consecutive rows on
-// eight distinct slots of a 128-byte one.
-//  64-byte rows (4 chunks): period 32;  128-byte rows (8 chunks): period 16.
-template <int ROWB>
-__device__ __forceinline__ int swr(int r) {
-  if constexpr (ROWB == 64) return ((r >> 1) ^ (r >> 3)) & 3;
-  return ((r >> 1) ^ ((r & 1) << 2)) & 7;
-}
-
-// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left alone (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// wait until at most m*L of this wave's vector-memory ops are outstanding,
-// for a runtime m in [0, MMAX]
-template <int L, int MMAX>
-__device__ __forceinline__ void wait_vm_stages(int m) {
-  if constexpr (MMAX > 0) {
-    if (m >= MMAX) {
-      wait_vmcnt<MMAX * L>();
-      return;
-    }
-    wait_vm_stages<L, MMAX - 1>(m);
-  } else {
-    wait_vmcnt<0>();
-  }
-}
-// All of this wave's LDS reads have returned, then the workgroup barrier.
-// The memory clobber keeps every LDS access on its side of the barrier.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 // One BM x BN output tile of one row tile (one expert).  Waves form a WM x WN
 // grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments.
 //  up:   the B tile stacks BN/2 rows of W1 over the same BN/2 rows of W3, each

@@ -11,19 +11,21 @@
 //
 // Three variants, picked on the host by shape (never silently):
 //   kind 0  E <= 16: fp32 FMA.  Each wave keeps its slice of Wg (8 values of
-//           H per lane, all experts) in registers
-//           and re-uses it for 16 tokens; per-token partial logits are reduced
-//           across the 64 lanes with a multi-value butterfly (E values in
-//           log2(64) steps, halving the vector each step), then across waves
-//           through LDS.  Logits never leave the chip.
-//   kind 1  16 < E <= 64, bf16: MFMA 16x16x32 bf16 over a 64-expert slice,
-//           x tiles staged in LDS, logits kept in LDS, top-k in the same kernel.
-//   kind 2  64 < E <= 256, bf16: the same MFMA tile computes a [BT x 64]
-//           logits block per workgroup (experts split over workgroups so each
-//           CU streams a quarter of Wg instead of all of it, and K optionally
-//           split for decode-sized T), partial logits go to the workspace, and
-//           a second kernel sums the K splits in a fixed order and runs the
-//           wave top-k.  Deterministic: no floating-point atomics.
+//           H per lane, all experts) in registers and re-uses it for 16
+//           tokens, whose x chunks are all loaded before the first FMA;
+//           per-token partial logits are reduced across the 64 lanes with a
+//           multi-value butterfly (E values in log2(64) steps, halving the
+//           vector each step), then across waves through LDS.  Logits never
+//           leave the chip.
+//   kind 1  16 < E <= 64, bf16: MFMA 32x32x16 bf16 over 64-token x 64-expert
+//           tiles, K streamed through a deep direct-to-LDS pipeline, logits
+//           kept in LDS, top-k (and the per-token quantisation) in the same
+//           kernel.
+//   kind 2  otherwise (E up to 256, or few tokens), bf16: the same tile
+//           kernel, experts split over workgroups and K optionally split,
+//           writes partial logits to the workspace; a second kernel sums the
+//           K splits in a fixed order and runs the wave top-k.
+//           Deterministic: no floating-point atomics.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -82,6 +84,40 @@ __device__ void wave_topk_store(float v[4], int E, int k, int64_t t, int32_t* __
     ids[t * k + lane] = my_id;
     w[t * k + lane] = ex / se;
     if (prob) prob[t * k + lane] = ex / s;
+  }
+}
+
+// Top-k of one token by rank, for E <= 64: the token's E logits are in an LDS
+// row (16-byte aligned, padded with -inf to a multiple of 4, read by every
+// lane at once); lane l < E ranks expert
+// l by counting the experts ahead of it in (logit descending, id ascending)
+// order, and the k lanes of rank < k write selection rank.  The same order
+// and arithmetic as wave_topk_store, without its serial argmax rounds.
+__device__ void wave_topk_rank_store(const float* L, int E, int k, int64_t t, int32_t* __restrict__ ids,
+                                     float* __restrict__ w, float* __restrict__ prob) {
+  const int lane = threadIdx.x & 63;
+  const float v = lane < E ? L[lane] : -INFINITY;
+  int rank = 0;
+  for (int j = 0; j < E; j += 4) {
+    const float4 q = *reinterpret_cast<const float4*>(L + j);   // padded past E
+    rank += (q.x > v || (q.x == v && j < lane)) ? 1 : 0;
+    rank += (q.y > v || (q.y == v && j + 1 < lane)) ? 1 : 0;
+    rank += (q.z > v || (q.z == v && j + 2 < lane)) ? 1 : 0;
+    rank += (q.w > v || (q.w == v && j + 3 < lane)) ? 1 : 0;
+  }
+  const bool in = lane < E;
+  const uint64_t top = __ballot(in && rank == 0);
+  // the largest logit, from the lane of rank 0
+  const float mf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), __ffsll((unsigned long long)top) - 1));
+  const bool sel = in && rank < k;
+  const float ex = sel ? expf(v - mf) : 0.f;
+  const float se = wave_sum(ex);
+  float s = 0.f;
+  if (prob) s = wave_sum(in ? expf(v - mf) : 0.f);
+  if (sel) {
+    ids[t * k + rank] = lane;
+    w[t * k + rank] = ex / se;
+    if (prob) prob[t * k + rank] = ex / s;
   }
 }
 
@@ -144,237 +180,345 @@ __device__ __forceinline__ void multi_reduce(float (&a)[EP], int lane) {
 
 constexpr int kFmaTB = 16;   // tokens per workgroup
 
-template <int EP, int NCH, typename XT, typename WT, bool QUANT>
-__global__ __launch_bounds__(EP <= 8 ? 1024 : 512) void route_fma_kernel(
+// The raw bytes of 8 consecutive x values, loaded in one go and widened later
+// (so a batch of rows can be in flight before the first use).
+template <typename XT>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+  u32x4 a;
+  __device__ __forceinline__ void load(const uint16_t* p) { a = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void zero() { a = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
+};
+template <>
+struct Raw8<float> {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const u32x4*>(p)[0];
+    b = reinterpret_cast<const u32x4*>(p)[1];
+  }
+  __device__ __forceinline__ void zero() { a = b = u32x4{0u, 0u, 0u, 0u}; }
+  __device__ __forceinline__ void get(float (&v)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+};
+
+// WIDE: more than 8 waves (H > 4096, E <= 8 only), 1024 threads and hence at
+// most 128 VGPRs: fewer rows in flight.
+// A workgroup's token rows are loaded in batches of PF rows, each batch before
+// its first FMA; the per-token partial logits of RB
+// tokens are reduced together, RB*EP values in one butterfly, so the
+// shuffles of a level are independent of one another.
+template <int EP, bool WIDE, typename XT, typename WT, bool QUANT>
+__global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
+  constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);   // rows per load batch
+  constexpr int RB = 1;   // rows per butterfly: with more, LLVM turns the butterfly selects into dynamic indexing
+  static_assert(PF % RB == 0 && kFmaTB % PF == 0, "batches");
   __shared__ float part[16][kFmaTB][EP];
   __shared__ float amax_s[16][kFmaTB];
+  __shared__ __attribute__((aligned(16))) float lg[kFmaTB][16];
   const int nw = blockDim.x >> 6;
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
 
-  // this lane's slice of Wg: NCH chunks of 8 consecutive h, for every expert
-  float wr[NCH][EP][8];
-  int h0[NCH];
-  bool hv[NCH];
+  // this lane's slice of Wg: 8 consecutive h, for every expert
+  float wr[EP][8];
+  const int h0 = (wv * 64 + lane) * 8;
+  const bool hv = h0 < H;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    h0[c] = ((wv * NCH + c) * 64 + lane) * 8;
-    hv[c] = h0[c] < H;
+  for (int e = 0; e < EP; ++e) {
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (hv && e < E) load8(wg + (size_t)e * H + h0, v);
 #pragma unroll
-    for (int e = 0; e < EP; ++e) {
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (hv[c] && e < E) load8(wg + (size_t)e * H + h0[c], v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wr[c][e][i] = v[i];
-    }
+    for (int i = 0; i < 8; ++i) wr[e][i] = v[i];
   }
 
   const int64_t t0 = (int64_t)blockIdx.x * kFmaTB;
   const int ntok = (int)((T - t0) < kFmaTB ? (T - t0) : kFmaTB);
-  for (int tt = 0; tt < ntok; ++tt) {
-    const XT* xrow = x + (t0 + tt) * H;
-    float acc[EP];
+  for (int tb = 0; tb < ntok; tb += PF) {
+    Raw8<XT> r[PF];
 #pragma unroll
-    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-    float am = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (!hv[c]) continue;
-      float v[8];
-      load8(xrow + h0[c], v);
-#pragma unroll
-      for (int e = 0; e < EP; ++e)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[e] = fmaf(v[i], wr[c][e][i], acc[e]);
-      if (QUANT)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    for (int u = 0; u < PF; ++u) {
+      if (hv && tb + u < ntok)
+        r[u].load(x + (t0 + tb + u) * H + h0);
+      else
+        r[u].zero();
     }
-    multi_reduce<EP>(acc, lane);
-    if ((lane & (64 / EP - 1)) == 0) part[wv][tt][lane / (64 / EP)] = acc[0];
-    if (QUANT) {
-      am = wave_max(am);
-      if (lane == 0) amax_s[wv][tt] = am;
+#pragma unroll
+    for (int ub = 0; ub < PF; ub += RB) {
+      if (tb + ub >= ntok) break;
+      float acc[RB * EP];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        float v[8];
+        r[ub + u].get(v);
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+          float a = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaf(v[i], wr[e][i], a);
+          acc[u * EP + e] = a;
+        }
+        if (QUANT) {
+          float am = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+          am = wave_max(am);
+          if (lane == 0 && tb + ub + u < ntok) amax_s[wv][tb + ub + u] = am;
+        }
+      }
+      // lane l ends with value l / (64 / (RB*EP)): token l / (64/RB), expert (l % (64/RB)) / (64/(RB*EP))
+      multi_reduce<RB * EP>(acc, lane);
+      constexpr int LPV = 64 / (RB * EP);   // lanes per value
+      const int vi = lane / LPV;
+      const int u = vi / EP, e = vi - u * EP;
+      if ((lane & (LPV - 1)) == 0 && tb + ub + u < ntok) part[wv][tb + ub + u][e] = acc[0];
     }
   }
   __syncthreads();
 
-  for (int tt = wv; tt < ntok; tt += nw) {
-    float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (lane < E) {
-      float s = 0.f;
-      for (int q = 0; q < nw; ++q) s += part[q][tt][lane];
-      if (bias) s += bias[lane];
-      v[0] = s;
+  // logits (plus bias) of the block's tokens, rows padded with -inf
+  for (int i = threadIdx.x; i < kFmaTB * 16; i += blockDim.x) {
+    const int tt = i >> 4, e = i & 15;
+    float s = -INFINITY;
+    if (tt < ntok && e < E) {
+      s = 0.f;
+      for (int q = 0; q < nw; ++q) s += part[q][tt][e];
+      if (bias) s += bias[e];
     }
-    wave_topk_store(v, E, k, t0 + tt, ids, w, prob);
+    lg[tt][e] = s;
   }
+  __syncthreads();
+  for (int tt = wv; tt < ntok; tt += nw) wave_topk_rank_store(&lg[tt][0], E, k, t0 + tt, ids, w, prob);
 
   if (QUANT) {
-    for (int tt = 0; tt < ntok; ++tt) {
-      float am = 0.f;
-      for (int q = 0; q < nw; ++q) am = fmaxf(am, amax_s[q][tt]);
-      const float s = row_scale(am);
-      const int64_t t = t0 + tt;
+    for (int tb = 0; tb < ntok; tb += PF) {
+      Raw8<XT> r[PF];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        if (!hv[c]) continue;
-        float v[8];
-        load8(x + t * H + h0[c], v);
-        *reinterpret_cast<uint2*>(xq + t * H + h0[c]) = quant8(v, s);
+      for (int u = 0; u < PF; ++u) {
+        if (hv && tb + u < ntok)
+          r[u].load(x + (t0 + tb + u) * H + h0);
+        else
+          r[u].zero();
       }
-      if (threadIdx.x == 0) xs[t] = s;
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        const int tt = tb + u;
+        if (tt >= ntok) break;
+        float am = 0.f;
+        for (int q = 0; q < nw; ++q) am = fmaxf(am, amax_s[q][tt]);
+        const float s = row_scale(am);
+        if (hv) {
+          float v[8];
+          r[u].get(v);
+          *reinterpret_cast<uint2*>(xq + (t0 + tt) * H + h0) = quant8(v, s);
+        }
+        if (threadIdx.x == 0) xs[t0 + tt] = s;
+      }
     }
   }
 }
 
 // ------------------------------------------------------- kinds 1 and 2 ----
-// MFMA 16x16x32 bf16: lane l supplies A[m = l%16][k = 8*(l/16) .. +8] and
-// B[k = 8*(l/16) .. +8][n = l%16]; it receives D[m = 4*(l/16) + i][n = l%16].
-// Rows of the LDS x tile are 64 bf16 (8 chunks of 16 B); chunk c of row r is
-// stored at chunk c ^ (r & 7) so the 16-lane column reads are conflict-free.
-template <int BT, bool FUSED, bool QUANT>
-__global__ __launch_bounds__(256) void route_mfma_kernel(
+// Gate logits on MFMA: one workgroup computes a 64-token x 64-expert tile of
+// x Wg^T over a K range (all of H unless split).  K is streamed 64 bf16 (128
+// bytes) per stage from global memory straight into LDS, kRS stages deep;
+// waves form a 2 x 2 grid, each owning one 32 x 32 MFMA 32x32x16 fragment.
+// Token rows past T and expert rows past E copy a valid row; their results
+// are never used.  Fused (E <= 64, no K split): the logits tile goes to LDS
+// and each wave runs the top-k of 16 tokens; with quantisation the row
+// absmax is folded from the A stages as they pass through LDS, and the row is
+// re-read once to write its codes.  Otherwise the tile is written to the
+// workspace for route_topk_kernel.
+constexpr int kRT = 64;                        // tokens per tile
+constexpr int kRE = 64;                        // experts per tile
+constexpr int kRRow = 128;                     // bytes of K per stage row
+constexpr int kRS = 8;                         // stages
+constexpr int kRStage = (kRT + kRE) * kRRow;   // 16 KiB
+constexpr int kRL = (kRT + kRE) * kRRow / 1024 / 4;   // 1 KiB copies per wave per stage
+
+template <bool FUSED, bool QUANT>
+__global__ __launch_bounds__(256) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
-    int64_t T, int H, int E, int k, int kchunk, float* __restrict__ part,
-    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob,
-    int8_t* __restrict__ xq, float* __restrict__ xs) {
-  constexpr int MF = BT / 16;
-  constexpr int APASS = (BT * 8 + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BT * 64];
-  __shared__ float Ls[FUSED ? BT : 1][FUSED ? 65 : 1];
-  __shared__ float rowmax_s[BT];
+    int64_t T, int H, int E, int k, int kchunk, float* __restrict__ part, int32_t* __restrict__ ids,
+    float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
+  static_assert(!QUANT || FUSED, "quantisation is fused only with the top-k");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRS * kRStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int64_t t0 = (int64_t)blockIdx.x * kRT;
+  const int e0 = blockIdx.y * kRE;
+  const int64_t rowbytes = (int64_t)H * 2;
+  const int nk = kchunk / kRRow;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * BT;
-  const int eb = blockIdx.y * 64 + wv * 16 + (lane & 15);
-  const bool e_ok = eb < E;
-  const uint16_t* brow = wg + (size_t)(e_ok ? eb : 0) * H + (lane >> 4) * 8;
-  const int kbeg = blockIdx.z * kchunk;
-  const int nk = kchunk / 64;
-
-  const uint16_t* arow[APASS];
-  int alds[APASS];
-  bool aval[APASS];
+  // this wave's copies: 1 KiB block q = wv*kRL + j holds stage rows 8q..8q+7
+  // (rows 0..63 tokens, 64..127 experts); lane i copies row 8q + i/8, LDS
+  // chunk i%8, which holds logical chunk (i%8) ^ sw(row)
+  const uint8_t* src[kRL];
 #pragma unroll
-  for (int p = 0; p < APASS; ++p) {
-    const int idx = tid + 256 * p;
-    const int r = idx >> 3, c = idx & 7;
-    aval[p] = idx < BT * 8 && t0 + r < T;
-    arow[p] = x + (aval[p] ? (t0 + r) * H : 0) + c * 8;
-    alds[p] = r * 64 + ((c ^ (r & 7)) * 8);
+  for (int j = 0; j < kRL; ++j) {
+    const int q = wv * kRL + j;
+    const int srow = q * 8 + (lane >> 3);
+    const int trow = srow & 63;
+    const int c = (lane & 7) ^ swr<kRRow>(trow);
+    int64_t grow;
+    const uint8_t* base;
+    if (srow < kRT) {
+      grow = t0 + trow < T ? t0 + trow : T - 1;
+      base = reinterpret_cast<const uint8_t*>(x);
+    } else {
+      grow = e0 + trow < E ? e0 + trow : 0;
+      base = reinterpret_cast<const uint8_t*>(wg);
+    }
+    src[j] = base + grow * rowbytes + (int64_t)blockIdx.z * kchunk + c * 16;
   }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % kRS) * kRStage;
+#pragma unroll
+    for (int j = 0; j < kRL; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void*)(src[j] + kt * kRRow),
+                                       (lds_void*)(st + (wv * kRL + j) * 1024), 16, 0, 0);
+  };
+  int lo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int r = lane & 31;
+    lo[s] = r * kRRow + (((2 * s + (lane >> 5)) ^ swr<kRRow>(r)) << 4);
+  }
+  // quantisation: thread tid folds |x| of stage row tid/4, 16 values
+  const int qrow = tid >> 2;
+  int qoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) qoff[i] = qrow * kRRow + (((2 * (tid & 3) + i) ^ swr<kRRow>(qrow)) << 4);
+  uint32_t amax = 0;   // bf16 magnitude bits
 
-  f32x4 acc[MF];
+  f32x16 acc = {};
 #pragma unroll
-  for (int i = 0; i < MF; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float am[APASS];
-  uint4 areg[APASS];
+  for (int p = 0; p < kRS - 1; ++p)
+    if (p < nk) issue(p);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int after = nk - 1 - kt < kRS - 2 ? nk - 1 - kt : kRS - 2;
+    wait_vm_stages<kRL, kRS - 2>(after);
+    lds_barrier();
+    if (kt + kRS - 1 < nk) issue(kt + kRS - 1);
+    const uint8_t* As = smem + (kt % kRS) * kRStage;
+    const uint8_t* Bs = As + kRT * kRRow;
+    u32x4 af[4], bf[4];
 #pragma unroll
-  for (int p = 0; p < APASS; ++p) am[p] = 0.f;
-
-  auto load_a = [&](int kk) {
+    for (int s = 0; s < 4; ++s) {
+      af[s] = *reinterpret_cast<const u32x4*>(As + wm * 32 * kRRow + lo[s]);
+      bf[s] = *reinterpret_cast<const u32x4*>(Bs + wn * 32 * kRRow + lo[s]);
+    }
+    if constexpr (QUANT) {
 #pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      areg[p] = aval[p] ? *reinterpret_cast<const uint4*>(arow[p] + kk) : make_uint4(0, 0, 0, 0);
-      if (QUANT) {
-        const uint32_t u[4] = {areg[p].x, areg[p].y, areg[p].z, areg[p].w};
+      for (int i = 0; i < 2; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(As + qoff[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          am[p] = fmaxf(am[p], fabsf(__uint_as_float(u[i] << 16)));
-          am[p] = fmaxf(am[p], fabsf(__uint_as_float(u[i] & 0xFFFF0000u)));
+        for (int j = 0; j < 4; ++j) {
+          amax = max(amax, v[j] & 0x7FFFu);
+          amax = max(amax, (v[j] >> 16) & 0x7FFFu);
         }
       }
     }
-  };
-  auto store_a = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < APASS; ++p)
-      if (tid + 256 * p < BT * 8) *reinterpret_cast<uint4*>(&As[buf][alds[p]]) = areg[p];
-  };
-  const bf16x8 bzero = {};
-  auto load_b = [&](int kk, bf16x8& b0, bf16x8& b1) {
-    b0 = e_ok ? *reinterpret_cast<const bf16x8*>(brow + kk) : bzero;
-    b1 = e_ok ? *reinterpret_cast<const bf16x8*>(brow + kk + 32) : bzero;
-  };
-
-  bf16x8 b0, b1;
-  load_a(kbeg);
-  load_b(kbeg, b0, b1);
-  store_a(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bf16x8 cb0 = b0, cb1 = b1;
-    if (kt + 1 < nk) {
-      load_a(kbeg + (kt + 1) * 64);
-      load_b(kbeg + (kt + 1) * 64, b0, b1);
-    }
-#pragma unroll
-    for (int mi = 0; mi < MF; ++mi) {
-      const int r = mi * 16 + (lane & 15);
-      const int c0 = lane >> 4;
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&As[cur][r * 64 + ((c0 ^ (r & 7)) * 8)]);
-      const bf16x8 a1 =
-          *reinterpret_cast<const bf16x8*>(&As[cur][r * 64 + (((c0 + 4) ^ (r & 7)) * 8)]);
-      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, cb0, acc[mi], 0, 0, 0);
-      acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, cb1, acc[mi], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_a(cur ^ 1);
-    __syncthreads();
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[s]),
+                                                    __builtin_bit_cast(bf16x8, bf[s]), acc, 0, 0, 0);
   }
 
-  if (!FUSED) {
+  if constexpr (!FUSED) {
+    const int e = e0 + wn * 32 + (lane & 31);
 #pragma unroll
-    for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t t = t0 + mi * 16 + 4 * (lane >> 4) + i;
-        if (t < T && e_ok) part[((size_t)blockIdx.z * T + t) * E + eb] = acc[mi][i];
-      }
+    for (int v = 0; v < 16; ++v) {
+      const int64_t t = t0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[v];
+    }
     return;
   }
 
-  // fused: logits of this block's tokens stay in LDS
+  // fused: the logits tile and the row maxima go to LDS (stage memory reused)
+  constexpr int LSTR = kRE + 4;                       // 16-byte aligned rows
+  float* Ls = reinterpret_cast<float*>(smem);        // [kRT][LSTR]
+  float* rmax = Ls + kRT * LSTR;                     // [kRT]
+  lds_barrier();
 #pragma unroll
-  for (int mi = 0; mi < MF; ++mi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Ls[mi * 16 + 4 * (lane >> 4) + i][wv * 16 + (lane & 15)] = acc[mi][i];
-  if (QUANT) {
-#pragma unroll
-    for (int p = 0; p < APASS; ++p) {
-      float v = am[p];
-      v = fmaxf(v, __shfl_xor(v, 1, kWave));
-      v = fmaxf(v, __shfl_xor(v, 2, kWave));
-      v = fmaxf(v, __shfl_xor(v, 4, kWave));
-      const int idx = tid + 256 * p;
-      if ((idx & 7) == 0 && idx < BT * 8) rowmax_s[idx >> 3] = v;
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int e = wn * 32 + (lane & 31);
+    Ls[r * LSTR + e] = acc[v] + (bias && e < E ? bias[e] : 0.f);
+  }
+  if constexpr (QUANT) {
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
+    if ((tid & 3) == 0) rmax[qrow] = __uint_as_float(amax << 16);
   }
   __syncthreads();
-  for (int tt = wv; tt < BT; tt += 4) {
-    if (t0 + tt >= T) break;
-    float v[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (lane < E) v[0] = Ls[tt][lane] + (bias ? bias[lane] : 0.f);
-    wave_topk_store(v, E, k, t0 + tt, ids, w, prob);
-  }
-  if (QUANT) {
-    const int cpr = H / 8;   // 8-value chunks per row
-    for (int q = tid; q < BT * cpr; q += 256) {
-      const int rr = q / cpr, c = q - rr * cpr;
-      const int64_t t = t0 + rr;
-      if (t >= T) break;
-      float v[8];
-      load8(x + t * H + c * 8, v);
-      *reinterpret_cast<uint2*>(xq + t * H + c * 8) = quant8(v, row_scale(rowmax_s[rr]));
+  // quantisation: codes of 16 values per thread and step, QB steps' loads in
+  // flight; the first batch is issued before the top-k so it lands meanwhile
+  constexpr int QB = 8;
+  const int cpr = H / 16;
+  const int64_t rows = T - t0 < kRT ? T - t0 : kRT;
+  const int total = QUANT ? (int)rows * cpr : 0;
+  u32x4 raw[QB][2];
+  auto qload = [&](int q0) {
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      const int q = q0 + u * 256;
+      if (q < total) {
+        const int rr = q / cpr, c = q - rr * cpr;
+        const u32x4* p = reinterpret_cast<const u32x4*>(x + (t0 + rr) * H + c * 16);
+        raw[u][0] = p[0];
+        raw[u][1] = p[1];
+      }
     }
-    if (tid < BT && t0 + tid < T) xs[t0 + tid] = row_scale(rowmax_s[tid]);
+  };
+  if constexpr (QUANT) qload(tid);
+  for (int tt = wv; tt < kRT; tt += 4) {
+    if (t0 + tt >= T) break;
+    wave_topk_rank_store(Ls + tt * LSTR, E, k, t0 + tt, ids, w, prob);
+  }
+  if constexpr (QUANT) {
+    for (int q0 = tid; q0 < total; q0 += QB * 256) {
+      if (q0 != tid) qload(q0);
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int q = q0 + u * 256;
+        if (q < total) {
+          const int rr = q / cpr, c = q - rr * cpr;
+          const float sc = row_scale(rmax[rr]);
+          u32x4 out;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[2 * i] = __uint_as_float(raw[u][hh][i] << 16);
+              v[2 * i + 1] = __uint_as_float(raw[u][hh][i] & 0xFFFF0000u);
+            }
+            const uint2 b = quant8(v, sc);
+            out[2 * hh] = b.x;
+            out[2 * hh + 1] = b.y;
+          }
+          *reinterpret_cast<u32x4*>(xq + (t0 + rr) * H + c * 16) = out;
+        }
+      }
+    }
+    if (tid < rows) xs[t0 + tid] = row_scale(rmax[tid]);
   }
 }
 
@@ -386,71 +530,79 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float v[4];
+  // K splits summed in a fixed order; 8 splits of each of the lane's 4
+  // experts are loaded at once
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int z0 = 0; z0 < ks; z0 += 8) {
+    float q[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = lane + 64 * j;
+        q[j][u] = (e < E && z0 + u < ks) ? part[((size_t)(z0 + u) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] += ((q[j][0] + q[j][1]) + (q[j][2] + q[j][3])) + ((q[j][4] + q[j][5]) + (q[j][6] + q[j][7]));
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    if (e < E) {
-      float s = 0.f;
-      for (int z = 0; z < ks; ++z) s += part[((size_t)z * T + t) * E + e];
-      v[j] = s + (bias ? bias[e] : 0.f);
-    } else {
-      v[j] = -INFINITY;
-    }
+    v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : -INFINITY;
   }
   wave_topk_store(v, E, k, t, ids, w, prob);
   if (QUANT) wave_quant_row(x + t * H, H, xq + t * H, xs + t);
 }
 
-template <int EP, int NCH, typename XT, typename WT>
+template <int EP, bool WIDE, typename XT, typename WT>
 hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                       int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                       int8_t* xq, float* xs, hipStream_t s) {
   const dim3 grid((unsigned)((T + kFmaTB - 1) / kFmaTB));
   const dim3 block(64 * p.nw);
   if (xq)
-    route_fma_kernel<EP, NCH, XT, WT, true><<<grid, block, 0, s>>>(
+    route_fma_kernel<EP, WIDE, XT, WT, true><<<grid, block, 0, s>>>(
         (const XT*)x, (const WT*)wg, bias, T, H, E, k, ids, w, prob, xq, xs);
   else
-    route_fma_kernel<EP, NCH, XT, WT, false><<<grid, block, 0, s>>>(
+    route_fma_kernel<EP, WIDE, XT, WT, false><<<grid, block, 0, s>>>(
         (const XT*)x, (const WT*)wg, bias, T, H, E, k, ids, w, prob, xq, xs);
   return hipGetLastError();
 }
 
-template <int EP, int NCH>
+template <int EP, bool WIDE>
 hipError_t launch_fma_dt(const RoutePlan& p, const void* x, int xd, const void* wg, int wd,
                          const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
                          float* prob, int8_t* xq, float* xs, hipStream_t s) {
   if (xd == kF32 && wd == kF32)
-    return launch_fma<EP, NCH, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
   if (xd == kF32 && wd == kBF16)
-    return launch_fma<EP, NCH, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
   if (xd == kBF16 && wd == kF32)
-    return launch_fma<EP, NCH, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-  return launch_fma<EP, NCH, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+  return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
 }
 
-template <int BT>
 hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                        int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                        int8_t* xq, float* xs, void* ws, hipStream_t s) {
-  const unsigned bx = (unsigned)((T + BT - 1) / BT);
+  const unsigned bx = (unsigned)((T + kRT - 1) / kRT);
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)wg;
   if (p.kind == 1) {
     const dim3 grid(bx, 1, 1);
     if (xq)
-      route_mfma_kernel<BT, true, true><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, H, nullptr,
-                                                             ids, w, prob, xq, xs);
+      route_gemm_kernel<true, true><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H, nullptr, ids, w,
+                                                         prob, xq, xs);
     else
-      route_mfma_kernel<BT, true, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, H, nullptr,
-                                                              ids, w, prob, xq, xs);
+      route_gemm_kernel<true, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H, nullptr, ids, w,
+                                                          prob, xq, xs);
     return hipGetLastError();
   }
   float* part = (float*)ws;
-  const dim3 grid(bx, (unsigned)((E + 63) / 64), (unsigned)p.ks);
-  route_mfma_kernel<BT, false, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, H / p.ks, part,
-                                                           ids, w, prob, xq, xs);
+  const dim3 grid(bx, (unsigned)((E + kRE - 1) / kRE), (unsigned)p.ks);
+  route_gemm_kernel<false, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H / p.ks, part, ids,
+                                                       w, prob, xq, xs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 g2((unsigned)((T + 3) / 4));
@@ -476,16 +628,17 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
     return p;
   }
   if (x_dtype != kBF16 || wg_dtype != kBF16 || E % 16 != 0 || E > kMaxE) return p;
-  p.bt = T >= 4096 ? 64 : (T >= 1024 ? 32 : 16);
-  const int64_t tblocks = (T + p.bt - 1) / p.bt;
-  if (E <= 64 && tblocks >= 64) {
+  p.bt = kRT;
+  const int64_t tblocks = (T + kRT - 1) / kRT;
+  if (E <= kRE && tblocks >= 128) {
     p.kind = 1;
     return p;
   }
   p.kind = 2;
-  const int64_t blocks = tblocks * ((E + 63) / 64);
+  const int64_t blocks = tblocks * ((E + kRE - 1) / kRE);
+  // split K while the grid is small: each split keeps >= 2 stages of 64 values
   int ks = 1;
-  while (blocks * ks < 256 && H % (ks * 2 * 64) == 0 && H / (ks * 2) >= 256) ks *= 2;
+  while (blocks * ks < 256 && H % (128 * ks) == 0 && H >= 256 * ks) ks *= 2;
   p.ks = ks;
   p.ws_bytes = (size_t)ks * (size_t)T * (size_t)E * sizeof(float);
   return p;
@@ -496,20 +649,16 @@ hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const vo
                         int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
                         hipStream_t s) {
   if (p.kind == 0) {
+    if (E <= 8 && p.nw > 8)
+      return launch_fma_dt<8, true>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
+                                    xs, s);
     if (E <= 8)
-      return launch_fma_dt<8, 1>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
+      return launch_fma_dt<8, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
                                  xs, s);
-    return launch_fma_dt<16, 1>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
+    return launch_fma_dt<16, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
                                 xs, s);
   }
-  switch (p.bt) {
-    case 64:
-      return launch_mfma<64>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, s);
-    case 32:
-      return launch_mfma<32>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, s);
-    default:
-      return launch_mfma<16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, s);
-  }
+  return launch_mfma(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, s);
 }
 
 }  // namespace moe

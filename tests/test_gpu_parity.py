@@ -130,6 +130,46 @@ def test_route_zero_rows_and_quant_edge_values():
         np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
 
 
+# one case per router variant (the dispatch name is checked, so each case
+# really takes its path): FMA for E <= 16 at ordinary and wide H, the fused
+# MFMA tile kernel (E <= 64, many tokens, ragged last tile, bias), and the MFMA
+# logits + top-k pair with and without a K split
+ROUTE_PATHS = [
+    (moe_synth.Spec("fma_wide_bf16", 37, 8192, 8, 2, 64, wg_dtype="f32"), True, "route_fma_kernel"),
+    (moe_synth.Spec("fma_wide_f32", 21, 6144, 4, 2, 64, x_dtype="f32", wg_dtype="f32"), True,
+     "route_fma_kernel"),
+    (moe_synth.Spec("fma_e16_f32x", 50, 4096, 16, 4, 64, x_dtype="f32"), True, "route_fma_kernel"),
+    (moe_synth.Spec("fused_e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
+     "route_gemm_kernel<fused>"),
+    (moe_synth.Spec("fused_e32", 128 * 64 + 1, 128, 32, 3, 64), False, "route_gemm_kernel<fused>"),
+    (moe_synth.Spec("logits_e64_splitk", 16, 4096, 64, 6, 64), True, "route_gemm_kernel<logits>"),
+    (moe_synth.Spec("logits_e128", 300, 1024, 128, 4, 64), False, "route_gemm_kernel<logits>"),
+    (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel<logits>"),
+]
+
+
+@pytest.mark.parametrize("spec,quant,path", ROUTE_PATHS, ids=[p[0].name for p in ROUTE_PATHS])
+def test_route_paths(spec, quant, path):
+    moe = _moe()
+    i = moe_synth.make_inputs(spec, 99, with_experts=False)
+    r = moe.route(to_dev(i.x), to_dev(i.wg), spec.k, bias=to_dev(i.bias), want_p=True, quant=quant)
+    torch.cuda.synchronize()
+    print(moe.last_dispatch())
+    d = moe.last_dispatch()
+    assert path in d
+    if "splitk" in spec.name or spec.name == "logits_e128":
+        assert "ksplit=1)" not in d            # K really split
+    ro = oracle.route(oracle.to_f64(i.x, spec.x_dtype), oracle.to_f64(i.wg, spec.wg_dtype), spec.k, i.bias)
+    same = check_ids(r["ids"].cpu().numpy(), ro)
+    assert np.abs(r["w"].cpu().numpy()[same] - ro["w"][same]).max() <= 1e-5
+    assert np.abs(r["p"].cpu().numpy()[same] - ro["p_sel"][same]).max() <= 1e-5
+    if quant:
+        xf = i.x if spec.x_dtype == "f32" else moe_synth.bf16_bits_as_f32(i.x)
+        xq_o, xs_o = oracle.quant_per_token_int8(xf)
+        np.testing.assert_array_equal(r["xq"].cpu().numpy(), xq_o)
+        np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
+
+
 # ------------------------------------------------------------------ align
 def _check_align(ids, E, C, bm):
     moe = _moe()
