@@ -78,8 +78,6 @@ __device__ __forceinline__ int xcd_remap(int P, int G) {
   return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
-constexpr int kGroupN = 8;   // N blocks per raster group
-
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -113,7 +111,11 @@ struct GemmArgs {
 };
 
 // One BM x BN output tile of one row tile (one expert).  Waves form a WM x WN
-// grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments.
+// grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments; with
+// four waves per SIMD one wave's MFMAs cover another's copy and LDS waits.
+// Raster: groups of GN N blocks; within a group the row tiles run fastest,
+// so consecutive workgroups (one XCD) share A rows across GN N blocks and
+// B rows across the row tiles of one expert.
 //  up:   the B tile stacks BN/2 rows of W1 over the same BN/2 rows of W3, each
 //        wave holds matching G and U fragments, and the epilogue writes
 //        h = silu(G) * U;
@@ -128,7 +130,7 @@ struct GemmArgs {
 // K loop is specialised on their number), and rows past the valid ones copy
 // the tile's first row: their accumulators are never stored (an MFMA output
 // row depends only on its A row).
-template <bool I8, bool UP, int BM, int BN, int WM, int WN, int S, int ROWB>
+template <bool I8, bool UP, int BM, int BN, int WM, int WN, int S, int ROWB, int GN>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(
     (BM / WM) * (BN / WN) <= 128 * 64 && 2 * S * (BM + BN) * ROWB <= 160 * 1024 ? 2 : 1)))
@@ -168,12 +170,12 @@ void gg_kernel(const GemmArgs a) {
   const int nwork = nt * a.n_blocks;
   if ((int)blockIdx.x >= nwork) return;
   const int L0 = xcd_remap(blockIdx.x, nwork);
-  const int per_group = nt * kGroupN;
+  const int per_group = nt * GN;
   const int g = L0 / per_group;
   const int rem = L0 - g * per_group;
-  const int gs = min(kGroupN, a.n_blocks - g * kGroupN);
+  const int gs = min(GN, a.n_blocks - g * GN);
   const int tile = rem / gs;
-  const int nb = g * kGroupN + (rem - tile * gs);
+  const int nb = g * GN + (rem - tile * gs);
   // the tile descriptor is uniform: keep it in scalar registers so every
   // branch on it below is a scalar branch
   const int4 td = reinterpret_cast<const int4*>(a.tiles)[tile];
@@ -507,22 +509,24 @@ FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype) {
 }
 
 struct Variant {
-  int bm, bn, wm, wn, stages, rowb;
+  int bm, bn, wm, wn, stages, rowb, gn;
 };
 // Rows: tile family (BN) by the divisibility of I (up) or H (down); columns:
-// prefill (256 x BN, 2 x 2 waves, 128-byte stage rows: every 1 KiB copy is 8
-// whole cache lines), mid (256 x BN, waves split N), decode (64 x BN, deeper
-// pipeline for weight streaming).  Where a family has no distinct mid tile
-// the prefill one is reused (entries 4 up, 7 down).
-constexpr Variant kUpVar[] = {{256, 256, 2, 2, 2, 128}, {256, 256, 1, 4, 4, 64}, {64, 256, 1, 4, 6, 64},
-                              {256, 128, 2, 2, 3, 128}, {256, 128, 2, 2, 3, 128}, {64, 128, 1, 2, 6, 64}};
-constexpr Variant kDownVar[] = {{256, 256, 2, 2, 2, 128}, {256, 256, 1, 4, 4, 64}, {64, 256, 1, 4, 6, 64},
-                                {256, 128, 2, 2, 3, 128}, {256, 128, 1, 4, 4, 64}, {64, 128, 1, 4, 6, 64},
-                                {256, 64, 2, 2, 3, 128},  {256, 64, 2, 2, 3, 128},  {64, 64, 1, 2, 6, 64}};
+// prefill (256 x BN, 16 waves of 64 x 64 where BN allows, 128-byte stage rows:
+// every 1 KiB copy is 8 whole cache lines; raster groups of 4 N blocks), mid
+// (one 256-row tile per expert: 4 stages of 64-byte rows, groups of 8 N
+// blocks so the expert's rows are shared by more of them), decode (64 x BN,
+// deeper pipeline for weight streaming).  Where a family has no distinct mid
+// tile the prefill one is reused (entries 4 up, 7 down).
+constexpr Variant kUpVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8}, {64, 256, 1, 4, 6, 64, 8},
+                              {256, 128, 2, 2, 3, 128, 8}, {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 6, 64, 8}};
+constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8}, {64, 256, 1, 4, 6, 64, 8},
+                                {256, 128, 2, 2, 3, 128, 8}, {256, 128, 1, 4, 4, 64, 8}, {64, 128, 1, 4, 6, 64, 8},
+                                {256, 64, 2, 2, 3, 128, 8},  {256, 64, 2, 2, 3, 128, 8},  {64, 64, 1, 2, 6, 64, 8}};
 
-#define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R) \
-  case IDX:                                    \
-    gg_kernel<I8, UP, BM, BN, WM, WN, S, R><<<grid, WM * WN * 64, 0, s>>>(a); \
+#define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R, G) \
+  case IDX:                                       \
+    gg_kernel<I8, UP, BM, BN, WM, WN, S, R, G><<<grid, WM * WN * 64, 0, s>>>(a); \
     break;
 
 template <bool I8, bool UP>
@@ -530,24 +534,24 @@ hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
   if constexpr (UP) {
     switch (var) {
-      MOE_GG_CASE(0, 256, 256, 2, 2, 2, 128)
-      MOE_GG_CASE(1, 256, 256, 1, 4, 4, 64)
-      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64)
-      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128)
-      MOE_GG_CASE(5, 64, 128, 1, 2, 6, 64)
+      MOE_GG_CASE(0, 256, 256, 4, 4, 2, 128, 4)
+      MOE_GG_CASE(1, 256, 256, 4, 4, 4, 64, 8)
+      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64, 8)
+      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG_CASE(5, 64, 128, 1, 2, 6, 64, 8)
       default:
         return hipErrorInvalidValue;
     }
   } else {
     switch (var) {
-      MOE_GG_CASE(0, 256, 256, 2, 2, 2, 128)
-      MOE_GG_CASE(1, 256, 256, 1, 4, 4, 64)
-      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64)
-      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128)
-      MOE_GG_CASE(4, 256, 128, 1, 4, 4, 64)
-      MOE_GG_CASE(5, 64, 128, 1, 4, 6, 64)
-      MOE_GG_CASE(6, 256, 64, 2, 2, 3, 128)
-      MOE_GG_CASE(8, 64, 64, 1, 2, 6, 64)
+      MOE_GG_CASE(0, 256, 256, 4, 4, 2, 128, 4)
+      MOE_GG_CASE(1, 256, 256, 4, 4, 4, 64, 8)
+      MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64, 8)
+      MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG_CASE(4, 256, 128, 1, 4, 4, 64, 8)
+      MOE_GG_CASE(5, 64, 128, 1, 4, 6, 64, 8)
+      MOE_GG_CASE(6, 256, 64, 2, 2, 3, 128, 8)
+      MOE_GG_CASE(8, 64, 64, 1, 2, 6, 64, 8)
       default:
         return hipErrorInvalidValue;
     }
@@ -629,10 +633,10 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     p.block_m = cls == 2 ? 64 : 256;
     const char* t = w_dtype == kI8 ? "i8" : "bf16";
     const Variant u = kUpVar[p.up_var], d = kDownVar[p.down_var];
-    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<%s,up,%dx%d,%dx%d,S%d,R%d>", t, u.bm, u.bn, u.wm,
-             u.wn, u.stages, u.rowb);
-    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<%s,down,%dx%d,%dx%d,S%d,R%d>", t, d.bm, d.bn,
-             d.wm, d.wn, d.stages, d.rowb);
+    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<%s,up,%dx%d,%dx%d,S%d,R%d,G%d>", t, u.bm, u.bn,
+             u.wm, u.wn, u.stages, u.rowb, u.gn);
+    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<%s,down,%dx%d,%dx%d,S%d,R%d,G%d>", t, d.bm,
+             d.bn, d.wm, d.wn, d.stages, d.rowb, d.gn);
     if (w_dtype == kBF16)
       p.ws_bytes = align256((size_t)n * I * 2);
     else
