@@ -144,22 +144,23 @@ void gg_kernel(const GemmArgs a) {
   constexpr int SUB = ROWB / 32;                     // MFMA k-substeps per stage
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int NBLK = (BM + BN) / RPB;              // 1 KiB copy blocks per stage
-  constexpr int L = NBLK / NW;                       // copies per wave per stage
   constexpr int EB = I8 ? 1 : 2;
-  static_assert(L * NW == NBLK, "copies must split evenly over the waves");
+  constexpr int L = NBLK / NW;                       // copies per wave per stage
+  static_assert(L * NW == NBLK && S >= 2, "copies must split evenly over the waves");
   static_assert(FM >= 1 && NF >= 1, "wave tile too small");
   static_assert(!UP || (NF % 2 == 0), "up needs paired G/U fragments");
-  // per-row epilogue scale, loaded once before the K loop so the epilogue
-  // does no dependent global loads: up W8A8 the token's activation scale,
-  // down the route weight (times the row's h scale for W8A8).  It lives in
-  // the same LDS allocation as the stages: with a second LDS object the
-  // compiler can no longer tell the stage reads from the in-flight copies
-  // and drains every copy (vmcnt(0)) before each stage.
+  static_assert(S * STAGE <= 160 * 1024, "LDS stages");
+  // One LDS allocation: with a second LDS object the compiler can no longer
+  // tell the stage reads from the in-flight copies and drains every copy
+  // (vmcnt(0)) before each stage.
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
+  // per-row epilogue scale (up W8A8: the token's activation scale; down: the
+  // route weight, times the row's h scale for W8A8): loaded into a register
+  // before the K loop, moved to the freed stage memory after it, so the
+  // epilogue does no dependent global loads
   constexpr bool ROWSCALE = (UP && I8) || !UP;
-  constexpr int SCALE_BYTES = ROWSCALE ? BM * 4 : 0;
-  static_assert(S >= 2 && S * STAGE + SCALE_BYTES <= 160 * 1024, "LDS stages");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE + SCALE_BYTES];
-  float* row_scale = reinterpret_cast<float*>(smem + S * STAGE);
+  static_assert(!ROWSCALE || NT >= BM, "one thread per row scale");
+  float* row_scale = reinterpret_cast<float*>(smem);
 
   // The grid covers the host's bound on tiles; only the first
   // num_tiles * n_blocks workgroups have work.  Those are renumbered over
@@ -193,6 +194,15 @@ void gg_kernel(const GemmArgs a) {
   // i%CPR, which holds logical chunk (i%CPR) ^ sw(row).
   const uint8_t* abase = UP ? a.act : a.act + (int64_t)r0 * kbytes;
   const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes;
+  // A wave whose copy blocks hold only A rows past the tile's valid rows
+  // issues no copies at all (those rows are never stored); any other wave
+  // issues all L per stage, so its vmcnt waits stay exact.
+  bool copies = false;
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const int q = wv * L + j;
+    copies |= q >= BM / RPB || q * RPB < rows;
+  }
   uint32_t goff[L];
 #pragma unroll
   for (int j = 0; j < L; ++j) {
@@ -212,6 +222,7 @@ void gg_kernel(const GemmArgs a) {
     goff[j] = row * (uint32_t)kbytes + c * 16;
   }
   auto issue = [&](int kt) {
+    if (!copies) return;
     uint8_t* st = smem + (kt % S) * STAGE;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
@@ -221,19 +232,16 @@ void gg_kernel(const GemmArgs a) {
     }
   };
 
+  float rs = 0.f;
   if constexpr (ROWSCALE) {
-    for (int r = tid; r < BM; r += NT) {
-      float v = 0.f;
-      if (r < rows) {
-        const int slot = a.sorted_slot[r0 + r];
-        if constexpr (UP) {
-          v = a.xs[slot / a.k];
-        } else {
-          v = a.topk_w ? a.topk_w[slot] : 1.f;
-          if (I8) v *= a.hs[r0 + r];
-        }
+    if (tid < rows) {
+      const int slot = a.sorted_slot[r0 + tid];
+      if constexpr (UP) {
+        rs = a.xs[slot / a.k];
+      } else {
+        rs = a.topk_w ? a.topk_w[slot] : 1.f;
+        if (I8) rs *= a.hs[r0 + tid];
       }
-      row_scale[r] = v;   // published by the K loop's first barrier
     }
   }
   // number of this wave's 32-row fragments that hold valid rows (uniform)
@@ -270,9 +278,9 @@ void gg_kernel(const GemmArgs a) {
       wait_vm_stages<L, S - 2>(after);
       lds_barrier();
       if (kt + S - 1 < nk) issue(kt + S - 1);
+      const uint8_t* As = smem + (kt % S) * STAGE;
+      const uint8_t* Bs = As + BM * ROWB;
       if constexpr (V > 0) {
-        const uint8_t* As = smem + (kt % S) * STAGE;
-        const uint8_t* Bs = As + BM * ROWB;
         u32x4 af[SUB][V], bfr[SUB][NF];
         // read order A0, B0..B(NF-1), A1..A(V-1): the first MFMA (A0 x B0)
         // waits for two reads only
@@ -312,6 +320,11 @@ void gg_kernel(const GemmArgs a) {
     }
   };
   dispatch_valid<FM>(fmv, kloop);
+  if constexpr (ROWSCALE) {
+    lds_barrier();   // every wave is done with the stages (all copies have landed)
+    if (tid < BM) row_scale[tid] = rs;
+    lds_barrier();
+  }
   bool fv[FM];
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) fv[fm] = fm < fmv;
@@ -518,11 +531,14 @@ struct Variant {
 // blocks so the expert's rows are shared by more of them), decode (64 x BN,
 // deeper pipeline for weight streaming).  Where a family has no distinct mid
 // tile the prefill one is reused (entries 4 up, 7 down).
-constexpr Variant kUpVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8}, {64, 256, 1, 4, 6, 64, 8},
-                              {256, 128, 2, 2, 3, 128, 8}, {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 6, 64, 8}};
-constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8}, {64, 256, 1, 4, 6, 64, 8},
-                                {256, 128, 2, 2, 3, 128, 8}, {256, 128, 1, 4, 4, 64, 8}, {64, 128, 1, 4, 6, 64, 8},
-                                {256, 64, 2, 2, 3, 128, 8},  {256, 64, 2, 2, 3, 128, 8},  {64, 64, 1, 2, 6, 64, 8}};
+constexpr Variant kUpVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8},
+                              {64, 256, 1, 4, 6, 64, 8},    {256, 128, 2, 2, 3, 128, 8},
+                              {256, 128, 2, 2, 3, 128, 8},  {64, 128, 1, 2, 6, 64, 8}};
+constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8},
+                                {64, 256, 1, 4, 6, 64, 8},    {256, 128, 2, 2, 3, 128, 8},
+                                {256, 128, 1, 4, 4, 64, 8},   {64, 128, 1, 4, 6, 64, 8},
+                                {256, 64, 2, 2, 3, 128, 8},   {256, 64, 2, 2, 3, 128, 8},
+                                {64, 64, 1, 2, 6, 64, 8}};
 
 #define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R, G) \
   case IDX:                                       \
