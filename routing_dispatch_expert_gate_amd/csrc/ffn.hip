@@ -526,7 +526,8 @@ struct Variant {
 };
 // Rows: tile family (BN) by the divisibility of I (up) or H (down); columns:
 // prefill (256 x BN, 16 waves of 64 x 64 where BN allows, 128-byte stage rows:
-// every 1 KiB copy is 8 whole cache lines; raster groups of 4 N blocks), mid
+// every 1 KiB copy is 8 whole cache lines; raster groups of 4 N blocks up, 2
+// down, measured best), mid
 // (one 256-row tile per expert: 4 stages of 64-byte rows, groups of 8 N
 // blocks so the expert's rows are shared by more of them), decode (64 x BN,
 // deeper pipeline for weight streaming).  Where a family has no distinct mid
@@ -534,7 +535,7 @@ struct Variant {
 constexpr Variant kUpVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8},
                               {64, 256, 1, 4, 6, 64, 8},    {256, 128, 2, 2, 3, 128, 8},
                               {256, 128, 2, 2, 3, 128, 8},  {64, 128, 1, 2, 6, 64, 8}};
-constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 4}, {256, 256, 4, 4, 4, 64, 8},
+constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4, 64, 8},
                                 {64, 256, 1, 4, 6, 64, 8},    {256, 128, 2, 2, 3, 128, 8},
                                 {256, 128, 1, 4, 4, 64, 8},   {64, 128, 1, 4, 6, 64, 8},
                                 {256, 64, 2, 2, 3, 128, 8},   {256, 64, 2, 2, 3, 128, 8},
@@ -560,7 +561,7 @@ hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
     }
   } else {
     switch (var) {
-      MOE_GG_CASE(0, 256, 256, 4, 4, 2, 128, 4)
+      MOE_GG_CASE(0, 256, 256, 4, 4, 2, 128, 2)
       MOE_GG_CASE(1, 256, 256, 4, 4, 4, 64, 8)
       MOE_GG_CASE(2, 64, 256, 1, 4, 6, 64, 8)
       MOE_GG_CASE(3, 256, 128, 2, 2, 3, 128, 8)
