@@ -5,61 +5,78 @@
 // accumulating on chip; the LightOP page, section 3.2 (MoE Sum), reads and
 // writes with 128-bit vectors and spreads one token over several blocks.
 //
-// One thread owns 8 consecutive output values of one token: it loads the k
-// slot positions (and weights), issues up to k independent 16-byte row loads,
-// accumulates in fp32 registers in slot order, and writes once.  A 4096-wide
-// token is spread over two 256-thread blocks.  Dropped slots (pos < 0) add
-// nothing, so a fully dropped token gets 0.
+// One thread owns VPT consecutive output values of one token (16 when k <= 4,
+// else 8): it loads the k slot positions (and weights), issues all k * VPT/8
+// independent 16-byte row loads, accumulates in fp32 registers in slot order,
+// and writes once.  k is rounded up to a compile-time KT (2, 4 or 8; the
+// extra slots are masked) so the loads and sums unroll exactly.  Dropped
+// slots (pos < 0) add nothing, so a fully dropped token gets 0.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-template <typename YT, typename OT, bool WEIGHTED>
+template <typename YT, typename OT, bool WEIGHTED, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                      const int32_t* __restrict__ pos,
                                                      const float* __restrict__ w, int64_t T, int k,
                                                      int H, OT* __restrict__ out) {
-  const int cpr = H >> 3;
+  constexpr int VPT = KT <= 4 ? 16 : 8;
+  constexpr int NC = VPT / 8;   // 8-value chunks per thread
+  const int cpr = H / VPT;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= T * cpr) return;
   const int64_t t = g / cpr;
   const int c = (int)(g - t * cpr);
-  int p[kMaxK];
-  float wt[kMaxK];
+  int p[KT];
+  float wt[KT];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
+  for (int j = 0; j < KT; ++j) {
     p[j] = j < k ? pos[t * k + j] : -1;
     wt[j] = (WEIGHTED && j < k) ? w[t * k + j] : 1.f;
   }
-  float v[kMaxK][8];
+  float v[KT][NC][8];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    if (p[j] >= 0) {
-      load8(y + (int64_t)p[j] * H + c * 8, v[j]);
-    } else {
+  for (int j = 0; j < KT; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+    for (int q = 0; q < NC; ++q) {
+      if (p[j] >= 0) {
+        load8(y + (int64_t)p[j] * H + c * VPT + q * 8, v[j][q]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[j][q][i] = 0.f;
+      }
     }
+#pragma unroll
+  for (int q = 0; q < NC; ++q) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KT; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = WEIGHTED ? fmaf(wt[j], v[j][q][i], acc[i]) : acc[i] + v[j][q][i];
+    store8(out + t * H + c * VPT + q * 8, acc);
   }
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = WEIGHTED ? fmaf(wt[j], v[j][i], acc[i]) : acc[i] + v[j][i];
-  store8(out + t * H + c * 8, acc);
+}
+
+template <typename YT, typename OT, int KT>
+hipError_t launch_k(const void* y, const int32_t* pos, const float* w, int64_t T, int k, int H,
+                    void* out, hipStream_t s) {
+  constexpr int VPT = KT <= 4 ? 16 : 8;
+  const int64_t work = T * (H / VPT);
+  const dim3 grid((unsigned)((work + 255) / 256));
+  if (w)
+    combine_kernel<YT, OT, true, KT><<<grid, 256, 0, s>>>((const YT*)y, pos, w, T, k, H, (OT*)out);
+  else
+    combine_kernel<YT, OT, false, KT><<<grid, 256, 0, s>>>((const YT*)y, pos, w, T, k, H, (OT*)out);
+  return hipGetLastError();
 }
 
 template <typename YT, typename OT>
 hipError_t launch_t(const void* y, const int32_t* pos, const float* w, int64_t T, int k, int H,
                     void* out, hipStream_t s) {
-  const int64_t work = T * (H / 8);
-  const dim3 grid((unsigned)((work + 255) / 256));
-  if (w)
-    combine_kernel<YT, OT, true><<<grid, 256, 0, s>>>((const YT*)y, pos, w, T, k, H, (OT*)out);
-  else
-    combine_kernel<YT, OT, false><<<grid, 256, 0, s>>>((const YT*)y, pos, w, T, k, H, (OT*)out);
-  return hipGetLastError();
+  if (k <= 2) return launch_k<YT, OT, 2>(y, pos, w, T, k, H, out, s);
+  if (k <= 4) return launch_k<YT, OT, 4>(y, pos, w, T, k, H, out, s);
+  return launch_k<YT, OT, 8>(y, pos, w, T, k, H, out, s);
 }
 
 }  // namespace

@@ -160,22 +160,49 @@ __device__ void wave_quant_row(const XT* __restrict__ xrow, int H, int8_t* __res
 }
 
 // ------------------------------------------------------------ kind 0 -----
-// Multi-value butterfly: lane l ends with the 64-lane sum of value
-// index l / (64 / EP) in a[0].
+// DPP move of a float from another lane (0 where the source lane is outside
+// the row): quad_perm xor 1 = 0xB1, xor 2 = 0x4E; row_shr:n = 0x110 + n.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of each of EP values over the 64 lanes.  Two butterfly steps inside
+// each quad (DPP xor 1, xor 2) halve the vector twice, so lane l keeps EP/4
+// values: indices (l & 1) * EP/2 + ((l >> 1) & 1) * EP/4 + i.  Lanes 4 apart
+// in a 16-lane row then hold the same indices: two DPP shift-adds (row_shr 4,
+// 8) leave each row's sums in its lanes 12..15, and two shuffles (xor 16, 32)
+// add the rows.  Only those two levels go through the LDS crossbar, and the
+// EP/4 chains are independent.  Lanes 12..15 end with the totals.
 template <int EP>
-__device__ __forceinline__ void multi_reduce(float (&a)[EP], int lane) {
-  int o = 32;
+__device__ __forceinline__ void wave_reduce_quads(float (&a)[EP], int lane) {
+  static_assert(EP % 4 == 0, "EP");
+  {
+    const bool up = (lane & 1) != 0;
 #pragma unroll
-  for (int n = EP; n > 1; n >>= 1, o >>= 1) {
-    const bool up = (lane & o) != 0;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float send = up ? a[i] : a[i + n / 2];
-      const float keep = up ? a[i + n / 2] : a[i];
-      a[i] = keep + __shfl_xor(send, o, kWave);
+    for (int i = 0; i < EP / 2; ++i) {
+      const float send = up ? a[i] : a[i + EP / 2];
+      const float keep = up ? a[i + EP / 2] : a[i];
+      a[i] = keep + dpp_f<0xB1>(send);
     }
   }
-  for (; o > 0; o >>= 1) a[0] += __shfl_xor(a[0], o, kWave);
+  {
+    const bool up = (lane & 2) != 0;
+#pragma unroll
+    for (int i = 0; i < EP / 4; ++i) {
+      const float send = up ? a[i] : a[i + EP / 4];
+      const float keep = up ? a[i + EP / 4] : a[i];
+      a[i] = keep + dpp_f<0x4E>(send);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EP / 4; ++i) a[i] += dpp_f<0x114>(a[i]);
+#pragma unroll
+  for (int i = 0; i < EP / 4; ++i) a[i] += dpp_f<0x118>(a[i]);
+#pragma unroll
+  for (int i = 0; i < EP / 4; ++i) a[i] += __shfl_xor(a[i], 16, kWave);
+#pragma unroll
+  for (int i = 0; i < EP / 4; ++i) a[i] += __shfl_xor(a[i], 32, kWave);
 }
 
 constexpr int kFmaTB = 16;   // tokens per workgroup
@@ -217,17 +244,15 @@ struct Raw8<float> {
 // WIDE: more than 8 waves (H > 4096, E <= 8 only), 1024 threads and hence at
 // most 128 VGPRs: fewer rows in flight.
 // A workgroup's token rows are loaded in batches of PF rows, each batch before
-// its first FMA; the per-token partial logits of RB
-// tokens are reduced together, RB*EP values in one butterfly, so the
-// shuffles of a level are independent of one another.
+// its first FMA; each token's E partial logits are reduced over the wave by
+// wave_reduce_quads.
 template <int EP, bool WIDE, typename XT, typename WT, bool QUANT>
 __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
   constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);   // rows per load batch
-  constexpr int RB = 1;   // rows per butterfly: with more, LLVM turns the butterfly selects into dynamic indexing
-  static_assert(PF % RB == 0 && kFmaTB % PF == 0, "batches");
+  static_assert(kFmaTB % PF == 0, "batches");
   __shared__ float part[16][kFmaTB][EP];
   __shared__ float amax_s[16][kFmaTB];
   __shared__ __attribute__((aligned(16))) float lg[kFmaTB][16];
@@ -259,34 +284,34 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
         r[u].zero();
     }
 #pragma unroll
-    for (int ub = 0; ub < PF; ub += RB) {
+    for (int ub = 0; ub < PF; ++ub) {
       if (tb + ub >= ntok) break;
-      float acc[RB * EP];
-#pragma unroll
-      for (int u = 0; u < RB; ++u) {
+      float acc[EP];
+      {
         float v[8];
-        r[ub + u].get(v);
+        r[ub].get(v);
 #pragma unroll
         for (int e = 0; e < EP; ++e) {
           float a = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) a = fmaf(v[i], wr[e][i], a);
-          acc[u * EP + e] = a;
+          acc[e] = a;
         }
         if (QUANT) {
           float am = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
           am = wave_max(am);
-          if (lane == 0 && tb + ub + u < ntok) amax_s[wv][tb + ub + u] = am;
+          if (lane == 0) amax_s[wv][tb + ub] = am;
         }
       }
-      // lane l ends with value l / (64 / (RB*EP)): token l / (64/RB), expert (l % (64/RB)) / (64/(RB*EP))
-      multi_reduce<RB * EP>(acc, lane);
-      constexpr int LPV = 64 / (RB * EP);   // lanes per value
-      const int vi = lane / LPV;
-      const int u = vi / EP, e = vi - u * EP;
-      if ((lane & (LPV - 1)) == 0 && tb + ub + u < ntok) part[wv][tb + ub + u][e] = acc[0];
+      wave_reduce_quads<EP>(acc, lane);
+      if (lane >= 12 && lane < 16 && tb + ub < ntok) {
+        const int q = lane & 3;
+        const int base = (q & 1) * (EP / 2) + ((q >> 1) & 1) * (EP / 4);
+#pragma unroll
+        for (int i = 0; i < EP / 4; ++i) part[wv][tb + ub][base + i] = acc[i];
+      }
     }
   }
   __syncthreads();
