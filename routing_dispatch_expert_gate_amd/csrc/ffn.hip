@@ -419,16 +419,13 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ 
   const int lane = threadIdx.x & 63;
   const float am = __uint_as_float(rowmax[r]);
   const float s = am == 0.f ? 1.f : am / 127.f;
+  const float rs = 1.f / s;
   for (int c = lane * 8; c < I; c += 512) {
     float v[8];
     load8(h + r * I + c, v);
     uint32_t b[2] = {0u, 0u};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float z = rintf(v[q] / s);
-      z = fminf(fmaxf(z, -128.f), 127.f);
-      b[q >> 2] |= (uint32_t)((int)z & 0xFF) << (8 * (q & 3));
-    }
+    for (int q = 0; q < 8; ++q) b[q >> 2] |= (uint32_t)(quant_code(v[q], s, rs) & 0xFF) << (8 * (q & 3));
     *reinterpret_cast<uint2*>(hq + r * I + c) = make_uint2(b[0], b[1]);
   }
   if (lane == 0) hs[r] = s;

@@ -107,11 +107,9 @@ std::string route_name(const moe::RoutePlan& p) {
   char b[160];
   if (p.kind == 0)
     snprintf(b, sizeof b, "route_fma_kernel(tokens/wg=%d,waves=%d)", p.bt, p.nw);
-  else if (p.kind == 1)
-    snprintf(b, sizeof b, "route_gemm_kernel<fused>(tokens/wg=%d,experts/wg=64)", p.bt);
   else
-    snprintf(b, sizeof b, "route_gemm_kernel<logits>(tokens/wg=%d,experts/wg=64,ksplit=%d)+route_topk_kernel",
-             p.bt, p.ks);
+    snprintf(b, sizeof b, "route_gemm_kernel(tokens/wg=%d,experts/wg=64,ksplit=%d)+route_topk_kernel", p.bt,
+             p.ks);
   return b;
 }
 

@@ -62,6 +62,20 @@ __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8]) {
                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
+// ---------------------------------------------------- per-token int8 codes
+// Code of x at scale s: round-half-even(x / s) clamped to [-128, 127], equal
+// to what the correctly rounded quotient gives.  rs = 1/s, correctly rounded,
+// once per row.  With |x| <= 127 s (s is a row's absmax / 127), x * rs is
+// within 2^-15 of the correctly rounded quotient, so the two round to the
+// same integer unless x * rs lies within 2^-14 of a half-integer (or is not
+// finite): only those rare elements take the division.
+__device__ __forceinline__ int quant_code(float x, float s, float rs) {
+  const float y = x * rs;
+  float q = rintf(y);
+  if (!(fabsf(fabsf(y - q) - 0.5f) >= 0x1p-14f) || !(fabsf(y) <= 128.f)) q = rintf(x / s);
+  return (int)fminf(fmaxf(q, -128.f), 127.f);
+}
+
 // ------------------------------------------------------------- wave utils
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -120,7 +134,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // ------------------------------------------------------------- launchers
 // route.hip
 struct RoutePlan {
-  int kind;      // 0 = fused FMA (E <= 16), 1 = fused MFMA (E <= 64), 2 = MFMA logits + top-k
+  int kind;      // 0 = fused FMA (E <= 16), 2 = MFMA logits + top-k (E > 16)
   int bt;        // tokens per workgroup
   int ks;        // K splits (kind 2)
   int nw;        // waves per workgroup (kind 0)

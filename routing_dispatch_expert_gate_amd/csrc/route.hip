@@ -9,23 +9,19 @@
 // exponentials only where needed, unrolled argmax with erase of the winner).
 // The quantisation is the per-token int8 rule of the LightOP page, section 4.1.
 //
-// Three variants, picked on the host by shape (never silently):
+// Two variants, picked on the host by shape (never silently):
 //   kind 0  E <= 16: fp32 FMA.  Each wave keeps its slice of Wg (8 values of
 //           H per lane, all experts) in registers and re-uses it for 16
-//           tokens, whose x chunks are all loaded before the first FMA;
-//           per-token partial logits are reduced across the 64 lanes with a
-//           multi-value butterfly (E values in log2(64) steps, halving the
-//           vector each step), then across waves through LDS.  Logits never
-//           leave the chip.
-//   kind 1  16 < E <= 64, bf16: MFMA 32x32x16 bf16 over 64-token x 64-expert
-//           tiles, K streamed through a deep direct-to-LDS pipeline, logits
-//           kept in LDS, top-k (and the per-token quantisation) in the same
-//           kernel.
-//   kind 2  otherwise (E up to 256, or few tokens), bf16: the same tile
-//           kernel, experts split over workgroups and K optionally split,
-//           writes partial logits to the workspace; a second kernel sums the
-//           K splits in a fixed order and runs the wave top-k.
-//           Deterministic: no floating-point atomics.
+//           tokens, whose x chunks are loaded in batches before their FMAs;
+//           per-token partial logits are reduced across the 64 lanes with DPP
+//           inside quads and rows and two shuffles across rows, then across
+//           waves through LDS.  Logits never leave the chip.
+//   kind 2  E > 16, bf16: MFMA 32x32x16 bf16 over 64-token x 64-expert tiles,
+//           K streamed through a deep direct-to-LDS pipeline (split while the
+//           grid is small), partial logits to the workspace; a second kernel,
+//           one wave per token, sums the splits in a fixed order, runs the
+//           top-k and writes the per-token int8 codes.  Deterministic: no
+//           floating-point atomics.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -122,41 +118,16 @@ __device__ void wave_topk_rank_store(const float* L, int E, int k, int64_t t, in
 }
 
 // ------------------------------------------------------- per-token quant --
-// codes of 8 values with scale s: round-half-even(x / s) clamped to [-128, 127]
-__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s) {
+// codes of 8 values with scale s (rs = 1/s)
+__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float rs) {
   uint32_t b[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float q = rintf(v[i] / s);
-    q = fminf(fmaxf(q, -128.f), 127.f);
-    b[i >> 2] |= (uint32_t)((int)q & 0xFF) << (8 * (i & 3));
-  }
+  for (int i = 0; i < 8; ++i) b[i >> 2] |= (uint32_t)(quant_code(v[i], s, rs) & 0xFF) << (8 * (i & 3));
   return make_uint2(b[0], b[1]);
 }
 
 __device__ __forceinline__ float row_scale(float absmax) {
   return absmax == 0.f ? 1.f : absmax / 127.f;
-}
-
-// One wave quantises one row of H values.
-template <typename XT>
-__device__ void wave_quant_row(const XT* __restrict__ xrow, int H, int8_t* __restrict__ qrow,
-                               float* __restrict__ s_out) {
-  const int lane = threadIdx.x & 63;
-  float am = 0.f;
-  for (int h = lane * 8; h < H; h += 512) {
-    float v[8];
-    load8(xrow + h, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-  }
-  const float s = row_scale(wave_max(am));
-  for (int h = lane * 8; h < H; h += 512) {
-    float v[8];
-    load8(xrow + h, v);
-    *reinterpret_cast<uint2*>(qrow + h) = quant8(v, s);
-  }
-  if (lane == 0) *s_out = s;
 }
 
 // ------------------------------------------------------------ kind 0 -----
@@ -350,7 +321,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
         if (hv) {
           float v[8];
           r[u].get(v);
-          *reinterpret_cast<uint2*>(xq + (t0 + tt) * H + h0) = quant8(v, s);
+          *reinterpret_cast<uint2*>(xq + (t0 + tt) * H + h0) = quant8(v, s, 1.f / s);
         }
         if (threadIdx.x == 0) xs[t0 + tt] = s;
       }
@@ -358,17 +329,16 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
   }
 }
 
-// ------------------------------------------------------- kinds 1 and 2 ----
+// ------------------------------------------------------------ kind 2 -----
 // Gate logits on MFMA: one workgroup computes a 64-token x 64-expert tile of
 // x Wg^T over a K range (all of H unless split).  K is streamed 64 bf16 (128
 // bytes) per stage from global memory straight into LDS, kRS stages deep;
 // waves form a 2 x 2 grid, each owning one 32 x 32 MFMA 32x32x16 fragment.
 // Token rows past T and expert rows past E copy a valid row; their results
-// are never used.  Fused (E <= 64, no K split): the logits tile goes to LDS
-// and each wave runs the top-k of 16 tokens; with quantisation the row
-// absmax is folded from the A stages as they pass through LDS, and the row is
-// re-read once to write its codes.  Otherwise the tile is written to the
-// workspace for route_topk_kernel.
+// are never used.  The tile is written to the workspace; with quantisation
+// the first expert block also folds each token row's absmax over its K range
+// from the A stages as they pass through LDS.  route_topk_kernel then sums
+// the K splits, runs the top-k and writes the codes, one wave per token.
 constexpr int kRT = 64;                        // tokens per tile
 constexpr int kRE = 64;                        // experts per tile
 constexpr int kRRow = 128;                     // bytes of K per stage row
@@ -376,12 +346,17 @@ constexpr int kRS = 8;                         // stages
 constexpr int kRStage = (kRT + kRE) * kRRow;   // 16 KiB
 constexpr int kRL = (kRT + kRE) * kRRow / 1024 / 4;   // 1 KiB copies per wave per stage
 
-template <bool FUSED, bool QUANT>
-__global__ __launch_bounds__(256) void route_gemm_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias,
-    int64_t T, int H, int E, int k, int kchunk, float* __restrict__ part, int32_t* __restrict__ ids,
-    float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
-  static_assert(!QUANT || FUSED, "quantisation is fused only with the top-k");
+// workspace: partial logits [ks][T][E] fp32, then per-split row absmax [ks][T]
+size_t route_part_bytes(int64_t T, int E, int ks) {
+  return ((size_t)ks * (size_t)T * (size_t)E * sizeof(float) + 255) & ~(size_t)255;
+}
+
+template <bool QUANT>
+__global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ wg, int64_t T,
+                                                        int H, int E, int kchunk,
+                                                        float* __restrict__ part,
+                                                        float* __restrict__ amax_part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kRS * kRStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -466,97 +441,35 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(
                                                     __builtin_bit_cast(bf16x8, bf[s]), acc, 0, 0, 0);
   }
 
-  if constexpr (!FUSED) {
-    const int e = e0 + wn * 32 + (lane & 31);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t t = t0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[v];
-    }
-    return;
-  }
-
-  // fused: the logits tile and the row maxima go to LDS (stage memory reused)
-  constexpr int LSTR = kRE + 4;                       // 16-byte aligned rows
-  float* Ls = reinterpret_cast<float*>(smem);        // [kRT][LSTR]
-  float* rmax = Ls + kRT * LSTR;                     // [kRT]
-  lds_barrier();
+  const int e = e0 + wn * 32 + (lane & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const int r = wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    const int e = wn * 32 + (lane & 31);
-    Ls[r * LSTR + e] = acc[v] + (bias && e < E ? bias[e] : 0.f);
+    const int64_t t = t0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[v];
   }
   if constexpr (QUANT) {
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
-    if ((tid & 3) == 0) rmax[qrow] = __uint_as_float(amax << 16);
-  }
-  __syncthreads();
-  // quantisation: codes of 16 values per thread and step, QB steps' loads in
-  // flight; the first batch is issued before the top-k so it lands meanwhile
-  constexpr int QB = 8;
-  const int cpr = H / 16;
-  const int64_t rows = T - t0 < kRT ? T - t0 : kRT;
-  const int total = QUANT ? (int)rows * cpr : 0;
-  u32x4 raw[QB][2];
-  auto qload = [&](int q0) {
-#pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const int q = q0 + u * 256;
-      if (q < total) {
-        const int rr = q / cpr, c = q - rr * cpr;
-        const u32x4* p = reinterpret_cast<const u32x4*>(x + (t0 + rr) * H + c * 16);
-        raw[u][0] = p[0];
-        raw[u][1] = p[1];
-      }
-    }
-  };
-  if constexpr (QUANT) qload(tid);
-  for (int tt = wv; tt < kRT; tt += 4) {
-    if (t0 + tt >= T) break;
-    wave_topk_rank_store(Ls + tt * LSTR, E, k, t0 + tt, ids, w, prob);
-  }
-  if constexpr (QUANT) {
-    for (int q0 = tid; q0 < total; q0 += QB * 256) {
-      if (q0 != tid) qload(q0);
-#pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        const int q = q0 + u * 256;
-        if (q < total) {
-          const int rr = q / cpr, c = q - rr * cpr;
-          const float sc = row_scale(rmax[rr]);
-          u32x4 out;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v[2 * i] = __uint_as_float(raw[u][hh][i] << 16);
-              v[2 * i + 1] = __uint_as_float(raw[u][hh][i] & 0xFFFF0000u);
-            }
-            const uint2 b = quant8(v, sc);
-            out[2 * hh] = b.x;
-            out[2 * hh + 1] = b.y;
-          }
-          *reinterpret_cast<u32x4*>(xq + (t0 + rr) * H + c * 16) = out;
-        }
-      }
-    }
-    if (tid < rows) xs[t0 + tid] = row_scale(rmax[tid]);
+    if (blockIdx.y == 0 && (tid & 3) == 0 && t0 + qrow < T)
+      amax_part[(int64_t)blockIdx.z * T + t0 + qrow] = __uint_as_float(amax << 16);
   }
 }
 
+// One wave per token: sums the K splits of its logits in a fixed order (8
+// splits' loads in flight), adds the bias, selects the top-k (by rank from an
+// LDS row when E <= 64, else by argmax rounds) and, with quantisation, writes
+// the token's codes with the absmax the logits kernel folded.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ part, int ks, const float* __restrict__ bias, int64_t T, int E, int k,
-    int H, const uint16_t* __restrict__ x, int32_t* __restrict__ ids, float* __restrict__ w,
-    float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
+    const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
+    const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
+    float* __restrict__ xs) {
+  __shared__ __attribute__((aligned(16))) float lrow[4][64];
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;
-  // K splits summed in a fixed order; 8 splits of each of the lane's 4
-  // experts are loaded at once
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   for (int z0 = 0; z0 < ks; z0 += 8) {
     float q[4][8];
@@ -576,8 +489,32 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     const int e = lane + 64 * j;
     v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : -INFINITY;
   }
-  wave_topk_store(v, E, k, t, ids, w, prob);
-  if (QUANT) wave_quant_row(x + t * H, H, xq + t * H, xs + t);
+  if (E <= 64) {
+    lrow[wv][lane] = v[0];
+    __builtin_amdgcn_wave_barrier();
+    wave_topk_rank_store(lrow[wv], E, k, t, ids, w, prob);
+  } else {
+    wave_topk_store(v, E, k, t, ids, w, prob);
+  }
+  if constexpr (QUANT) {
+    float am = 0.f;
+    for (int z = 0; z < ks; ++z) am = fmaxf(am, amax_part[(size_t)z * T + t]);
+    const float s = row_scale(am);
+    const float rs = 1.f / s;
+    const uint16_t* xrow = x + t * H;
+    int8_t* qrow = xq + t * H;
+    // 4 chunks of 8 values per lane in flight
+    for (int h0 = lane * 8; h0 < H; h0 += 4 * 512) {
+      float c[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (h0 + u * 512 < H) load8(xrow + h0 + u * 512, c[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (h0 + u * 512 < H) *reinterpret_cast<uint2*>(qrow + h0 + u * 512) = quant8(c[u], s, rs);
+    }
+    if (lane == 0) xs[t] = s;
+  }
 }
 
 template <int EP, bool WIDE, typename XT, typename WT>
@@ -611,30 +548,24 @@ hipError_t launch_fma_dt(const RoutePlan& p, const void* x, int xd, const void* 
 hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                        int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                        int8_t* xq, float* xs, void* ws, hipStream_t s) {
-  const unsigned bx = (unsigned)((T + kRT - 1) / kRT);
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)wg;
-  if (p.kind == 1) {
-    const dim3 grid(bx, 1, 1);
-    if (xq)
-      route_gemm_kernel<true, true><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H, nullptr, ids, w,
-                                                         prob, xq, xs);
-    else
-      route_gemm_kernel<true, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H, nullptr, ids, w,
-                                                          prob, xq, xs);
-    return hipGetLastError();
-  }
   float* part = (float*)ws;
-  const dim3 grid(bx, (unsigned)((E + kRE - 1) / kRE), (unsigned)p.ks);
-  route_gemm_kernel<false, false><<<grid, 256, 0, s>>>(xb, wb, bias, T, H, E, k, 2 * H / p.ks, part, ids,
-                                                       w, prob, xq, xs);
+  float* amax_part = (float*)((uint8_t*)ws + route_part_bytes(T, E, p.ks));
+  const dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)((E + kRE - 1) / kRE), (unsigned)p.ks);
+  if (xq)
+    route_gemm_kernel<true><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
+  else
+    route_gemm_kernel<false><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 g2((unsigned)((T + 3) / 4));
   if (xq)
-    route_topk_kernel<true><<<g2, 256, 0, s>>>(part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq, xs);
+    route_topk_kernel<true><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq,
+                                               xs);
   else
-    route_topk_kernel<false><<<g2, 256, 0, s>>>(part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq, xs);
+    route_topk_kernel<false><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq,
+                                                xs);
   return hipGetLastError();
 }
 
@@ -654,18 +585,13 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
   }
   if (x_dtype != kBF16 || wg_dtype != kBF16 || E % 16 != 0 || E > kMaxE) return p;
   p.bt = kRT;
-  const int64_t tblocks = (T + kRT - 1) / kRT;
-  if (E <= kRE && tblocks >= 128) {
-    p.kind = 1;
-    return p;
-  }
   p.kind = 2;
-  const int64_t blocks = tblocks * ((E + kRE - 1) / kRE);
+  const int64_t blocks = ((T + kRT - 1) / kRT) * ((E + kRE - 1) / kRE);
   // split K while the grid is small: each split keeps >= 2 stages of 64 values
   int ks = 1;
   while (blocks * ks < 256 && H % (128 * ks) == 0 && H >= 256 * ks) ks *= 2;
   p.ks = ks;
-  p.ws_bytes = (size_t)ks * (size_t)T * (size_t)E * sizeof(float);
+  p.ws_bytes = route_part_bytes(T, E, ks) + (size_t)ks * (size_t)T * sizeof(float);
   return p;
 }
 

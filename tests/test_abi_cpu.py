@@ -54,7 +54,8 @@ def test_capacity_and_sizes(moe):
     big = L.moe_layer_workspace_size(4096, 4096, 14336, 8, 2, BF16, BF16)
     assert 0 < small < big
     assert big >= 4096 * 2 * 4096 * 2        # the expert-sorted output rows at least
-    assert L.moe_route_workspace_size(4096, 4096, 256, 8) == 4096 * 256 * 4
+    # partial logits [ks][T][E] fp32 (256-byte aligned), then per-split row absmax [ks][T]
+    assert L.moe_route_workspace_size(4096, 4096, 256, 8) == 4096 * 256 * 4 + 4096 * 4
     assert L.moe_route_workspace_size(4096, 4096, 8, 2) == 0
 
 

@@ -131,20 +131,20 @@ def test_route_zero_rows_and_quant_edge_values():
 
 
 # one case per router variant (the dispatch name is checked, so each case
-# really takes its path): FMA for E <= 16 at ordinary and wide H, the fused
-# MFMA tile kernel (E <= 64, many tokens, ragged last tile, bias), and the MFMA
-# logits + top-k pair with and without a K split
+# really takes its path): FMA for E <= 16 at ordinary and wide H, and the MFMA
+# logits + top-k pair for E <= 64 (rank top-k; many tokens, ragged last tile,
+# bias) and E > 64 (argmax rounds), with and without a K split
 ROUTE_PATHS = [
     (moe_synth.Spec("fma_wide_bf16", 37, 8192, 8, 2, 64, wg_dtype="f32"), True, "route_fma_kernel"),
     (moe_synth.Spec("fma_wide_f32", 21, 6144, 4, 2, 64, x_dtype="f32", wg_dtype="f32"), True,
      "route_fma_kernel"),
     (moe_synth.Spec("fma_e16_f32x", 50, 4096, 16, 4, 64, x_dtype="f32"), True, "route_fma_kernel"),
-    (moe_synth.Spec("fused_e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
-     "route_gemm_kernel<fused>"),
-    (moe_synth.Spec("fused_e32", 128 * 64 + 1, 128, 32, 3, 64), False, "route_gemm_kernel<fused>"),
-    (moe_synth.Spec("logits_e64_splitk", 16, 4096, 64, 6, 64), True, "route_gemm_kernel<logits>"),
-    (moe_synth.Spec("logits_e128", 300, 1024, 128, 4, 64), False, "route_gemm_kernel<logits>"),
-    (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel<logits>"),
+    (moe_synth.Spec("e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
+     "route_gemm_kernel("),
+    (moe_synth.Spec("e32_many_tokens", 128 * 64 + 1, 128, 32, 3, 64), False, "ksplit=1)"),
+    (moe_synth.Spec("logits_e64_splitk", 16, 4096, 64, 6, 64), True, "route_gemm_kernel("),
+    (moe_synth.Spec("logits_e128", 300, 1024, 128, 4, 64), False, "route_gemm_kernel("),
+    (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel("),
 ]
 
 
