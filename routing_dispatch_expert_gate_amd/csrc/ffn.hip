@@ -106,9 +106,44 @@ struct GemmArgs {
   const float* topk_w;         // down: route weight per slot (NULL: 1)
   void* out;                   // up: h [rows, I] (bf16; fp32 for W8A8); down: y [rows, H] bf16
   uint32_t* rowmax;            // up, W8A8: max |h| of each row (bit pattern of a non-negative float)
+  void* partial;               // down, last-round split: raw partial tiles [conc][BM * BN]
   int H, I, k;
   int n_blocks, max_tiles;
+  int conc;                    // down: workgroups resident at once (0: no last-round split)
 };
+
+// Last-round split (down GEMM).  With conc workgroups resident at once, the
+// nwork units run in ceil(nwork / conc) rounds.  When the last round is at
+// most half full, each of its units is split into ks K-parts (ks <= conc /
+// units, <= 8, >= 2 stages each) so that round fills the machine.  Units
+// [0, nmain) run whole; the parts, dispatched after them, write raw partial
+// tiles that tail_reduce_kernel sums in part order before the epilogue.
+struct TailPlan {
+  int nmain, ks;
+};
+__device__ __forceinline__ TailPlan tail_plan(int nwork, int conc, int nk) {
+  TailPlan p{nwork, 1};
+  if (conc <= 0 || nwork <= 0) return p;
+  const int tail = nwork - ((nwork - 1) / conc) * conc;
+  if (2 * tail > conc) return p;
+  const int ks = min(min(conc / tail, 8), nk / 2);
+  if (ks >= 2) {
+    p.nmain = nwork - tail;
+    p.ks = ks;
+  }
+  return p;
+}
+
+// unit L0 -> (row tile, N block): groups of GN N blocks, row tiles fastest
+template <int GN>
+__device__ __forceinline__ int2 raster(int L0, int nt, int n_blocks) {
+  const int per_group = nt * GN;
+  const int g = L0 / per_group;
+  const int rem = L0 - g * per_group;
+  const int gs = min(GN, n_blocks - g * GN);
+  const int tile = rem / gs;
+  return make_int2(tile, g * GN + (rem - tile * gs));
+}
 
 // One BM x BN output tile of one row tile (one expert).  Waves form a WM x WN
 // grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments; with
@@ -162,21 +197,35 @@ void gg_kernel(const GemmArgs a) {
   static_assert(!ROWSCALE || NT >= BM, "one thread per row scale");
   float* row_scale = reinterpret_cast<float*>(smem);
 
-  // The grid covers the host's bound on tiles; only the first
-  // num_tiles * n_blocks workgroups have work.  Those are renumbered over
-  // exactly that count, so the real work spreads evenly over the XCDs
-  // (renumbering over the whole grid would pile it onto the first few)
-  // and the idle workgroups, dispatched last, exit at once.
+  // The grid covers the host's bound on tiles (plus conc split parts); only
+  // the first num_tiles * n_blocks units have work.  The whole units are
+  // renumbered over exactly their count, so the real work spreads evenly over
+  // the XCDs (renumbering over the whole grid would pile it onto the first
+  // few); split parts follow; idle workgroups, dispatched last, exit at once.
   const int nt = __builtin_amdgcn_readfirstlane(*a.num_tiles);
   const int nwork = nt * a.n_blocks;
-  if ((int)blockIdx.x >= nwork) return;
-  const int L0 = xcd_remap(blockIdx.x, nwork);
-  const int per_group = nt * GN;
-  const int g = L0 / per_group;
-  const int rem = L0 - g * per_group;
-  const int gs = min(GN, a.n_blocks - g * GN);
-  const int tile = rem / gs;
-  const int nb = g * GN + (rem - tile * gs);
+  const int64_t kbytes = (int64_t)(UP ? a.H : a.I) * EB;
+  const int nk_all = (int)(kbytes / ROWB);
+  TailPlan tp{nwork, 1};
+  if constexpr (!UP) tp = tail_plan(nwork, a.conc, nk_all);
+  int L0, part = -1, kb = 0, nk = nk_all;
+  if ((int)blockIdx.x < tp.nmain) {
+    L0 = xcd_remap(blockIdx.x, tp.nmain);
+  } else {
+    const int idx = (int)blockIdx.x - tp.nmain;
+    if (idx >= (nwork - tp.nmain) * tp.ks) return;
+    const int u = idx / tp.ks, z = idx - u * tp.ks;
+    L0 = tp.nmain + u;
+    kb = (int)((int64_t)nk_all * z / tp.ks);
+    nk = (int)((int64_t)nk_all * (z + 1) / tp.ks) - kb;
+    part = idx;
+  }
+  L0 = __builtin_amdgcn_readfirstlane(L0);
+  part = __builtin_amdgcn_readfirstlane(part);
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  nk = __builtin_amdgcn_readfirstlane(nk);
+  const int2 tn = raster<GN>(L0, nt, a.n_blocks);
+  const int tile = tn.x, nb = tn.y;
   // the tile descriptor is uniform: keep it in scalar registers so every
   // branch on it below is a scalar branch
   const int4 td = reinterpret_cast<const int4*>(a.tiles)[tile];
@@ -186,14 +235,12 @@ void gg_kernel(const GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv / WN, wn = wv - (wv / WN) * WN;
-  const int64_t kbytes = (int64_t)(UP ? a.H : a.I) * EB;
-  const int nk = (int)(kbytes / ROWB);
 
   // This wave's copies: block q = wv*L + j; blocks [0, BM/RPB) are A rows,
   // the rest B rows.  Lane i copies row RPB*blk + i/CPR into LDS chunk
   // i%CPR, which holds logical chunk (i%CPR) ^ sw(row).
-  const uint8_t* abase = UP ? a.act : a.act + (int64_t)r0 * kbytes;
-  const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes;
+  const uint8_t* abase = (UP ? a.act : a.act + (int64_t)r0 * kbytes) + (int64_t)kb * ROWB;
+  const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes + (int64_t)kb * ROWB;
   // A wave whose copy blocks hold only A rows past the tile's valid rows
   // issues no copies at all (those rows are never stored); any other wave
   // issues all L per stage, so its vmcnt waits stay exact.
@@ -320,6 +367,33 @@ void gg_kernel(const GemmArgs a) {
     }
   };
   dispatch_valid<FM>(fmv, kloop);
+  if constexpr (!UP) {
+    if (part >= 0) {
+      // a split part: the raw accumulators of the tile's valid rows
+      int32_t* pp = reinterpret_cast<int32_t*>(a.partial) + (size_t)part * BM * BN;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if (fm >= fmv) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
+          if (row >= rows) continue;
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            // the element by value: __builtin_bit_cast of a vector-element
+            // lvalue reads element 0 with this compiler
+            int32_t bits;
+            if constexpr (I8)
+              bits = acc[fm][f][v];
+            else
+              bits = __float_as_int(acc[fm][f][v]);
+            pp[row * BN + wn * WCOLS + f * 32 + (lane & 31)] = bits;
+          }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (ROWSCALE) {
     lds_barrier();   // every wave is done with the stages (all copies have landed)
     if (tid < BM) row_scale[tid] = rs;
@@ -400,6 +474,58 @@ void gg_kernel(const GemmArgs a) {
       }
     }
   }
+}
+
+// ------------------------------------------------- last-round split sum ---
+// Sums the ks partial tiles of each split unit in part order (int32 exactly
+// for W8A8) and applies the down epilogue: y = acc * channel scale * row
+// scale, one bf16 rounding.  8 rows per 256-thread block, 8 columns per thread.
+template <bool I8, int BM, int BN, int ROWB, int GN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const GemmArgs a) {
+  constexpr int EB = I8 ? 1 : 2;
+  const int nt = *a.num_tiles;
+  const int nwork = nt * a.n_blocks;
+  const TailPlan tp = tail_plan(nwork, a.conc, (int)((int64_t)a.I * EB / ROWB));
+  const int u = blockIdx.x / (BM / 8);
+  if (u >= nwork - tp.nmain) return;
+  const int2 tn = raster<GN>(tp.nmain + u, nt, a.n_blocks);
+  const int4 td = reinterpret_cast<const int4*>(a.tiles)[tn.x];
+  const int row = (blockIdx.x - u * (BM / 8)) * 8 + (threadIdx.x >> 5);
+  if (row >= td.z) return;
+  const int c = (threadIdx.x & 31) * 8;
+  const int32_t* pp = reinterpret_cast<const int32_t*>(a.partial) + (size_t)u * tp.ks * BM * BN + row * BN + c;
+  float acc[8];
+  if constexpr (I8) {
+    int32_t s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int z = 0; z < tp.ks; ++z) {
+      const i32x4 p0 = *reinterpret_cast<const i32x4*>(pp + (size_t)z * BM * BN);
+      const i32x4 p1 = *reinterpret_cast<const i32x4*>(pp + (size_t)z * BM * BN + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] += p0[i];
+        s[4 + i] += p1[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (float)s[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int z = 0; z < tp.ks; ++z) {
+      float v[8];
+      load8(reinterpret_cast<const float*>(pp + (size_t)z * BM * BN), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+  const int r = td.y + row;
+  float wr = a.topk_w ? a.topk_w[a.sorted_slot[r]] : 1.f;
+  if (I8) wr *= a.hs[r];
+  const int col = tn.y * BN + c;
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = acc[i] * (I8 ? a.wscale[(int64_t)td.x * a.H + col + i] : 1.f) * wr;
+  store8(reinterpret_cast<uint16_t*>(a.out) + (int64_t)r * a.H + col, o);
 }
 
 // ----------------------------------------------------- W8A8 h quantise ---
@@ -502,20 +628,42 @@ struct FfnBufs {
   uint32_t* rowmax;
   int8_t* hq;
   float* hs;
+  void* partial;   // down, last-round split
 };
 
-FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype) {
+// the down GEMM's last-round split is used by the prefill tile (variant 0):
+// at most kTailParts partial 256 x 256 tiles of 4 bytes
+constexpr int kTailParts = 256;
+constexpr size_t kTailBytes = (size_t)kTailParts * 256 * 256 * 4;
+
+FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int down_var) {
   uint8_t* wsb = (uint8_t*)ws;
-  FfnBufs b{wsb, nullptr, nullptr, nullptr};
+  FfnBufs b{wsb, nullptr, nullptr, nullptr, nullptr};
+  size_t off = align256((size_t)n * I * (w_dtype == kI8 ? 4 : 2));
   if (w_dtype == kI8) {
-    size_t off = align256((size_t)n * I * 4);
     b.rowmax = (uint32_t*)(wsb + off);
     off += align256((size_t)n * 4);
     b.hq = (int8_t*)(wsb + off);
     off += align256((size_t)n * I);
     b.hs = (float*)(wsb + off);
+    off += align256((size_t)n * 4);
   }
+  if (w_dtype != kF32 && down_var == 0) b.partial = wsb + off;
   return b;
+}
+
+// workgroups resident at once for the one-per-CU prefill tile: the device's
+// compute units, capped at kTailParts (queried once per device)
+int resident_tiles() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  n = n < kTailParts ? n : kTailParts;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
 }
 
 struct Variant {
@@ -545,7 +693,7 @@ constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4,
 
 template <bool I8, bool UP>
 hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
-  const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
+  const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks + (unsigned)a.conc;
   if constexpr (UP) {
     switch (var) {
       MOE_GG_CASE(0, 256, 256, 4, 4, 2, 128, 4)
@@ -621,7 +769,13 @@ hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const 
   a.k = 1;
   a.n_blocks = H / kDownVar[p.down_var].bn;
   a.max_tiles = (int)p.max_tiles;
-  return launch_gg<I8, false>(p.down_var, a, s);
+  a.partial = b.partial;
+  a.conc = (p.down_var == 0 && b.partial) ? resident_tiles() : 0;
+  hipError_t err = launch_gg<I8, false>(p.down_var, a, s);
+  if (err != hipSuccess || a.conc == 0) return err;
+  // variant 0: 256 x 256, 128-byte rows, raster groups of 2
+  tail_reduce_kernel<I8, 256, 256, 128, 2><<<(unsigned)(a.conc / 2) * (256 / 8), 256, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -656,6 +810,7 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     else
       p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
                    align256((size_t)n * 4);
+    if (p.down_var == 0) p.ws_bytes += kTailBytes;
   }
   p.max_tiles = align_max_tiles(T, k, E, p.block_m);
   return p;
@@ -665,7 +820,7 @@ hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const
                          int w_dtype, const float* s13, const int32_t* sorted_slot,
                          const int32_t* tiles, const int32_t* num_tiles, int64_t T, int H, int I,
                          int k, void* ws, hipStream_t s) {
-  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype);
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.down_var);
   if (w_dtype == kF32) {
     const unsigned mt = (unsigned)p.max_tiles;
     ffn_f32_kernel<true><<<mt * (I / 32), 256, 0, s>>>((const float*)x, (const float*)w13, sorted_slot,
@@ -682,7 +837,7 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
                            const int32_t* sorted_slot, const int32_t* tiles,
                            const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
                            int k, void* y, void* ws, hipStream_t s) {
-  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype);
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.down_var);
   if (w_dtype == kF32) {
     const unsigned mt = (unsigned)p.max_tiles;
     ffn_f32_kernel<false><<<mt * (H / 32), 256, 0, s>>>((const float*)b.h, (const float*)w2,

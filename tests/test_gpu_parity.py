@@ -300,6 +300,10 @@ SMALL = [
     moe_synth.Spec("bf16_E1_k1", 200, 128, 1, 1, 128),
     moe_synth.Spec("bf16_k_eq_E", 90, 128, 4, 4, 64, wg_dtype="f32"),
     moe_synth.Spec("bf16_T1_E256", 1, 512, 256, 8, 128),
+    # prefill tiles with a mostly empty last round: the down GEMM splits that
+    # round's units over K (partial tiles summed by the reduce kernel)
+    moe_synth.Spec("bf16_prefill_last_round_split", 1024, 512, 4, 2, 512),
+    moe_synth.Spec("i8_prefill_last_round_split", 1024, 512, 4, 2, 512, w_dtype="i8"),
 ]
 
 
