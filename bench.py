@@ -48,6 +48,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, Mixtral-shaped prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-library-ref", action="store_true",
+                    help="skip the hipBLASLt (torch.bmm) reference on the same GEMM shapes")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (to calibrate HBM byte counters) and exit")
@@ -148,6 +150,33 @@ def traffic_for(workload: str, kernel_src: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def library_gemm_reference(torch, spec, d, N: int, D: int):
+    """hipBLASLt (torch.bmm) on the up and down GEMM shapes of this workload,
+    for context: D experts x ceil(N/D) rows, no gather and no epilogue."""
+    if spec.w_dtype != "bf16" or D == 0:
+        return None
+    m = -(-N // D)
+    H, I = spec.H, spec.I
+    e = torch.nonzero(torch.ones(spec.E)).flatten()[:D]
+    res = {}
+    for name, b, k_, n_ in (("up", d["w13"], H, 2 * I), ("down", d["w2"], I, H)):
+        bt = b[e.to(b.device)].transpose(1, 2).contiguous()    # [D, K, N], contiguous right operand
+        a = torch.randn(D, m, k_, device="cuda").to(torch.bfloat16)
+        torch.bmm(a, bt)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            torch.bmm(a, bt)
+        c1.record()
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / 5
+        res[name] = {"shape": [D, m, k_, n_], "ms": ms,
+                     "frac_of_peak": 2.0 * D * m * k_ * n_ / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"]}
+        del bt, a
+    return res
+
+
 def cpu_baseline(cfg: int, sample_n: int) -> dict:
     import moe_synth
     import oracle
@@ -222,17 +251,20 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    gpu_ms = e0.elapsed_time(e1) / args.steps
-    log(f"layer: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on the stream")
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    gpu_ms = float(per_step.mean())
+    log(f"layer: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on the stream "
+        f"(p10 {np.percentile(per_step, 10):.3f}, median {np.median(per_step):.3f}, "
+        f"p90 {np.percentile(per_step, 90):.3f})")
 
     # staged pass: per-kernel durations from events between launches
     st = Staged(moe, torch, spec, d, C)
@@ -248,6 +280,31 @@ def main() -> int:
         acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
     stage_ms = dict(zip(names, (acc / args.steps).tolist()))
     log("stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
+
+    # isolated cold: a 1 GiB write before each staged pass evicts L2 and the
+    # last-level cache, so every stage reads its inputs from HBM
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    acc = np.zeros(5)
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        st.run(evs)
+        torch.cuda.synchronize()
+        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
+    cold_ms = dict(zip(names, (acc / args.steps).tolist()))
+    log("stages cold (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in cold_ms.items()))
+    # measured streaming rate: a 1 GiB device copy (read + write)
+    dst = torch.empty_like(flush)
+    dst.copy_(flush)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(flush)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_GBps = 5 * 2 * flush.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del flush, dst
+    lib_ref = library_gemm_reference(torch, spec, d, N, D) if not args.no_library_ref else None
 
     # algorithmic work (bytes / flops the method must move or do)
     bx, bg, bw = BYTES[spec.x_dtype], BYTES[spec.wg_dtype], BYTES[spec.w_dtype]
@@ -289,6 +346,14 @@ def main() -> int:
                                 "GBps": rac_bytes / rac_s / 1e9,
                                 "frac_of_hbm": rac_bytes / rac_s / 1e9 / PEAK_HBM_GBPS},
         "stages_ms": stage_ms,
+        "stages_ms_cold": cold_ms,
+        "route_align_combine_cold": {"ms": sum(cold_ms[n] for n in ("route", "align", "combine")),
+                                     "frac_of_hbm": rac_bytes / (sum(cold_ms[n] for n in ("route", "align", "combine"))
+                                                                 * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "layer_ms_p10_p50_p90": [float(np.percentile(per_step, 10)), float(np.median(per_step)),
+                                 float(np.percentile(per_step, 90))],
+        "measured_copy_GBps": copy_GBps,
+        "library_bmm_same_shapes": lib_ref,
         "kept_rows_N": N, "active_experts_D": D, "capacity": C,
         "layer_gpu_ms": gpu_ms,
         "dispatch": dispatch,
