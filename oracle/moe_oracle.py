@@ -41,6 +41,9 @@ R7  W8A8: activations quantised per token with the LightOP rule, int8 weights
     carry one fp32 scale per output channel, the int GEMM result is scaled by
     (activation scale of the row) * (weight scale of the column); the FFN's
     second GEMM quantises h the same way, one scale per row of h.
+R8  MoE Sum's fused shared-expert factor and bias ([LightOP] section 3.2) add
+    shared_factor * S[t] (the shared expert's output for token t) and a
+    per-column bias b to the routed sum; the page names the fusion only.
 """
 from __future__ import annotations
 
@@ -52,7 +55,7 @@ import numpy as np
 __all__ = [
     "to_f64", "gate_logits", "softmax_rows", "topk_rows", "renormalise", "route",
     "quant_per_token_int8", "capacity", "align", "tiles", "silu", "swiglu_ffn",
-    "layer", "layer_from_inputs", "layer_token_major", "combine",
+    "layer", "layer_from_inputs", "layer_token_major", "combine", "combine_shared",
 ]
 
 
@@ -258,6 +261,24 @@ def combine(y_rows: np.ndarray, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
     for j in range(k):
         kept = pos[:, j] >= 0
         out[kept] += w[kept, j][:, None] * y_rows[pos[kept, j]]
+    return out
+
+
+def combine_shared(y_rows: np.ndarray, pos: np.ndarray, w: np.ndarray, shared: np.ndarray | None,
+                   shared_factor: float, bias: np.ndarray | None) -> np.ndarray:
+    """MoE Sum with the shared-expert term and a bias (R8):
+    out[t] = sum over kept slots j of w[t,j] * Y[pos[t,j]] + shared_factor * S[t] + b.
+
+    [LightOP] section 3.2 (MoE Sum) fuses the shared-expert factor and a bias
+    add into the merge without giving the formula; the reading here adds the
+    shared expert's output S [T,H], scaled by one scalar, and a per-column
+    bias [H] to the routed sum.  Either term may be absent.
+    """
+    out = combine(y_rows, pos, w)
+    if shared is not None:
+        out = out + float(shared_factor) * np.asarray(shared, dtype=np.float64)
+    if bias is not None:
+        out = out + np.asarray(bias, dtype=np.float64)[None, :]
     return out
 
 

@@ -350,3 +350,30 @@ def test_pages_figures():
     assert sum(v[0] for k, v in h.items() if isinstance(v, list)) == h["total_reads"]
     assert sum(v[1] for k, v in h.items() if isinstance(v, list)) == h["total_writes"]
     assert oracle.capacity(4096, 8, 256, g["capacity_factor"]["factor"]) == 160
+
+
+# ---------------------------------------------------------- combine_shared
+def test_combine_shared_closed_forms():
+    """R8: the shared-expert term and the bias are added to the routed sum.
+    Pins: every slot dropped leaves exactly factor*S + b; the difference from
+    the plain combine is factor*S + b whatever the routing; factor 0 and no
+    bias give the plain combine; a lone kept slot with weight 1 and a zero
+    shared term reproduces the expert row plus b."""
+    rng = np.random.default_rng(11)
+    T, k, H, N = 9, 3, 16, 20
+    y = rng.standard_normal((N, H))
+    pos = rng.integers(-1, N, size=(T, k))
+    w = rng.random((T, k))
+    S = rng.standard_normal((T, H))
+    b = rng.standard_normal(H)
+    f = -0.75
+    dropped = np.full((T, k), -1)
+    np.testing.assert_array_equal(oracle.combine_shared(y, dropped, w, S, f, b), f * S + b[None, :])
+    diff = oracle.combine_shared(y, pos, w, S, f, b) - oracle.combine(y, pos, w)
+    np.testing.assert_allclose(diff, f * S + b[None, :], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(oracle.combine_shared(y, pos, w, S, 0.0, None), oracle.combine(y, pos, w))
+    np.testing.assert_array_equal(oracle.combine_shared(y, pos, w, None, f, None), oracle.combine(y, pos, w))
+    one = np.full((1, k), -1)
+    one[0, 1] = 7
+    got = oracle.combine_shared(y, one, np.ones((1, k)), np.zeros((1, H)), 3.0, b)
+    np.testing.assert_array_equal(got[0], y[7] + b)
