@@ -187,6 +187,23 @@ moe_status moe_combine(const void* y_sorted, int32_t y_dtype, const int32_t* pos
                        const float* topk_w, int64_t T, int32_t k, int32_t H, void* out,
                        int32_t out_dtype, void* stream);
 
+/* moe_combine plus the shared expert's term and a bias, fused into the same
+ * single write ([LightOP] section 3.2, MoE Sum: shared-expert factor and bias
+ * add):
+ *   out[t, h] = ((sum as in moe_combine) + shared_factor * shared[t, h]) + bias[h]
+ * each step rounded in fp32, then one rounding to out_dtype.
+ *   shared [T, H] in out_dtype (the shared expert's output), or NULL for none;
+ *     it may be the same buffer as out (an in-place update), but must not
+ *     otherwise overlap it.
+ *   bias [H] fp32, 16-byte aligned, or NULL for none.
+ * Other arguments and errors as in moe_combine; a non-finite shared_factor
+ * is MOE_ERR_INVALID_ARG.  With shared and bias both NULL the result equals
+ * moe_combine's. */
+moe_status moe_combine_shared(const void* y_sorted, int32_t y_dtype, const int32_t* pos,
+                              const float* topk_w, int64_t T, int32_t k, int32_t H,
+                              const void* shared, float shared_factor, const float* bias,
+                              void* out, int32_t out_dtype, void* stream);
+
 /* -------------------------------------------------------------- layer ----
  * The whole MoE branch (route, align, expert FFN, combine) enqueued on one
  * stream with no host synchronisation ([FA-MoE] fused MoE call: attention

@@ -41,6 +41,8 @@ SIGNATURES = {
     "moe_ffn_down": (_st, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                            _i32, _vp, _sz, _vp]),
     "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
+    "moe_combine_shared": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, ctypes.c_float, _vp, _vp,
+                                 _i32, _vp]),
     "moe_layer_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_layer": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
                         _i32, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
@@ -213,6 +215,29 @@ def combine(y_sorted: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor | No
     out = torch.empty((T, H), dtype=out_dtype, device=y_sorted.device)
     _check(lib.moe_combine(_p(y_sorted), _DT[y_sorted.dtype], _p(pos), _p(topk_w), T, k, H, _p(out),
                            _DT[out_dtype], _stream(y_sorted.device)))
+    return out
+
+
+def combine_shared(y_sorted: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor | None, T: int, k: int,
+                   out_dtype: torch.dtype, shared: torch.Tensor | None = None, shared_factor: float = 1.0,
+                   bias: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """moe_combine_shared: out [T, H] = routed sum + shared_factor * shared + bias.
+    `out` may be `shared` itself (in-place update of the shared expert's output)."""
+    _dev(y_sorted, "y_sorted"), _dev(pos, "pos")
+    H = y_sorted.shape[1]
+    if shared is not None:
+        _dev(shared, "shared")
+        if shared.dtype != out_dtype or tuple(shared.shape) != (T, H):
+            raise ValueError(f"shared must be [{T}, {H}] {out_dtype}")
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != torch.float32 or tuple(bias.shape) != (H,):
+            raise ValueError(f"bias must be [{H}] float32")
+    if out is None:
+        out = torch.empty((T, H), dtype=out_dtype, device=y_sorted.device)
+    _check(lib.moe_combine_shared(_p(y_sorted), _DT[y_sorted.dtype], _p(pos), _p(topk_w), T, k, H,
+                                  _p(shared), float(shared_factor), _p(bias), _p(out), _DT[out_dtype],
+                                  _stream(y_sorted.device)))
     return out
 
 

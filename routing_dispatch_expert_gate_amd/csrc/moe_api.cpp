@@ -5,6 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <cmath>
 #include <string>
 
 #include "moe.h"
@@ -390,6 +391,36 @@ moe_status moe_combine(const void* y_sorted, int32_t y_dtype, const int32_t* pos
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_combine launch");
   return ok(topk_w ? "combine_kernel<weighted>" : "combine_kernel<pre-weighted>");
+}
+
+moe_status moe_combine_shared(const void* y_sorted, int32_t y_dtype, const int32_t* pos,
+                              const float* topk_w, int64_t T, int32_t k, int32_t H,
+                              const void* shared, float shared_factor, const float* bias,
+                              void* out, int32_t out_dtype, void* stream) {
+  MOE_TRY(check_dims(T, H, moe::kMaxE, k));
+  if (!is_act(y_dtype) || !is_act(out_dtype))
+    return fail(MOE_ERR_UNSUPPORTED, "combine dtypes must be MOE_F32 or MOE_BF16");
+  if (!std::isfinite(shared_factor))
+    return fail(MOE_ERR_INVALID_ARG, "shared_factor must be finite");
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(y_sorted);
+  MOE_NONNULL(pos);
+  MOE_NONNULL(out);
+  MOE_ALIGNED(y_sorted, 16);
+  MOE_ALIGNED(out, 16);
+  if (shared) MOE_ALIGNED(shared, 16);
+  if (bias) MOE_ALIGNED(bias, 16);
+  if (shared && shared != out) {
+    // partial overlap would let one thread's write land on another's input
+    const size_t bytes = (size_t)T * (size_t)H * (out_dtype == MOE_BF16 ? 2 : 4);
+    const char *a = (const char*)shared, *b = (const char*)out;
+    if (a < b + bytes && b < a + bytes)
+      return fail(MOE_ERR_INVALID_ARG, "shared overlaps out without being out");
+  }
+  hipError_t e = moe::launch_combine_shared(y_sorted, y_dtype, pos, topk_w, T, k, H, shared,
+                                            shared_factor, bias, out, out_dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_combine_shared launch");
+  return ok(topk_w ? "combine_kernel<weighted,shared+bias>" : "combine_kernel<pre-weighted,shared+bias>");
 }
 
 size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,

@@ -160,6 +160,11 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
 // combine.hip
 hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pos, const float* w, int64_t T,
                           int k, int H, void* out, int out_dtype, hipStream_t s);
+// the same plus factor * shared[t] (out dtype, may be null or equal to out)
+// and bias[h] (fp32, may be null), added to the fp32 sum before the write
+hipError_t launch_combine_shared(const void* y, int y_dtype, const int32_t* pos, const float* w,
+                                 int64_t T, int k, int H, const void* shared, float factor,
+                                 const float* bias, void* out, int out_dtype, hipStream_t s);
 
 // ffn_*.hip
 struct FfnPlan {

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -131,6 +131,18 @@ def test_combine_and_layer_validation(moe):
     assert L.moe_combine(P, I8, P, None, 64, 2, 128, P, BF16, None) == UNSUPPORTED
     assert L.moe_combine(None, BF16, P, None, 64, 2, 128, P, BF16, None) == INVALID
     assert L.moe_combine(P, BF16, P, None, 0, 2, 128, P, BF16, None) == OK
+
+    def cs(T=64, shared=None, f=1.0, bias=None, out=P, yd=BF16, od=BF16, H=128):
+        return L.moe_combine_shared(P, yd, P, None, T, 2, H, shared, f, bias, out, od, None)
+
+    assert cs(yd=I8) == UNSUPPORTED
+    assert cs(H=96) == UNSUPPORTED
+    assert cs(f=float("nan")) == INVALID
+    assert cs(f=float("inf"), T=0) == INVALID          # the factor is checked even for T == 0
+    assert cs(out=None) == INVALID
+    assert cs(bias=ctypes.c_void_p(260)) == INVALID    # bias must be 16-byte aligned
+    assert cs(shared=ctypes.c_void_p(272)) == INVALID  # overlaps out without being out
+    assert cs(T=0) == OK
 
     def layer(xd=BF16, wd=BF16, od=BF16, T=64, H=128, I=128, E=8, k=2, ws=None, nws=0, s=None):
         return L.moe_layer(P, xd, P, BF16, None, P, P, wd, s, s, T, H, I, E, k, 0, P, od, None, ws, nws, None)

@@ -312,6 +312,82 @@ def test_ffn_combine_small_shapes(spec):
     _ffn_combine_case(Case(spec, 4242), np.arange(spec.T))
 
 
+# -------------------------------------------------------- combine + shared
+COMBINE_SHARED = [
+    # T, H, E, k, C, y dtype, out dtype, shared, bias, in place
+    (257, 192, 8, 2, 60, "bf16", "bf16", True, True, False),
+    (130, 256, 16, 3, 0, "f32", "f32", True, False, False),
+    (64, 128, 64, 8, 9, "bf16", "f32", False, True, False),
+    (300, 320, 4, 1, 70, "f32", "bf16", True, True, True),
+    (33, 64, 32, 6, 2, "bf16", "bf16", True, True, True),   # almost every slot dropped
+]
+
+
+@pytest.mark.parametrize("case", COMBINE_SHARED, ids=lambda c: "T%d_H%d_k%d_%s_%s" % (c[0], c[1], c[3], c[5], c[6]))
+def test_combine_shared_matches_oracle(case):
+    """moe_combine_shared against the oracle's combine_shared, element by
+    element: routed sum in slot order + factor * S + b, fp32 on the GPU."""
+    moe = _moe()
+    T, H, E, k, C, ydt, odt, with_s, with_b, in_place = case
+    rng = np.random.default_rng(T * 1000 + H)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    al = oracle.align(ids, E, C)
+    pos = al["pos"].reshape(T, k)
+    N = max(int(al["offsets"][-1]), 1)
+    y = rng.standard_normal((N, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    S = rng.standard_normal((T, H)).astype(np.float32) if with_s else None
+    b = rng.standard_normal(H).astype(np.float32) if with_b else None
+    f = -0.625
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+    y_d = torch.from_numpy(y).cuda().to(tdt[ydt])
+    S_d = torch.from_numpy(S).cuda().to(tdt[odt]) if with_s else None
+    # the oracle sees exactly the stored values
+    y64 = y_d.float().cpu().numpy().astype(np.float64)
+    S64 = S_d.float().cpu().numpy().astype(np.float64) if with_s else None
+    ref = oracle.combine_shared(y64, pos, w.astype(np.float64), S64, f, b)
+    out = S_d if in_place else None
+    got = moe.combine_shared(y_d, to_dev(al["pos"].astype(np.int32)), to_dev(w), T, k, tdt[odt], shared=S_d,
+                             shared_factor=f, bias=to_dev(b), out=out)
+    if in_place:
+        assert got.data_ptr() == S_d.data_ptr()
+    torch.cuda.synchronize()
+    print(moe.last_dispatch())
+    g = got.float().cpu().numpy().astype(np.float64)
+    # fp32 accumulation of k+2 terms, then one rounding to the output dtype
+    mag = np.zeros((T, H))
+    for j in range(k):
+        keep = pos[:, j] >= 0
+        mag[keep] += np.abs(w[keep, j, None] * y64[pos[keep, j]])
+    if with_s:
+        mag += abs(f) * np.abs(S64)
+    if with_b:
+        mag += np.abs(b)[None, :]
+    out_eps = 2.0 ** -8 if odt == "bf16" else 2.0 ** -24
+    bound = out_eps * np.abs(ref) + (k + 2) * 2.0 ** -24 * mag * (1 + out_eps) + 1e-30
+    err = np.abs(g - ref)
+    assert np.all(err <= bound), (float((err / bound).max()), np.unravel_index(np.argmax(err / bound), err.shape))
+    # tokens with every slot dropped get exactly the rounded factor * S + b
+    dead = np.all(pos < 0, axis=1)
+    if dead.any() and not with_s and not with_b:
+        assert np.all(g[dead] == 0)
+
+
+def test_combine_shared_without_extras_equals_combine():
+    moe = _moe()
+    rng = np.random.default_rng(5)
+    T, H, E, k = 200, 256, 16, 4
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    al = oracle.align(ids, E, 40)
+    y = torch.from_numpy(rng.standard_normal((int(al["offsets"][-1]), H)).astype(np.float32)).cuda().bfloat16()
+    w = to_dev(rng.random((T, k)).astype(np.float32))
+    p = to_dev(al["pos"].astype(np.int32))
+    a = moe.combine(y, p, w, T, k, torch.bfloat16)
+    b = moe.combine_shared(y, p, w, T, k, torch.bfloat16, shared=None, shared_factor=3.0, bias=None)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 # ------------------------------------------------------------------ layer
 def _layer_case(c, sample, check_aux=True):
     moe = _moe()
