@@ -44,6 +44,15 @@ R7  W8A8: activations quantised per token with the LightOP rule, int8 weights
 R8  MoE Sum's fused shared-expert factor and bias ([LightOP] section 3.2) add
     shared_factor * S[t] (the shared expert's output for token t) and a
     per-column bias b to the routed sum; the page names the fusion only.
+R9  group-limited routing ([LightOP] section 3.1, Moe Fuse Gate: groups are
+    chosen first, with each group's Top1/Top2 kept): the E experts form
+    n_group contiguous groups of E/n_group; a group scores the sum of its two
+    largest softmax probabilities (its only one for groups of one); the
+    topk_group best groups (equal scores: lower group index first) are the
+    only candidates for the usual top-k, whose weights are renormalised as
+    in route.  The probabilities are those of the plain router's softmax.
+    parity of this reading against the page is unpinned: the page gives no
+    formula; the pins below fix the oracle to the reading itself.
 """
 from __future__ import annotations
 
@@ -56,6 +65,7 @@ __all__ = [
     "to_f64", "gate_logits", "softmax_rows", "topk_rows", "renormalise", "route",
     "quant_per_token_int8", "capacity", "align", "tiles", "silu", "swiglu_ffn",
     "layer", "layer_from_inputs", "layer_token_major", "combine", "combine_shared",
+    "group_scores", "route_grouped",
 ]
 
 
@@ -138,6 +148,55 @@ def route(x: np.ndarray, wg: np.ndarray, k: int, bias: np.ndarray | None = None)
         gap_l = np.full(T, np.inf)
     return {"logits": logits, "p": p, "ids": ids.astype(np.int32), "w": w, "p_sel": p_sel,
             "gap_p": gap_p, "gap_logit": gap_l}
+
+
+def group_scores(p: np.ndarray, n_group: int) -> np.ndarray:
+    """Score of each contiguous expert group (R9): the sum of the group's two
+    largest probabilities, or its single probability for groups of one."""
+    T, E = p.shape
+    gsz = E // n_group
+    grouped = p.reshape(T, n_group, gsz)
+    desc = -np.sort(-grouped, axis=2)
+    return desc[:, :, :min(2, gsz)].sum(axis=2)
+
+
+def route_grouped(x: np.ndarray, wg: np.ndarray, k: int, n_group: int, topk_group: int,
+                  bias: np.ndarray | None = None) -> dict:
+    """Group-limited router (R9) on float64 inputs: softmax as in route, the
+    topk_group best groups by group_scores, then top-k (R4 order) among their
+    experts only, renormalised.  Returns the keys of route plus the group
+    scores, the chosen groups and the topk_group-th/next group-score gap."""
+    T = x.shape[0]
+    E = wg.shape[0]
+    if E % n_group != 0 or not 1 <= topk_group <= n_group or k > topk_group * (E // n_group):
+        raise ValueError("need E % n_group == 0, 1 <= topk_group <= n_group, k <= topk_group * E / n_group")
+    logits = gate_logits(x, wg, bias)
+    p = softmax_rows(logits)
+    gsc = group_scores(p, n_group)
+    gorder = np.argsort(-gsc, axis=1, kind="stable")
+    chosen = gorder[:, :topk_group]
+    allowed = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(allowed, chosen, True, axis=1)
+    candidate = np.repeat(allowed, E // n_group, axis=1)
+    p_cand = np.where(candidate, p, -1.0)     # below every probability
+    ids = topk_rows(p_cand, k)
+    p_sel = np.take_along_axis(p, ids, axis=1)
+    w = renormalise(p_sel)
+    n_cand = topk_group * (E // n_group)
+    if k < n_cand:
+        order = np.argsort(-p_cand, axis=1, kind="stable")
+        pk = np.take_along_axis(p_cand, order[:, k - 1:k + 1], axis=1)
+        gap_p = pk[:, 0] - pk[:, 1]
+    else:
+        gap_p = np.full(T, np.inf)
+    if topk_group < n_group:
+        gk = np.take_along_axis(gsc, gorder[:, topk_group - 1:topk_group + 1], axis=1)
+        gap_group = gk[:, 0] - gk[:, 1]
+    else:
+        gap_group = np.full(T, np.inf)
+    return {"logits": logits, "p": p, "ids": ids.astype(np.int32), "w": w, "p_sel": p_sel,
+            "gap_p": gap_p, "group_scores": gsc, "groups": np.sort(chosen, axis=1),
+            "gap_group": gap_group}
 
 
 # ----------------------------------------------------------------------------

@@ -377,3 +377,99 @@ def test_combine_shared_closed_forms():
     one[0, 1] = 7
     got = oracle.combine_shared(y, one, np.ones((1, k)), np.zeros((1, H)), 3.0, b)
     np.testing.assert_array_equal(got[0], y[7] + b)
+
+
+# ----------------------------------------------------------- route_grouped
+def _identity_gate(logits):
+    """x = the logits, Wg = identity: the router sees exactly these logits."""
+    logits = np.atleast_2d(np.asarray(logits, dtype=np.float64))
+    return logits, np.eye(logits.shape[1])
+
+
+def test_route_grouped_hand_worked():
+    """E=8 in 4 groups of 2, 2 groups kept, top-2.  Probabilities
+    (.26 .01 | .20 .15 | .19 .17 | .01 .01): group scores .27 .35 .36 .02, so
+    groups 2 and 1 are kept and the global favourite, expert 0, is excluded;
+    the top-2 among experts 2..5 is (2, 4) with weights .20/.39 and .19/.39.
+    The plain router would pick (0, 2)."""
+    p = np.array([0.26, 0.01, 0.20, 0.15, 0.19, 0.17, 0.01, 0.01])
+    x, wg = _identity_gate(np.log(p))
+    r = oracle.route_grouped(x, wg, 2, 4, 2)
+    np.testing.assert_allclose(r["group_scores"][0], [0.27, 0.35, 0.36, 0.02], rtol=1e-12)
+    np.testing.assert_array_equal(r["groups"][0], [1, 2])
+    np.testing.assert_array_equal(r["ids"][0], [2, 4])
+    np.testing.assert_allclose(r["w"][0], [0.20 / 0.39, 0.19 / 0.39], rtol=1e-12)
+    np.testing.assert_allclose(r["p_sel"][0], [0.20, 0.19], rtol=1e-12)
+    np.testing.assert_array_equal(oracle.route(x, wg, 2)["ids"][0], [0, 2])
+
+
+def test_route_grouped_reduces_to_plain_route():
+    """Keeping every group, or groups of one expert with k <= topk_group,
+    leaves the plain top-k."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((50, 24))
+    wg = rng.standard_normal((16, 24))
+    b = rng.standard_normal(16)
+    plain = oracle.route(x, wg, 3, b)
+    for G in (1, 2, 4, 8, 16):
+        r = oracle.route_grouped(x, wg, 3, G, G, b)
+        np.testing.assert_array_equal(r["ids"], plain["ids"])
+        np.testing.assert_array_equal(r["w"], plain["w"])
+    for TG in (3, 5, 16):
+        r = oracle.route_grouped(x, wg, 3, 16, TG, b)
+        np.testing.assert_array_equal(r["ids"], plain["ids"])
+
+
+@pytest.mark.parametrize("E,G,TG,k", [(12, 4, 2, 3), (8, 4, 1, 2), (12, 3, 2, 5), (6, 2, 1, 3)])
+def test_route_grouped_brute_force(E, G, TG, k):
+    """Every subset of TG groups and every k-subset of their experts, scored
+    from the definition: a group's score is its best pair sum, the kept groups
+    maximise the summed score, the kept experts maximise the summed
+    probability among the kept groups' experts."""
+    rng = np.random.default_rng(E * 100 + G * 10 + TG)
+    x = rng.standard_normal((40, 8))
+    wg = rng.standard_normal((E, 8))
+    r = oracle.route_grouped(x, wg, k, G, TG)
+    p = oracle.softmax_rows(x @ wg.T)
+    gsz = E // G
+    for t in range(x.shape[0]):
+        score = []
+        for g in range(G):
+            members = range(g * gsz, (g + 1) * gsz)
+            if gsz == 1:
+                score.append(p[t, g])
+            else:
+                score.append(max(p[t, i] + p[t, j] for i, j in itertools.combinations(members, 2)))
+        best_groups = max(itertools.combinations(range(G), TG), key=lambda c: sum(score[g] for g in c))
+        cand = [e for g in best_groups for e in range(g * gsz, (g + 1) * gsz)]
+        best = max(itertools.combinations(cand, k), key=lambda c: sum(p[t, e] for e in c))
+        assert set(r["ids"][t]) == set(best), t
+        assert tuple(r["groups"][t]) == tuple(sorted(best_groups)), t
+        assert np.all(np.diff(p[t, r["ids"][t]]) <= 0)
+
+
+def test_route_grouped_ties_and_invariants():
+    # groups 0 and 1 score the same: the lower group wins, then the lower ids
+    x, wg = _identity_gate([0.0, 0.0, 0.0, 0.0, -5.0, -5.0, -5.0, -5.0])
+    r = oracle.route_grouped(x, wg, 2, 4, 1)
+    np.testing.assert_array_equal(r["groups"][0], [0])
+    np.testing.assert_array_equal(r["ids"][0], [0, 1])
+    np.testing.assert_allclose(r["w"][0], [0.5, 0.5], rtol=0, atol=0)
+    # random rows: ids lie in at most TG groups, weights sum to 1, and every
+    # selected probability beats every other candidate of the kept groups
+    rng = np.random.default_rng(3)
+    E, G, TG, k = 64, 8, 3, 6
+    x = rng.standard_normal((200, 32))
+    wg = rng.standard_normal((E, 32))
+    r = oracle.route_grouped(x, wg, k, G, TG)
+    gsz = E // G
+    for t in range(200):
+        gs = set(int(i) // gsz for i in r["ids"][t])
+        assert gs <= set(r["groups"][t].tolist()) and len(r["groups"][t]) == TG
+        cand = [e for g in r["groups"][t] for e in range(g * gsz, (g + 1) * gsz) if e not in r["ids"][t]]
+        assert r["p"][t, r["ids"][t]].min() >= r["p"][t, cand].max()
+    np.testing.assert_allclose(r["w"].sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.route_grouped(x, wg, k, 7, 3)          # E not a multiple of n_group
+    with pytest.raises(ValueError):
+        oracle.route_grouped(x, wg, 9, 8, 1)          # k beyond one group's 8 experts
