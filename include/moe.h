@@ -85,6 +85,28 @@ moe_status moe_route(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
                      int32_t* topk_ids, float* topk_w, float* topk_p, int8_t* xq, float* xs,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Group-limited routing ([LightOP] section 3.1, Moe Fuse Gate: groups are
+ * picked first, each group's Top1/Top2 kept).  The page gives no formula;
+ * this is the reading implemented:
+ *   the E experts form n_group contiguous groups of E / n_group experts;
+ *   a group's score is the sum of its two largest softmax probabilities (its
+ *   only one when groups have one expert);
+ *   the topk_group highest-scoring groups are kept (equal scores: the lower
+ *   group index first), and top-k runs over their experts only, ordered and
+ *   renormalised exactly as in moe_route; topk_p holds the probabilities of
+ *   the full softmax over all E experts.
+ * topk_group == n_group gives moe_route's result.
+ * Arguments as in moe_route (same workspace size), plus:
+ *   n_group     in [1, 64], divides E;  topk_group in [1, n_group];
+ *   k <= topk_group * E / n_group, else MOE_ERR_INVALID_ARG.
+ * Supported: 16 < E <= 256, E % 16 == 0, bf16 x and bf16 wg (the MFMA
+ * logits path); other shapes return MOE_ERR_UNSUPPORTED. */
+moe_status moe_route_grouped(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                             const float* bias, int64_t T, int32_t H, int32_t E, int32_t k,
+                             int32_t n_group, int32_t topk_group, int32_t* topk_ids, float* topk_w,
+                             float* topk_p, int8_t* xq, float* xs, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------- capacity -----
  * Per-expert capacity C = ceil(factor * T * k / E) ([Router] section on
  * communication/computation overlap, capacity limit, with the load counted as

@@ -27,6 +27,8 @@ SIGNATURES = {
     "moe_route_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
     "moe_route": (_st, [_vp, _i32, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                         _vp, _sz, _vp]),
+    "moe_route_grouped": (_st, [_vp, _i32, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                                _vp, _vp, _vp, _sz, _vp]),
     "moe_capacity": (_i64, [_i64, _i32, _i32, _f64]),
     "moe_align_workspace_size": (_sz, [_i64, _i32, _i32]),
     "moe_align_max_tiles": (_i64, [_i64, _i32, _i32, _i32]),
@@ -116,9 +118,11 @@ def capacity(T: int, k: int, E: int, factor: float) -> int:
 
 
 def route(x: torch.Tensor, wg: torch.Tensor, k: int, bias: torch.Tensor | None = None,
-          want_p: bool = True, quant: bool = False) -> dict:
+          want_p: bool = True, quant: bool = False, n_group: int | None = None,
+          topk_group: int | None = None) -> dict:
     """moe_route: returns ids [T,k] int32, w [T,k] fp32, p [T,k] fp32 (or None),
-    and xq [T,H] int8 / xs [T] fp32 when ``quant``."""
+    and xq [T,H] int8 / xs [T] fp32 when ``quant``.  With ``n_group`` and
+    ``topk_group`` it calls moe_route_grouped (group-limited selection)."""
     _dev(x, "x"), _dev(wg, "wg")
     T, H = x.shape
     E = wg.shape[0]
@@ -132,8 +136,15 @@ def route(x: torch.Tensor, wg: torch.Tensor, k: int, bias: torch.Tensor | None =
         _dev(bias, "bias")
     nws = lib.moe_route_workspace_size(T, H, E, k)
     ws = _ws(nws, dev)
-    _check(lib.moe_route(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), T, H, E, k, _p(ids),
-                         _p(w), _p(p), _p(xq), _p(xs), _p(ws), nws, _stream(dev)))
+    if (n_group is None) != (topk_group is None):
+        raise ValueError("n_group and topk_group go together")
+    if n_group is None:
+        _check(lib.moe_route(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), T, H, E, k, _p(ids),
+                             _p(w), _p(p), _p(xq), _p(xs), _p(ws), nws, _stream(dev)))
+    else:
+        _check(lib.moe_route_grouped(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), T, H, E, k,
+                                     int(n_group), int(topk_group), _p(ids), _p(w), _p(p), _p(xq), _p(xs),
+                                     _p(ws), nws, _stream(dev)))
     return {"ids": ids, "w": w, "p": p, "xq": xq, "xs": xs}
 
 

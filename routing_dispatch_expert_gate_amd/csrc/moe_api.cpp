@@ -222,6 +222,32 @@ moe_status moe_route(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   return ok(route_name(plan));
 }
 
+moe_status moe_route_grouped(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                             const float* bias, int64_t T, int32_t H, int32_t E, int32_t k,
+                             int32_t n_group, int32_t topk_group, int32_t* topk_ids, float* topk_w,
+                             float* topk_p, int8_t* xq, float* xs, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(T, H, E, k));
+  if (n_group < 1 || n_group > 64 || E % n_group != 0)
+    return fail(MOE_ERR_INVALID_ARG, "n_group (%d) must divide E (%d) and be in [1, 64]", n_group, E);
+  if (topk_group < 1 || topk_group > n_group)
+    return fail(MOE_ERR_INVALID_ARG, "topk_group (%d) must be in [1, n_group=%d]", topk_group, n_group);
+  if ((int64_t)k > (int64_t)topk_group * (E / n_group))
+    return fail(MOE_ERR_INVALID_ARG, "k (%d) exceeds the %d experts of the kept groups", k,
+                topk_group * (E / n_group));
+  moe::RoutePlan plan;
+  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, topk_ids, topk_w, xq, xs, &plan));
+  if (plan.kind != 2)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "group-limited routing needs 16 < E <= 256, E %% 16 == 0, bf16 x and bf16 wg (got E=%d)", E);
+  if (T == 0) return ok("none (T=0)");
+  MOE_TRY(check_ws(workspace, workspace_bytes, plan.ws_bytes));
+  hipError_t e = moe::launch_route_grouped(plan, x, wg, bias, T, H, E, k, n_group, topk_group, topk_ids,
+                                           topk_w, topk_p, xq, xs, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_grouped launch");
+  return ok(route_name(plan) + "<grouped>");
+}
+
 size_t moe_align_workspace_size(int64_t T, int32_t k, int32_t E) {
   return moe::plan_align(T, k, E).ws_bytes;
 }

@@ -144,6 +144,12 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype);
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                         const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
                         float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s);
+// group-limited variant (kind 2 plans only): n_group contiguous groups,
+// the topk_group best by their two largest probabilities
+hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* wg, const float* bias,
+                                int64_t T, int H, int E, int k, int n_group, int topk_group,
+                                int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
+                                hipStream_t s);
 
 // align.hip
 struct AlignPlan {

@@ -22,6 +22,8 @@
 //           one wave per token, sums the splits in a fixed order, runs the
 //           top-k and writes the per-token int8 codes.  Deterministic: no
 //           floating-point atomics.
+//           The same pair, with the top-k kernel's group-limited
+//           selection, serves the group-limited router.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -35,17 +37,12 @@ constexpr int kBF16 = 1;
 // --------------------------------------------------------------- top-k ----
 // One wave selects the top-k of one token.  Lane l owns the logits of experts
 // l + 64*j (j < 4, -inf beyond E).  Lanes 0..k-1 write selection i = lane.
-__device__ void wave_topk_store(float v[4], int E, int k, int64_t t, int32_t* __restrict__ ids,
-                                float* __restrict__ w, float* __restrict__ prob) {
+// Selection by k argmax rounds over v (excluded experts hold -inf); m is the
+// token's largest logit and s its softmax denominator (used only for prob).
+__device__ void wave_topk_select_store(float v[4], int k, float m, float s, int64_t t,
+                                       int32_t* __restrict__ ids, float* __restrict__ w,
+                                       float* __restrict__ prob) {
   const int lane = threadIdx.x & 63;
-  float m = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-  float s = 0.f;
-  if (prob) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j < E) s += expf(v[j] - m);
-    s = wave_sum(s);
-  }
   int my_id = 0;
   float my_l = -INFINITY;
   for (int i = 0; i < k; ++i) {
@@ -81,6 +78,76 @@ __device__ void wave_topk_store(float v[4], int E, int k, int64_t t, int32_t* __
     w[t * k + lane] = ex / se;
     if (prob) prob[t * k + lane] = ex / s;
   }
+}
+
+__device__ __forceinline__ float wave_logit_max(const float v[4]) {
+  return wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+}
+__device__ __forceinline__ float wave_softmax_denominator(const float v[4], int E, float m) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (lane + 64 * j < E) s += expf(v[j] - m);
+  return wave_sum(s);
+}
+
+__device__ void wave_topk_store(float v[4], int E, int k, int64_t t, int32_t* __restrict__ ids,
+                                float* __restrict__ w, float* __restrict__ prob) {
+  const float m = wave_logit_max(v);
+  const float s = prob ? wave_softmax_denominator(v, E, m) : 0.f;
+  wave_topk_select_store(v, k, m, s, t, ids, w, prob);
+}
+
+// Group-limited top-k of one token (LightOP page, section 3.1, Moe Fuse Gate:
+// pick the groups first, keeping each group's Top1/Top2).  The E experts form
+// G contiguous groups of E/G; a group's score is the sum of the
+// exponentials of its two largest logits (its probabilities' sum times the
+// token's common softmax denominator, so the order is that of the
+// probabilities); the TG best groups (equal scores: lower group first) keep
+// their experts, every other expert is set to -inf, and the usual argmax
+// rounds select k, weighted as in the plain router with the full softmax.
+// L: this wave's 256-float LDS row; gs: its 64-float LDS row.  G <= 64.
+__device__ void wave_grouped_topk_store(float v[4], float* L, float* gs, int E, int k, int G, int TG,
+                                        int64_t t, int32_t* __restrict__ ids, float* __restrict__ w,
+                                        float* __restrict__ prob) {
+  const int lane = threadIdx.x & 63;
+  const float m = wave_logit_max(v);
+  const float s = prob ? wave_softmax_denominator(v, E, m) : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) L[lane + 64 * j] = v[j];
+  __builtin_amdgcn_wave_barrier();
+  const int gsz = E / G;
+  float score = -INFINITY;
+  if (lane < G) {
+    // the group's two largest logits (a tie counts twice)
+    float a1 = -INFINITY, a2 = -INFINITY;
+    for (int i = 0; i < gsz; ++i) {
+      const float u = L[lane * gsz + i];
+      if (u > a1) {
+        a2 = a1;
+        a1 = u;
+      } else if (u > a2) {
+        a2 = u;
+      }
+    }
+    score = expf(a1 - m) + (gsz > 1 ? expf(a2 - m) : 0.f);
+    gs[lane] = score;
+  }
+  __builtin_amdgcn_wave_barrier();
+  int rank = 0;
+  if (lane < G)
+    for (int g = 0; g < G; ++g) {
+      const float o = gs[g];
+      rank += (o > score || (o == score && g < lane)) ? 1 : 0;
+    }
+  const uint64_t keep = __ballot(lane < G && rank < TG);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    if (e < E && !((keep >> (e / gsz)) & 1ull)) v[j] = -INFINITY;
+  }
+  wave_topk_select_store(v, k, m, s, t, ids, w, prob);
 }
 
 // Top-k of one token by rank, for E <= 64: the token's E logits are in an LDS
@@ -459,12 +526,12 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
 // splits' loads in flight), adds the bias, selects the top-k (by rank from an
 // LDS row when E <= 64, else by argmax rounds) and, with quantisation, writes
 // the token's codes with the absmax the logits kernel folded.
-template <bool QUANT>
+template <bool QUANT, bool GROUPED>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
     const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
-    float* __restrict__ xs) {
+    float* __restrict__ xs, int n_group, int topk_group) {
   __shared__ __attribute__((aligned(16))) float lrow[4][64];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -489,7 +556,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     const int e = lane + 64 * j;
     v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : -INFINITY;
   }
-  if (E <= 64) {
+  if constexpr (GROUPED) {
+    __shared__ __attribute__((aligned(16))) float grow[4][256];
+    __shared__ float gscore[4][64];
+    wave_grouped_topk_store(v, grow[wv], gscore[wv], E, k, n_group, topk_group, t, ids, w, prob);
+  } else if (E <= 64) {
     lrow[wv][lane] = v[0];
     __builtin_amdgcn_wave_barrier();
     wave_topk_rank_store(lrow[wv], E, k, t, ids, w, prob);
@@ -545,9 +616,10 @@ hipError_t launch_fma_dt(const RoutePlan& p, const void* x, int xd, const void* 
   return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
 }
 
+template <bool GROUPED>
 hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                        int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
-                       int8_t* xq, float* xs, void* ws, hipStream_t s) {
+                       int8_t* xq, float* xs, void* ws, int n_group, int topk_group, hipStream_t s) {
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)wg;
   float* part = (float*)ws;
@@ -561,11 +633,11 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
   if (err != hipSuccess) return err;
   const dim3 g2((unsigned)((T + 3) / 4));
   if (xq)
-    route_topk_kernel<true><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq,
-                                               xs);
+    route_topk_kernel<true, GROUPED><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
+                                                        prob, xq, xs, n_group, topk_group);
   else
-    route_topk_kernel<false><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq,
-                                                xs);
+    route_topk_kernel<false, GROUPED><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
+                                                         prob, xq, xs, n_group, topk_group);
   return hipGetLastError();
 }
 
@@ -609,7 +681,15 @@ hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const vo
     return launch_fma_dt<16, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
                                 xs, s);
   }
-  return launch_mfma(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, s);
+  return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, s);
+}
+
+hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* wg, const float* bias,
+                                int64_t T, int H, int E, int k, int n_group, int topk_group,
+                                int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
+                                hipStream_t s) {
+  if (p.kind != 2) return hipErrorInvalidValue;
+  return launch_mfma<true>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, n_group, topk_group, s);
 }
 
 }  // namespace moe

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -87,6 +87,26 @@ def test_route_validation(moe):
     assert _route(moe, E=256, k=8, H=512, ws=ctypes.c_void_p(4096 + 8), nws=1 << 30) == WORKSPACE
     assert _route(moe, T=0) == OK
     assert moe.lib.moe_last_dispatch().decode() == "none (T=0)"
+
+
+def test_route_grouped_validation(moe):
+    L = moe.lib
+    msg = lambda: L.moe_last_error().decode()   # noqa: E731
+
+    def rg(T=64, H=512, E=256, k=8, G=8, TG=4, xd=BF16, wd=BF16, ws=None, nws=0):
+        return L.moe_route_grouped(P, xd, P, wd, None, T, H, E, k, G, TG, P, P, None, None, None, ws, nws, None)
+
+    assert rg(G=7) == INVALID and "n_group" in msg()       # does not divide E
+    assert rg(G=128, E=256) == INVALID                    # more than 64 groups
+    assert rg(TG=0) == INVALID
+    assert rg(TG=9) == INVALID and "topk_group" in msg()
+    assert rg(E=64, G=8, TG=1, k=9) == UNSUPPORTED        # k > 8 fails first
+    assert rg(E=64, G=16, TG=1, k=6) == INVALID and "kept groups" in msg()
+    assert rg(E=16, G=4, TG=2, k=2) == UNSUPPORTED        # E <= 16: no grouped path
+    assert rg(wd=F32) == UNSUPPORTED
+    assert rg() == WORKSPACE
+    assert rg(T=0) == OK
+    assert L.moe_route_workspace_size(64, 512, 256, 8) > 0
 
 
 def test_align_validation(moe):

@@ -170,6 +170,82 @@ def test_route_paths(spec, quant, path):
         np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
 
 
+# --------------------------------------------------- group-limited route
+# (spec, n_group, topk_group, quant): DeepSeek-V3-like 256 experts in 8
+# groups with 4 kept; 160 experts in 8 groups of 20 with 3 kept (groups that
+# straddle lanes); one kept group of 8 (k = 6 inside it); groups of one
+GROUPED = [
+    (moe_synth.Spec("g_e160_G8_TG3", 300, 512, 160, 6, 64, zipf_s=1.1), 8, 3, True),
+    (moe_synth.Spec("g_e64_G8_TG1", 257, 1024, 64, 6, 64), 8, 1, False),
+    (moe_synth.Spec("g_e32_G32_TG5_T1", 1, 256, 32, 4, 64), 32, 5, True),
+    (moe_synth.Spec("g_e256_G8_TG4_splitk", 64, 4096, 256, 8, 64), 8, 4, False),
+]
+
+
+def _check_grouped(r, ro):
+    """ids parity with near ties exempt: the k-th/next candidate gap or the
+    kept/next group-score gap below 1e-4 (fp32 logits vs the fp64 oracle)."""
+    band = dict(ro, gap_p=np.minimum(ro["gap_p"], ro["gap_group"]))
+    ids_g = r["ids"].cpu().numpy()
+    same = check_ids(ids_g, band)
+    assert np.abs(r["w"].cpu().numpy()[same] - ro["w"][same]).max() <= 1e-5
+    if r["p"] is not None:
+        assert np.abs(r["p"].cpu().numpy()[same] - ro["p_sel"][same]).max() <= 1e-5
+    # every row, exempt or not: ids distinct, inside at most topk_group groups
+    return same
+
+
+@pytest.mark.parametrize("spec,G,TG,quant", GROUPED, ids=[g[0].name for g in GROUPED])
+def test_route_grouped_matches_oracle(spec, G, TG, quant):
+    moe = _moe()
+    i = moe_synth.make_inputs(spec, 77, with_experts=False)
+    r = moe.route(to_dev(i.x), to_dev(i.wg), spec.k, bias=to_dev(i.bias), want_p=True, quant=quant,
+                  n_group=G, topk_group=TG)
+    torch.cuda.synchronize()
+    d = moe.last_dispatch()
+    print(d)
+    assert "<grouped>" in d
+    ro = oracle.route_grouped(oracle.to_f64(i.x, spec.x_dtype), oracle.to_f64(i.wg, spec.wg_dtype), spec.k, G,
+                              TG, i.bias)
+    _check_grouped(r, ro)
+    ids = r["ids"].cpu().numpy()
+    gsz = spec.E // G
+    for t in range(spec.T):
+        assert len(set(ids[t].tolist())) == spec.k
+        assert len(set((ids[t] // gsz).tolist())) <= TG
+    if quant:
+        xq_o, xs_o = oracle.quant_per_token_int8(moe_synth.bf16_bits_as_f32(i.x))
+        np.testing.assert_array_equal(r["xq"].cpu().numpy(), xq_o)
+        np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
+
+
+def test_route_grouped_on_fine_grained_workload():
+    """The 4096-token, 256-expert, top-8 workload with 8 groups and 4 kept."""
+    moe = _moe()
+    c = config_case(3)
+    s = c.spec
+    r = moe.route(c.x, c.wg, s.k, bias=c.bias, want_p=True, n_group=8, topk_group=4)
+    torch.cuda.synchronize()
+    ro = oracle.route_grouped(oracle.to_f64(c.inp.x, s.x_dtype), oracle.to_f64(c.inp.wg, s.wg_dtype), s.k, 8, 4,
+                              c.inp.bias)
+    same = _check_grouped(r, ro)
+    # the group limit really changes the routing of some tokens
+    assert (ro["ids"] != c.route["ids"]).any(axis=1).sum() > 0
+    assert same.mean() > 0.99
+
+
+def test_route_grouped_all_groups_equals_plain_route():
+    """topk_group == n_group: bit-identical to moe_route (same arithmetic)."""
+    moe = _moe()
+    spec = moe_synth.Spec("g_all", 300, 1024, 256, 8, 64)
+    i = moe_synth.make_inputs(spec, 5, with_experts=False)
+    a = moe.route(to_dev(i.x), to_dev(i.wg), 8, bias=to_dev(i.bias), want_p=True)
+    b = moe.route(to_dev(i.x), to_dev(i.wg), 8, bias=to_dev(i.bias), want_p=True, n_group=8, topk_group=8)
+    torch.cuda.synchronize()
+    assert torch.equal(a["ids"], b["ids"])
+    assert torch.equal(a["w"], b["w"]) and torch.equal(a["p"], b["p"])
+
+
 # ------------------------------------------------------------------ align
 def _check_align(ids, E, C, bm):
     moe = _moe()
