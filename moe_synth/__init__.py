@@ -20,6 +20,9 @@ parallel and every chunk is reproducible on its own):
   ``clip(rint(N(0, 1) * 32), -127, 127)`` with per-output-channel fp32 scales
   ``0.02 / 32 * (0.75 + 0.5 * U(0, 1))``, i.e. weights of std ~0.02 already in
   their quantised storage form;
+* int4 expert weights (W4A16) are drawn the same way with
+  ``clip(rint(N(0, 1) * 2.5), -8, 7)`` codes (stored one per int8, unpacked)
+  and scales ``0.02 / 2.5 * (0.75 + 0.5 * U(0, 1))``;
 * the skewed workload adds per-expert logit offsets ``-s * ln(rank_e)`` with
   ``rank_e = perm(e) + 1`` for a seeded permutation ``perm`` of the experts and
   s = 1.1, which gives the softmax a Zipf(s) prior over experts.
@@ -35,6 +38,7 @@ import numpy as np
 TENSOR_X, TENSOR_WG, TENSOR_W13, TENSOR_W2, TENSOR_PERM, TENSOR_S13, TENSOR_S2 = range(7)
 
 INT8_WEIGHT_STD = 32.0
+INT4_WEIGHT_STD = 2.5
 X_ROW_CHUNK = 1024
 
 
@@ -50,7 +54,7 @@ class Spec:
     I: int
     x_dtype: str = "bf16"      # "f32" | "bf16"
     wg_dtype: str = "bf16"     # "f32" | "bf16"
-    w_dtype: str = "bf16"      # "f32" | "bf16" | "i8"
+    w_dtype: str = "bf16"      # "f32" | "bf16" | "i8" | "i4" (codes in int8 storage)
     out_dtype: str = "bf16"    # "f32" | "bf16"
     capacity_factor: float = 0.0   # <= 0: no capacity limit
     zipf_s: float = 0.0            # > 0: per-expert Zipf(s) logit offsets
@@ -104,15 +108,16 @@ def _normal_into(out: np.ndarray, dtype: str, rng: np.random.Generator, std: flo
         out[...] = v
 
 
-def _int8_into(q_out: np.ndarray, s_out: np.ndarray, rng_q, rng_s, std: float) -> None:
-    v = rng_q.standard_normal(q_out.shape, dtype=np.float32) * np.float32(INT8_WEIGHT_STD)
-    q_out[...] = np.clip(np.rint(v), -127, 127).astype(np.int8)
+def _int8_into(q_out: np.ndarray, s_out: np.ndarray, rng_q, rng_s, std: float, bits: int = 8) -> None:
+    qstd, lo, hi = (INT8_WEIGHT_STD, -127, 127) if bits == 8 else (INT4_WEIGHT_STD, -8, 7)
+    v = rng_q.standard_normal(q_out.shape, dtype=np.float32) * np.float32(qstd)
+    q_out[...] = np.clip(np.rint(v), lo, hi).astype(np.int8)
     u = rng_s.random(s_out.shape, dtype=np.float32)
-    s_out[...] = np.float32(std / INT8_WEIGHT_STD) * (np.float32(0.75) + np.float32(0.5) * u)
+    s_out[...] = np.float32(std / qstd) * (np.float32(0.75) + np.float32(0.5) * u)
 
 
 def _storage(dtype: str):
-    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8}[dtype]
+    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.int8}[dtype]
 
 
 @dataclass
@@ -126,8 +131,8 @@ class Inputs:
     bias: np.ndarray | None      # [E] fp32 or None
     w13: np.ndarray              # [E, 2I, H]: rows 0..I-1 are W1, rows I..2I-1 are W3
     w2: np.ndarray               # [E, H, I]
-    s13: np.ndarray | None = None    # [E, 2I] fp32 (int8 weights only)
-    s2: np.ndarray | None = None     # [E, H] fp32 (int8 weights only)
+    s13: np.ndarray | None = None    # [E, 2I] fp32 (int8 / int4 weights only)
+    s2: np.ndarray | None = None     # [E, H] fp32 (int8 / int4 weights only)
     extra: dict = field(default_factory=dict)
 
 
@@ -148,7 +153,7 @@ def make_inputs(spec: Spec, seed_base: int, threads: int | None = None,
     if with_experts:
         w13 = np.empty((E, 2 * I, H), dtype=_storage(spec.w_dtype))
         w2 = np.empty((E, H, I), dtype=_storage(spec.w_dtype))
-        if spec.w_dtype == "i8":
+        if spec.w_dtype in ("i8", "i4"):
             s13 = np.empty((E, 2 * I), dtype=np.float32)
             s2 = np.empty((E, H), dtype=np.float32)
 
@@ -157,9 +162,10 @@ def make_inputs(spec: Spec, seed_base: int, threads: int | None = None,
         _normal_into(out, dt, _rng(seed_base, tid, chunk), std)
 
     def run_expert(e):
-        if spec.w_dtype == "i8":
-            _int8_into(w13[e], s13[e], _rng(seed_base, TENSOR_W13, e), _rng(seed_base, TENSOR_S13, e), spec.w_std)
-            _int8_into(w2[e], s2[e], _rng(seed_base, TENSOR_W2, e), _rng(seed_base, TENSOR_S2, e), spec.w_std)
+        if spec.w_dtype in ("i8", "i4"):
+            b = 8 if spec.w_dtype == "i8" else 4
+            _int8_into(w13[e], s13[e], _rng(seed_base, TENSOR_W13, e), _rng(seed_base, TENSOR_S13, e), spec.w_std, b)
+            _int8_into(w2[e], s2[e], _rng(seed_base, TENSOR_W2, e), _rng(seed_base, TENSOR_S2, e), spec.w_std, b)
         else:
             _normal_into(w13[e], spec.w_dtype, _rng(seed_base, TENSOR_W13, e), spec.w_std)
             _normal_into(w2[e], spec.w_dtype, _rng(seed_base, TENSOR_W2, e), spec.w_std)

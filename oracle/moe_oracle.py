@@ -53,6 +53,12 @@ R9  group-limited routing ([LightOP] section 3.1, Moe Fuse Gate: groups are
     in route.  The probabilities are those of the plain router's softmax.
     parity of this reading against the page is unpinned: the page gives no
     formula; the pins below fix the oracle to the reading itself.
+R10 W4A16 ([LightOP] section 4.3, the quantisation matrix: INT4 weights with
+    16-bit activations): integer weight codes in [-8, 7] with one fp32 scale
+    per output channel (per row of W13 and of W2, as R7), so each expert
+    weight is code * scale; activations stay in their 16-bit storage type and
+    the FFN is the R6 SwiGLU on those weights.  How the codes are made from
+    real weights is offline and outside the hot path.
 """
 from __future__ import annotations
 
@@ -65,7 +71,7 @@ __all__ = [
     "to_f64", "gate_logits", "softmax_rows", "topk_rows", "renormalise", "route",
     "quant_per_token_int8", "capacity", "align", "tiles", "silu", "swiglu_ffn",
     "layer", "layer_from_inputs", "layer_token_major", "combine", "combine_shared",
-    "group_scores", "route_grouped",
+    "group_scores", "route_grouped", "dequant_rows",
 ]
 
 
@@ -308,6 +314,12 @@ def _w8a8_ffn(xq: np.ndarray, xs: np.ndarray, w13q: np.ndarray, s13: np.ndarray,
     return acc2 * hs.astype(np.float64)[:, None] * s2.astype(np.float64)[None, :]
 
 
+def dequant_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Weight of integer codes with one scale per output row (R7, R10):
+    W[n, k] = q[n, k] * s[n]."""
+    return np.asarray(q).astype(np.float64) * np.asarray(s, dtype=np.float64)[:, None]
+
+
 def combine(y_rows: np.ndarray, pos: np.ndarray, w: np.ndarray) -> np.ndarray:
     """out[t] = sum over kept slots j of w[t,j] * Y[pos[t,j]] (R3).
 
@@ -377,6 +389,9 @@ def layer(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capacity_factor,
         tokens_e = tok[np.nonzero(sel)[0]]
         if w_dtype == "i8":
             y_rows[rows] = _w8a8_ffn(xq[tokens_e], xs[tokens_e], w13[e], s13[e], w2[e], s2[e], I)
+        elif w_dtype == "i4":
+            w13e = dequant_rows(w13[e], s13[e])
+            y_rows[rows] = swiglu_ffn(x64[tokens_e], w13e[:I], w13e[I:], dequant_rows(w2[e], s2[e]))
         else:
             w13e = to_f64(w13[e], w_dtype)
             y_rows[rows] = swiglu_ffn(x64[tokens_e], w13e[:I], w13e[I:], to_f64(w2[e], w_dtype))
@@ -414,6 +429,12 @@ def layer_token_major(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capac
                 continue
             if w_dtype == "i8":
                 y = _w8a8_ffn(xq[t:t + 1], xs[t:t + 1], w13[e], s13[e], w2[e], s2[e], I)[0]
+            elif w_dtype == "i4":
+                # element by element in Python floats (binary64)
+                w1 = np.array([[float(q) * float(s13[e][n]) for q in w13[e][n]] for n in range(I)])
+                w3 = np.array([[float(q) * float(s13[e][I + n]) for q in w13[e][I + n]] for n in range(I)])
+                w2e = np.array([[float(q) * float(s2[e][n]) for q in w2[e][n]] for n in range(H)])
+                y = swiglu_ffn(x64[t:t + 1], w1, w3, w2e)[0]
             else:
                 w13e = to_f64(w13[e], w_dtype)
                 y = swiglu_ffn(x64[t:t + 1], w13e[:I], w13e[I:], to_f64(w2[e], w_dtype))[0]

@@ -276,7 +276,8 @@ def test_k_equals_e_is_dense_soft_mixture():
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-14)
 
 
-@pytest.mark.parametrize("w_dtype,cap", [("f32", 0.0), ("f32", 0.6), ("i8", 0.0), ("i8", 0.7), ("bf16", 1.0)])
+@pytest.mark.parametrize("w_dtype,cap", [("f32", 0.0), ("f32", 0.6), ("i8", 0.0), ("i8", 0.7), ("bf16", 1.0),
+                                         ("i4", 0.0), ("i4", 0.6)])
 def test_expert_major_equals_token_major(w_dtype, cap):
     inp = _small_inputs(48, 32, 8, 3, 16, w_dtype=w_dtype, cap=cap,
                         x_dtype="bf16" if w_dtype != "f32" else "f32")
@@ -473,3 +474,61 @@ def test_route_grouped_ties_and_invariants():
         oracle.route_grouped(x, wg, k, 7, 3)          # E not a multiple of n_group
     with pytest.raises(ValueError):
         oracle.route_grouped(x, wg, 9, 8, 1)          # k beyond one group's 8 experts
+
+
+# ------------------------------------------------------------------- W4A16
+def test_w4a16_hand_worked():
+    """One token, H=2, I=1.  x = (1, 2); W1 codes (1, -1) at scale 1/2 give
+    g = -1/2; W3 codes (2, 1) at scale 1/4 give u = 1; W2 codes (3, -8) at
+    scales (1, 1/2) give y = (3, -4) * silu(-1/2)."""
+    spec = moe_synth.Spec("w4", 1, 2, 1, 1, 1, x_dtype="f32", wg_dtype="f32", w_dtype="i4", out_dtype="f32")
+    x = np.array([[1.0, 2.0]], dtype=np.float32)
+    wg = np.zeros((1, 2), dtype=np.float32)
+    w13 = np.array([[[1, -1], [2, 1]]], dtype=np.int8)
+    s13 = np.array([[0.5, 0.25]], dtype=np.float32)
+    w2 = np.array([[[3], [-8]]], dtype=np.int8)
+    s2 = np.array([[1.0, 0.5]], dtype=np.float32)
+    res = oracle.layer(x, "f32", wg, "f32", None, w13, w2, "i4", 1, 0.0, s13, s2)
+    h = -0.5 / (1.0 + math.exp(0.5))
+    np.testing.assert_allclose(res["out"][0], [3.0 * h, -4.0 * h], rtol=1e-15)
+    assert spec.w_dtype == "i4"
+
+
+def test_w4a16_scales_are_per_output_row():
+    """Unit scales give the layer of float weights equal to the codes; a
+    scale on W2 rows or on W3 rows scales those outputs linearly, a scale on
+    W1 rows does not (it passes through silu); a transposed scale (per input
+    column) would break the first check of each pair."""
+    inp = _small_inputs(24, 32, 4, 2, 16, w_dtype="i4", x_dtype="bf16")
+    I = 16
+    ones13 = np.ones_like(inp.s13)
+    ones2 = np.ones_like(inp.s2)
+    base = _layer(inp, s13=ones13, s2=ones2)
+    out1 = oracle.layer(**base)["out"]
+    as_f32 = dict(base, w13=inp.w13.astype(np.float32), w2=inp.w2.astype(np.float32), w_dtype="f32")
+    np.testing.assert_allclose(out1, oracle.layer(**as_f32)["out"], rtol=1e-13, atol=1e-13)
+    # W2 row h scaled by 3: output column h scaled by 3, others unchanged
+    s2 = ones2.copy()
+    s2[:, 5] = 3.0
+    out2 = oracle.layer(**dict(base, s2=s2))["out"]
+    np.testing.assert_allclose(out2[:, 5], 3.0 * out1[:, 5], rtol=1e-12)
+    np.testing.assert_array_equal(np.delete(out2, 5, axis=1), np.delete(out1, 5, axis=1))
+    # every W3 row scaled by 2: the whole output doubles
+    s13 = ones13.copy()
+    s13[:, I:] = 2.0
+    np.testing.assert_allclose(oracle.layer(**dict(base, s13=s13))["out"], 2.0 * out1, rtol=1e-12, atol=1e-14)
+    # every W1 row scaled by 2: not linear
+    s13 = ones13.copy()
+    s13[:, :I] = 2.0
+    assert not np.allclose(oracle.layer(**dict(base, s13=s13))["out"], 2.0 * out1, rtol=1e-3)
+    # dequant_rows is codes times the row's scale
+    q = np.array([[-8, 7], [1, -1]], dtype=np.int8)
+    np.testing.assert_array_equal(oracle.dequant_rows(q, np.array([0.5, 4.0])), [[-4.0, 3.5], [4.0, -4.0]])
+
+
+def test_int4_codes_in_range():
+    inp = moe_synth.make_inputs(moe_synth.Spec("w4", 8, 128, 4, 2, 64, w_dtype="i4"), 3)
+    for q in (inp.w13, inp.w2):
+        assert q.dtype == np.int8 and q.min() >= -8 and q.max() <= 7
+        assert q.min() == -8 and q.max() == 7      # both ends occur
+    assert inp.s13.shape == (4, 128) and inp.s2.shape == (4, 128)
