@@ -53,7 +53,8 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_I8 = 2
+  MOE_I8 = 2,
+  MOE_I4 = 3   /* int4 codes packed two per byte (see moe_pack_int4); weights only */
 } moe_dtype;
 
 /* Limits shared by all entry points: 1 <= E <= 256, 1 <= k <= min(E, 8),
@@ -160,16 +161,30 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  *     int32 accumulation, dequantised by xs[t] * s13[e][n]; h is quantised
  *     per row with the per-token rule before the second GEMM, whose int32
  *     result is scaled by that row scale * s2[e][n]  ([LightOP] section 4.1)
+ *   act_dtype MOE_BF16 with w_dtype MOE_I4 (W4A16, [LightOP] section 4.3):
+ *     a_t = x[t]; each weight is its int4 code (in [-8, 7]) times the
+ *     per-output-channel scale s13[e][n] or s2[e][n]; bf16 MFMA with fp32
+ *     accumulation, the channel scale applied to the sum (before SwiGLU in
+ *     the up GEMM); h is bf16 as in W16A16
  *   x        [T, H] act_dtype;  xs [T] fp32 (MOE_I8 only, else NULL)
  *   w13      [E, 2I, H] w_dtype: rows 0..I-1 are W1[e], rows I..2I-1 W3[e]
- *   w2       [E, H, I] w_dtype
- *   s13, s2  [E, 2I], [E, H] fp32 per-output-channel scales (MOE_I8 only)
+ *            (MOE_I4: [E, 2I, H/2] bytes as written by moe_pack_int4)
+ *   w2       [E, H, I] w_dtype (MOE_I4: [E, H, I/2] packed bytes)
+ *   s13, s2  [E, 2I], [E, H] fp32 per-output-channel scales (MOE_I8 and
+ *            MOE_I4 only)
  *   sorted_slot, tiles, num_tiles: from moe_align with the same block_m;
  *   block_m must equal moe_ffn_block_m() for this shape
  *   y_sorted [T*k, H] y_dtype out (MOE_F32 for f32 activations, else
  *            MOE_BF16): rows >= N are not written
  */
 int32_t moe_ffn_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype);
+
+/* Offline weight preparation for W4A16: packs int4 codes, given one per int8
+ * ([rows, K], each in [-8, 7]; other values are stored modulo 16), two per
+ * byte along K: packed byte j of a row holds code 2j in its low nibble and
+ * code 2j+1 in its high nibble (two's complement nibbles).  [rows, K/2]
+ * bytes out.  K % 64 == 0; both pointers 16-byte aligned; device memory. */
+moe_status moe_pack_int4(const int8_t* codes, int64_t rows, int32_t K, uint8_t* packed, void* stream);
 size_t moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                               int32_t w_dtype);
 moe_status moe_expert_ffn(const void* x, int32_t act_dtype, const float* xs, const void* w13,
@@ -233,7 +248,8 @@ moe_status moe_combine_shared(const void* y_sorted, int32_t y_dtype, const int32
  *   x [T, H] (MOE_F32 or MOE_BF16), wg [E, H], bias [E] or NULL,
  *   w13/w2/s13/s2 as in moe_expert_ffn, capacity as in moe_align
  *   (<= 0: none), out [T, H] with out_dtype == x_dtype.
- *   w_dtype MOE_I8 quantises x per token inside the route step (W8A8).
+ *   w_dtype MOE_I8 quantises x per token inside the route step (W8A8);
+ *   w_dtype MOE_I4 (packed int4 weights, with s13/s2) needs bf16 x (W4A16).
  * aux (host struct, may be NULL; each member may be NULL) names device
  * buffers the layer writes its intermediates to instead of the workspace:
  * topk_ids/topk_w/topk_p [T,k], counts [E], offsets [E+1], sorted_slot and

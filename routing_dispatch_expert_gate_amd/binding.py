@@ -16,8 +16,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_I8 = 0, 1, 2
-_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8}
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
+# torch.uint8 expert weights are int4 codes packed by pack_int4 (W4A16)
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8, torch.uint8: MOE_I4}
 
 _vp, _i32, _i64, _sz, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
 _st = ctypes.c_int
@@ -42,6 +43,7 @@ SIGNATURES = {
                          _i32, _vp, _sz, _vp]),
     "moe_ffn_down": (_st, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                            _i32, _vp, _sz, _vp]),
+    "moe_pack_int4": (_st, [_vp, _i64, _i32, _vp, _vp]),
     "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "moe_combine_shared": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, ctypes.c_float, _vp, _vp,
                                  _i32, _vp]),
@@ -172,6 +174,23 @@ def align(ids: torch.Tensor, E: int, capacity: int = 0, block_m: int = 128) -> d
     return out
 
 
+def _inner(w: torch.Tensor) -> int:
+    """K extent of a weight tensor's rows (packed int4 holds two per byte)."""
+    return w.shape[-1] * (2 if w.dtype == torch.uint8 else 1)
+
+
+def pack_int4(codes: torch.Tensor) -> torch.Tensor:
+    """moe_pack_int4: int8 codes [..., K] in [-8, 7] -> packed uint8 [..., K/2]."""
+    _dev(codes, "codes")
+    if codes.dtype != torch.int8:
+        raise ValueError("codes must be int8")
+    K = codes.shape[-1]
+    rows = codes.numel() // K if K else 0
+    out = torch.empty(codes.shape[:-1] + (K // 2,), dtype=torch.uint8, device=codes.device)
+    _check(lib.moe_pack_int4(_p(codes), rows, K, _p(out), _stream(codes.device)))
+    return out
+
+
 def ffn_block_m(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype) -> int:
     return int(lib.moe_ffn_block_m(T, H, I, E, k, _DT[w_dtype]))
 
@@ -184,7 +203,7 @@ def expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, sorted_slot
     for t, nme in ((x, "x"), (w13, "w13"), (w2, "w2"), (sorted_slot, "sorted_slot"), (tiles, "tiles")):
         _dev(t, nme)
     T, H = x.shape
-    E, I = w2.shape[0], w2.shape[2]
+    E, I = w2.shape[0], _inner(w2)
     dev = x.device
     ydt = torch.float32 if w13.dtype == torch.float32 else torch.bfloat16
     y = torch.empty((T * k, H), dtype=ydt, device=dev)
@@ -212,7 +231,7 @@ def ffn_up(x, w13, sorted_slot, tiles, num_tiles, block_m, k, E, I, ws, xs=None,
 
 def ffn_down(w2, sorted_slot, tiles, num_tiles, block_m, k, T, ws, y, topk_w=None, s2=None):
     """moe_ffn_down from the workspace filled by ffn_up into ``y`` [T*k, H]."""
-    E, H, I = w2.shape
+    E, H, I = w2.shape[0], w2.shape[1], _inner(w2)
     _check(lib.moe_ffn_down(_p(w2), _DT[w2.dtype], _p(s2), _p(sorted_slot), _p(tiles), _p(num_tiles),
                             block_m, _p(topk_w), T, H, I, E, k, _p(y), _DT[y.dtype], _p(ws[0]), ws[1],
                             _stream(y.device)))
@@ -281,6 +300,6 @@ def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None)
     """One moe_layer call (allocates its workspace); ``aux`` maps moe_layer_aux
     member names to device tensors that receive the intermediates."""
     T, H = x.shape
-    E, I = w2.shape[0], w2.shape[2]
+    E, I = w2.shape[0], _inner(w2)
     return Layer(T, H, I, E, k, x.dtype, w13.dtype, x.device)(x, wg, w13, w2, capacity, bias, s13, s2,
                                                              aux=aux)

@@ -34,6 +34,13 @@
 //    writes h in fp32 and folds each row's max |h| in with an integer atomic
 //    max (non-negative floats order like their bit patterns); a row pass then
 //    quantises h with the per-token rule, and the down GEMM runs int8 MFMA.
+//  * W4A16 (LightOP page, section 4.3, INT4 weights with 16-bit
+//    activations): weights are int4 codes, two per byte along K (low nibble
+//    first), with one fp32 scale per output channel.  B tiles are copied to
+//    LDS packed (a quarter of the bf16 bytes), each lane reads its fragment's
+//    eight codes as one 32-bit word and widens them exactly to bf16 in
+//    registers, and the MFMAs are the bf16 ones; the epilogue applies the
+//    channel scales (before SwiGLU in the up GEMM).
 #include <math.h>
 #include <stdio.h>
 
@@ -45,6 +52,7 @@ namespace {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kI8 = 2;
+constexpr int kI4 = 3;
 
 
 template <bool I8>
@@ -69,6 +77,22 @@ struct Mma<true> {
 // MFMA 32x32 accumulator element v of lane l sits at row 8*(v/4) + 4*(l/32) + v%4,
 // column l%32 of the fragment.
 __device__ __forceinline__ int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Eight int4 codes (two per byte, low nibble first, two's complement) to
+// eight bf16 values in K order: each code is sign-extended, converted to fp32
+// and narrowed, all exactly (|code| <= 8).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 widen_i4(uint32_t w) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = (float)((int32_t)(w << (28 - 8 * j)) >> 28);
+    const float hi = (float)((int32_t)(w << (24 - 8 * j)) >> 28);
+    const bf16x2 p = {(__bf16)lo, (__bf16)hi};
+    r[j] = __builtin_bit_cast(uint32_t, p);
+  }
+  return r;
+}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup P runs on
 // XCD P % 8).  Renumber them so that consecutive logical ids run on the same
@@ -106,6 +130,7 @@ struct GemmArgs {
   const float* topk_w;         // down: route weight per slot (NULL: 1)
   void* out;                   // up: h [rows, I] (bf16; fp32 for W8A8); down: y [rows, H] bf16
   uint32_t* rowmax;            // up, W8A8: max |h| of each row (bit pattern of a non-negative float)
+                               // (W4A16: wscale as for W8A8, w packed two codes per byte)
   void* partial;               // down, last-round split: raw partial tiles [conc][BM * BN]
   int H, I, k;
   int n_blocks, max_tiles;
@@ -165,11 +190,13 @@ __device__ __forceinline__ int2 raster(int L0, int nt, int n_blocks) {
 // K loop is specialised on their number), and rows past the valid ones copy
 // the tile's first row: their accumulators are never stored (an MFMA output
 // row depends only on its A row).
-template <bool I8, bool UP, int BM, int BN, int WM, int WN, int S, int ROWB, int GN>
+template <bool I8, bool UP, int BM, int BN, int WM, int WN, int S, int ROWB, int GN, bool W4 = false>
 __global__ __launch_bounds__(WM* WN * 64)
 __attribute__((amdgpu_waves_per_eu(
-    (BM / WM) * (BN / WN) <= 128 * 64 && 2 * S * (BM + BN) * ROWB <= 160 * 1024 ? 2 : 1)))
+    (BM / WM) * (BN / WN) <= 128 * 64 && 2 * S * (BM * ROWB + BN * (W4 ? ROWB / 4 : ROWB)) <= 160 * 1024 ? 2
+                                                                                                        : 1)))
 void gg_kernel(const GemmArgs a) {
+  static_assert(!(I8 && W4), "W4A16 takes bf16 activations");
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int WROWS = BM / WM, FM = WROWS / 32;
   constexpr int WCOLS = BN / WN, NF = WCOLS / 32;
@@ -177,11 +204,21 @@ void gg_kernel(const GemmArgs a) {
   constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
   constexpr int RPB = 1024 / ROWB;                   // rows per 1 KiB copy block
   constexpr int SUB = ROWB / 32;                     // MFMA k-substeps per stage
-  constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int NBLK = (BM + BN) / RPB;              // 1 KiB copy blocks per stage
+  constexpr int BROWB = W4 ? ROWB / 4 : ROWB;       // B bytes per row per stage
+  constexpr int STAGE = BM * ROWB + BN * BROWB;
   constexpr int EB = I8 ? 1 : 2;
-  constexpr int L = NBLK / NW;                       // copies per wave per stage
-  static_assert(L * NW == NBLK && S >= 2, "copies must split evenly over the waves");
+  // 1 KiB copy blocks per stage.  bf16/int8: A and B blocks are split evenly,
+  // L per wave.  W4A16: each wave copies LA A blocks, and B block w + NW*j
+  // for every j that exists (LB or LB + 1 of them), so each wave's count is
+  // a constant of its index and its waits stay exact.
+  constexpr int ABLK = BM * ROWB / 1024, BBLK = BN * BROWB / 1024;
+  constexpr int NBLK = ABLK + BBLK;
+  constexpr int L = W4 ? 1 : NBLK / NW;
+  constexpr int LA = ABLK / NW, LB = BBLK / NW, LBR = BBLK % NW;
+  static_assert(W4 ? (LA * NW == ABLK && BBLK >= 1 && BBLK * 1024 == BN * BROWB)
+                   : (L * NW == NBLK),
+                "copies must split evenly over the waves");
+  static_assert(S >= 2, "at least two stages");
   static_assert(FM >= 1 && NF >= 1, "wave tile too small");
   static_assert(!UP || (NF % 2 == 0), "up needs paired G/U fragments");
   static_assert(S * STAGE <= 160 * 1024, "LDS stages");
@@ -205,6 +242,7 @@ void gg_kernel(const GemmArgs a) {
   const int nt = __builtin_amdgcn_readfirstlane(*a.num_tiles);
   const int nwork = nt * a.n_blocks;
   const int64_t kbytes = (int64_t)(UP ? a.H : a.I) * EB;
+  const int64_t kbytes_b = W4 ? kbytes / 4 : kbytes;   // a packed int4 weight row
   const int nk_all = (int)(kbytes / ROWB);
   TailPlan tp{nwork, 1};
   if constexpr (!UP) tp = tail_plan(nwork, a.conc, nk_all);
@@ -240,42 +278,96 @@ void gg_kernel(const GemmArgs a) {
   // the rest B rows.  Lane i copies row RPB*blk + i/CPR into LDS chunk
   // i%CPR, which holds logical chunk (i%CPR) ^ sw(row).
   const uint8_t* abase = (UP ? a.act : a.act + (int64_t)r0 * kbytes) + (int64_t)kb * ROWB;
-  const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes + (int64_t)kb * ROWB;
+  const uint8_t* bbase = a.w + (int64_t)e * (UP ? 2 * a.I : a.H) * kbytes_b + (int64_t)kb * BROWB;
   // A wave whose copy blocks hold only A rows past the tile's valid rows
   // issues no copies at all (those rows are never stored); any other wave
-  // issues all L per stage, so its vmcnt waits stay exact.
+  // issues all of its copies per stage, so its vmcnt waits stay exact.
   bool copies = false;
+  // W4A16: this wave's B blocks (wv, wv + NW, ...)
+  const int nbw = W4 ? LB + (wv < LBR ? 1 : 0) : 0;
+  if constexpr (W4) {
+    copies = nbw > 0;
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const int q = wv * L + j;
-    copies |= q >= BM / RPB || q * RPB < rows;
-  }
-  uint32_t goff[L];
+    for (int j = 0; j < LA; ++j) copies |= (wv * LA + j) * RPB < rows;
+  } else {
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const int q = wv * L + j;
-    const bool is_a = q < BM / RPB;                  // uniform
-    const int trow = (is_a ? q : q - BM / RPB) * RPB + lane / CPR;
-    const int c = (lane % CPR) ^ swr<ROWB>(trow);
-    uint32_t row;
-    if (is_a) {
-      const int r = trow < rows ? trow : 0;
-      row = UP ? (uint32_t)(a.sorted_slot[r0 + r] / a.k) : (uint32_t)r;
-    } else if (UP) {
-      row = (uint32_t)(trow < HB ? nb * HB + trow : a.I + nb * HB + (trow - HB));
-    } else {
-      row = (uint32_t)(nb * BN + trow);
+    for (int j = 0; j < L; ++j) {
+      const int q = wv * L + j;
+      copies |= q >= BM / RPB || q * RPB < rows;
     }
-    goff[j] = row * (uint32_t)kbytes + c * 16;
+  }
+  auto a_off = [&](int trow) -> uint32_t {
+    const int c = (lane % CPR) ^ swr<ROWB>(trow);
+    const int r = trow < rows ? trow : 0;
+    const uint32_t row = UP ? (uint32_t)(a.sorted_slot[r0 + r] / a.k) : (uint32_t)r;
+    return row * (uint32_t)kbytes + c * 16;
+  };
+  auto b_row = [&](int trow) -> uint32_t {
+    if (UP) return (uint32_t)(trow < HB ? nb * HB + trow : a.I + nb * HB + (trow - HB));
+    return (uint32_t)(nb * BN + trow);
+  };
+  constexpr int NG = W4 ? LA + LB + (LBR > 0 ? 1 : 0) : L;
+  uint32_t goff[NG];
+  if constexpr (W4) {
+    // packed B rows are not swizzled: BROWB bytes, lane i copies row
+    // i / (BROWB/16), chunk i % (BROWB/16) of its 1 KiB block
+    constexpr int CPRB = BROWB / 16, RPBB = 1024 / BROWB;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) goff[j] = a_off((wv * LA + j) * RPB + lane / CPR);
+#pragma unroll
+    for (int j = 0; j < NG - LA; ++j) {
+      const int qb = wv + NW * j;                      // B block (may not exist)
+      const int trow = (qb < BBLK ? qb : 0) * RPBB + lane / CPRB;
+      goff[LA + j] = b_row(trow) * (uint32_t)kbytes_b + (lane % CPRB) * 16;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int q = wv * L + j;
+      const bool is_a = q < BM / RPB;                  // uniform
+      const int trow = (is_a ? q : q - BM / RPB) * RPB + lane / CPR;
+      if (is_a) {
+        goff[j] = a_off(trow);
+      } else {
+        const int c = (lane % CPR) ^ swr<ROWB>(trow);
+        goff[j] = b_row(trow) * (uint32_t)kbytes + c * 16;
+      }
+    }
   }
   auto issue = [&](int kt) {
     if (!copies) return;
     uint8_t* st = smem + (kt % S) * STAGE;
+    if constexpr (W4) {
 #pragma unroll
-    for (int j = 0; j < L; ++j) {
-      const int q = wv * L + j;
-      const uint8_t* src = (q < BM / RPB ? abase : bbase) + (size_t)kt * ROWB + goff[j];
-      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(st + q * 1024), 16, 0, 0);
+      for (int j = 0; j < LA; ++j)
+        __builtin_amdgcn_global_load_lds((glb_void*)(abase + (size_t)kt * ROWB + goff[j]),
+                                         (lds_void*)(st + (wv * LA + j) * 1024), 16, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NG - LA; ++j)
+        if (j < nbw)
+          __builtin_amdgcn_global_load_lds((glb_void*)(bbase + (size_t)kt * BROWB + goff[LA + j]),
+                                           (lds_void*)(st + BM * ROWB + (wv + NW * j) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < L; ++j) {
+        const int q = wv * L + j;
+        const uint8_t* src = (q < BM / RPB ? abase : bbase) + (size_t)kt * ROWB + goff[j];
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(st + q * 1024), 16, 0, 0);
+      }
+    }
+  };
+  // exact wait for stage kt with `after` later stages in flight
+  auto wait_stage = [&](int after) {
+    if constexpr (W4) {
+      if constexpr (LBR > 0) {
+        if (nbw > LB) {
+          wait_vm_stages<LA + LB + 1, S - 2>(after);
+          return;
+        }
+      }
+      wait_vm_stages<LA + LB, S - 2>(after);
+    } else {
+      wait_vm_stages<L, S - 2>(after);
     }
   };
 
@@ -322,12 +414,35 @@ void gg_kernel(const GemmArgs a) {
     for (int kt = 0; kt < nk; ++kt) {
       // stages issued after kt: min(S-2, nk-1-kt)
       const int after = nk - 1 - kt < S - 2 ? nk - 1 - kt : S - 2;
-      wait_vm_stages<L, S - 2>(after);
+      wait_stage(after);
       lds_barrier();
       if (kt + S - 1 < nk) issue(kt + S - 1);
       const uint8_t* As = smem + (kt % S) * STAGE;
       const uint8_t* Bs = As + BM * ROWB;
-      if constexpr (V > 0) {
+      if constexpr (V > 0 && W4) {
+        // packed B: lane's eight codes of row (lane % 32), k-chunk
+        // 2s + lane / 32, one 32-bit LDS read, widened in registers
+        u32x4 af[SUB][V];
+        uint32_t bw[SUB][NF];
+#pragma unroll
+        for (int s = 0; s < SUB; ++s) {
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf)
+            bw[s][nf] = *reinterpret_cast<const uint32_t*>(Bs + (brow_of(nf) + (lane & 31)) * BROWB +
+                                                           4 * (2 * s + (lane >> 5)));
+#pragma unroll
+          for (int fm = 0; fm < V; ++fm)
+            af[s][fm] = *reinterpret_cast<const u32x4*>(As + lo[s] + (wm * WROWS + fm * 32) * ROWB);
+        }
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
+#pragma unroll
+          for (int nf = 0; nf < NF; ++nf) {
+            const u32x4 b = widen_i4(bw[s][nf]);
+#pragma unroll
+            for (int fm = 0; fm < V; ++fm) acc[fm][nf] = Mma<false>::run(af[s][fm], b, acc[fm][nf]);
+          }
+      } else if constexpr (V > 0) {
         u32x4 af[SUB][V], bfr[SUB][NF];
         // read order A0, B0..B(NF-1), A1..A(V-1): the first MFMA (A0 x B0)
         // waits for two reads only
@@ -405,6 +520,13 @@ void gg_kernel(const GemmArgs a) {
 
   if constexpr (UP && !I8) {
     uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
+    float sg[NF / 2], su[NF / 2];
+#pragma unroll
+    for (int f = 0; f < NF / 2; ++f) {
+      const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+      sg[f] = W4 ? a.wscale[(int64_t)e * 2 * a.I + col] : 1.f;
+      su[f] = W4 ? a.wscale[(int64_t)e * 2 * a.I + a.I + col] : 1.f;
+    }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
@@ -415,7 +537,11 @@ void gg_kernel(const GemmArgs a) {
 #pragma unroll
         for (int f = 0; f < NF / 2; ++f) {
           const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
-          const float gv = (float)acc[fm][f][v], uv = (float)acc[fm][NF / 2 + f][v];
+          float gv = (float)acc[fm][f][v], uv = (float)acc[fm][NF / 2 + f][v];
+          if constexpr (W4) {
+            gv *= sg[f];
+            uv *= su[f];
+          }
           h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)f32_to_bf16_bits(silu_f32(gv) * uv);
         }
       }
@@ -457,7 +583,7 @@ void gg_kernel(const GemmArgs a) {
     float sc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
-      sc[f] = I8 ? a.wscale[(int64_t)e * a.H + nb * BN + wn * WCOLS + f * 32 + (lane & 31)] : 1.f;
+      sc[f] = (I8 || W4) ? a.wscale[(int64_t)e * a.H + nb * BN + wn * WCOLS + f * 32 + (lane & 31)] : 1.f;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
@@ -648,7 +774,7 @@ FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int down_var) {
     b.hs = (float*)(wsb + off);
     off += align256((size_t)n * 4);
   }
-  if (w_dtype != kF32 && down_var == 0) b.partial = wsb + off;
+  if ((w_dtype == kBF16 || w_dtype == kI8) && down_var == 0) b.partial = wsb + off;
   return b;
 }
 
@@ -686,6 +812,16 @@ constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4,
                                 {256, 64, 2, 2, 3, 128, 8},   {256, 64, 2, 2, 3, 128, 8},
                                 {64, 64, 1, 2, 6, 64, 8}};
 
+// W4A16 tiles: packed B stages are a quarter of the bf16 ones, so the
+// prefill/mid tile keeps 256 x 256 with 8 waves of 128 x 64 (each B fragment
+// is widened by two waves, not four) and three 40 KiB stages; decode keeps
+// 64 x BN with eight 8 KiB stages in flight for weight streaming.
+constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 3, 128, 4}, {64, 256, 1, 4, 8, 64, 8},
+                                {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 8, 64, 8}};
+constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {64, 256, 1, 4, 8, 64, 8},
+                                  {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 8, 64, 8},
+                                  {256, 64, 2, 2, 3, 128, 8},  {64, 64, 1, 2, 8, 64, 8}};
+
 #define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R, G) \
   case IDX:                                       \
     gg_kernel<I8, UP, BM, BN, WM, WN, S, R, G><<<grid, WM * WN * 64, 0, s>>>(a); \
@@ -721,6 +857,78 @@ hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 #undef MOE_GG_CASE
+
+#define MOE_GG4_CASE(IDX, BM, BN, WM, WN, S, R, G) \
+  case IDX:                                        \
+    gg_kernel<false, UP, BM, BN, WM, WN, S, R, G, true><<<grid, WM * WN * 64, 0, s>>>(a); \
+    break;
+
+template <bool UP>
+hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
+  if constexpr (UP) {
+    switch (var) {
+      MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 4)
+      MOE_GG4_CASE(1, 64, 256, 1, 4, 8, 64, 8)
+      MOE_GG4_CASE(2, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(3, 64, 128, 1, 2, 8, 64, 8)
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    switch (var) {
+      MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 2)
+      MOE_GG4_CASE(1, 64, 256, 1, 4, 8, 64, 8)
+      MOE_GG4_CASE(2, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(3, 64, 128, 1, 2, 8, 64, 8)
+      MOE_GG4_CASE(4, 256, 64, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(5, 64, 64, 1, 2, 8, 64, 8)
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
+}
+#undef MOE_GG4_CASE
+
+hipError_t launch_up_w4(const FfnPlan& p, const void* x, const void* w13, const float* s13,
+                        const int32_t* sorted_slot, const int32_t* tiles, const int32_t* num_tiles,
+                        int H, int I, int k, const FfnBufs& b, hipStream_t s) {
+  GemmArgs a{};
+  a.act = (const uint8_t*)x;
+  a.w = (const uint8_t*)w13;
+  a.sorted_slot = sorted_slot;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.wscale = s13;
+  a.out = b.h;
+  a.H = H;
+  a.I = I;
+  a.k = k;
+  a.n_blocks = I / (kUpVarW4[p.up_var].bn / 2);
+  a.max_tiles = (int)p.max_tiles;
+  return launch_gg_w4<true>(p.up_var, a, s);
+}
+
+hipError_t launch_down_w4(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
+                          const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int H,
+                          int I, void* y, const FfnBufs& b, hipStream_t s) {
+  GemmArgs a{};
+  a.act = (const uint8_t*)b.h;
+  a.w = (const uint8_t*)w2;
+  a.sorted_slot = sorted_slot;
+  a.tiles = tiles;
+  a.num_tiles = num_tiles;
+  a.wscale = s2;
+  a.topk_w = topk_w;
+  a.out = y;
+  a.H = H;
+  a.I = I;
+  a.k = 1;
+  a.n_blocks = H / kDownVarW4[p.down_var].bn;
+  a.max_tiles = (int)p.max_tiles;
+  return launch_gg_w4<false>(p.down_var, a, s);
+}
 
 template <bool I8>
 hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const void* w13,
@@ -780,6 +988,32 @@ hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const 
 
 }  // namespace
 
+namespace {
+// int4 packing (offline weight preparation for W4A16): 16 codes per thread,
+// byte j of the output holds code 2j in its low nibble and code 2j+1 in its
+// high nibble.
+__global__ __launch_bounds__(256) void pack_i4_kernel(const int8_t* __restrict__ codes, int64_t n16,
+                                                      uint8_t* __restrict__ packed) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n16) return;
+  const uint4 c = reinterpret_cast<const uint4*>(codes)[i];
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[2] = {0u, 0u};
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const uint32_t nib = (w[b >> 2] >> (8 * (b & 3))) & 0xFu;
+    o[b >> 3] |= nib << (4 * (b & 7));
+  }
+  reinterpret_cast<uint2*>(packed)[i] = make_uint2(o[0], o[1]);
+}
+}  // namespace
+
+hipError_t launch_pack_i4(const int8_t* codes, int64_t n, uint8_t* packed, hipStream_t s) {
+  const int64_t n16 = n / 16;
+  pack_i4_kernel<<<(unsigned)((n16 + 255) / 256), 256, 0, s>>>(codes, n16, packed);
+  return hipGetLastError();
+}
+
 FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
   FfnPlan p{};
   const int64_t n = T * k;
@@ -788,6 +1022,17 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     p.ws_bytes = align256((size_t)n * I * 4);
     snprintf(p.up_name, sizeof p.up_name, "ffn_f32_kernel<up>");
     snprintf(p.down_name, sizeof p.down_name, "ffn_f32_kernel<down>");
+  } else if (w_dtype == kI4) {
+    const bool decode = (double)n / E <= 24.0;
+    p.up_var = (I % 128 == 0 ? 0 : 2) + (decode ? 1 : 0);
+    p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 2 : 4)) + (decode ? 1 : 0);
+    p.block_m = decode ? 64 : 256;
+    const Variant u = kUpVarW4[p.up_var], d = kDownVarW4[p.down_var];
+    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<w4a16,up,%dx%d,%dx%d,S%d,R%d,G%d>", u.bm, u.bn, u.wm,
+             u.wn, u.stages, u.rowb, u.gn);
+    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<w4a16,down,%dx%d,%dx%d,S%d,R%d,G%d>", d.bm, d.bn,
+             d.wm, d.wn, d.stages, d.rowb, d.gn);
+    p.ws_bytes = align256((size_t)n * I * 2);
   } else {
     // shape class from the mean rows per expert: decode-sized (weight
     // streaming, short tiles), mid (one 256-row tile per expert, waves split
@@ -828,6 +1073,7 @@ hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const
                                                         (float*)b.h);
     return hipGetLastError();
   }
+  if (w_dtype == kI4) return launch_up_w4(p, x, w13, s13, sorted_slot, tiles, num_tiles, H, I, k, b, s);
   if (w_dtype == kBF16)
     return launch_up<false>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
   return launch_up<true>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
@@ -845,6 +1091,8 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
                                                          k, H / 32, (float*)y);
     return hipGetLastError();
   }
+  if (w_dtype == kI4)
+    return launch_down_w4(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
   if (w_dtype == kBF16)
     return launch_down<false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
   return launch_down<true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);

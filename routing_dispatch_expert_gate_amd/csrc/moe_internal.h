@@ -195,4 +195,7 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
 
 int64_t align_max_tiles(int64_t T, int k, int E, int block_m);
 
+// int4 codes [n] (one per int8, in [-8, 7]) -> packed [n / 2], n % 16 == 0
+hipError_t launch_pack_i4(const int8_t* codes, int64_t n, uint8_t* packed, hipStream_t s);
+
 }  // namespace moe

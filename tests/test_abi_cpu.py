@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -107,6 +107,40 @@ def test_route_grouped_validation(moe):
     assert rg() == WORKSPACE
     assert rg(T=0) == OK
     assert L.moe_route_workspace_size(64, 512, 256, 8) > 0
+
+
+def test_pack_int4_and_w4a16_validation(moe):
+    L = moe.lib
+    assert L.moe_pack_int4(P, 4, 96, P, None) == UNSUPPORTED     # K % 64
+    assert L.moe_pack_int4(P, -1, 64, P, None) == INVALID
+    assert L.moe_pack_int4(None, 4, 64, P, None) == INVALID
+    assert L.moe_pack_int4(P, 4, 64, ctypes.c_void_p(264), None) == INVALID   # misaligned
+    assert L.moe_pack_int4(P, 0, 64, None, None) == OK
+    I4 = 3
+    assert L.moe_ffn_block_m(16, 4096, 1024, 256, 8, I4) == 64
+    assert L.moe_ffn_block_m(4096, 4096, 1024, 8, 2, I4) == 256
+    # W4A16 needs bf16 activations and both scale arrays
+    n = L.moe_ffn_workspace_size(64, 256, 128, 8, 2, I4)
+    assert n >= 64 * 2 * 128 * 2
+    bm = L.moe_ffn_block_m(64, 256, 128, 8, 2, I4)
+
+    def ffn(act=BF16, s13=P, s2=P, T=64):
+        return L.moe_expert_ffn(P, act, None, P, P, I4, s13, s2, P, P, P, bm, None, T, 256, 128, 8, 2, P, BF16,
+                                None, 0, None)
+
+    assert ffn(act=F32) == UNSUPPORTED
+    assert ffn(act=I8) == UNSUPPORTED
+    assert ffn(s13=None) == INVALID
+    assert ffn(s2=None) == INVALID
+    assert ffn() == WORKSPACE
+    assert ffn(T=0) == OK
+
+    def layer(xd=BF16, s=P):
+        return L.moe_layer(P, xd, P, BF16, None, P, P, I4, s, s, 64, 256, 128, 8, 2, 0, P, xd, None, None, 0, None)
+
+    assert layer(xd=F32) == UNSUPPORTED
+    assert layer(s=None) == INVALID
+    assert layer() == WORKSPACE
 
 
 def test_align_validation(moe):

@@ -21,7 +21,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "i8": 5e-2, "f32": 1e-4}
+TOL = {"bf16": 2e-2, "i8": 5e-2, "f32": 1e-4, "i4": 2e-2}
 SAMPLE = {1: None, 2: 192, 3: 24, 4: None, 5: 128}
 
 
@@ -48,6 +48,9 @@ class Case:
         i = self.inp
         self.x, self.wg, self.bias = to_dev(i.x), to_dev(i.wg), to_dev(i.bias)
         self.w13, self.w2, self.s13, self.s2 = to_dev(i.w13), to_dev(i.w2), to_dev(i.s13), to_dev(i.s2)
+        if spec.w_dtype == "i4" and self.w13 is not None:
+            # int4 codes -> the kernels' packed layout (two per byte)
+            self.w13, self.w2 = _moe().pack_int4(self.w13), _moe().pack_int4(self.w2)
         s = spec
         self.route = oracle.route(oracle.to_f64(i.x, s.x_dtype), oracle.to_f64(i.wg, s.wg_dtype), s.k, i.bias)
         self.C = oracle.capacity(s.T, s.k, s.E, s.capacity_factor)
@@ -329,7 +332,7 @@ def _ffn_combine_case(c, sample):
     the oracle layer on ``sample``."""
     moe = _moe()
     s = c.spec
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}[s.w_dtype]
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8}[s.w_dtype]
     bm = moe.ffn_block_m(s.T, s.H, s.I, s.E, s.k, wdt)
     ids = to_dev(c.route["ids"])
     w = to_dev(c.route["w"].astype(np.float32))
@@ -380,6 +383,13 @@ SMALL = [
     # round's units over K (partial tiles summed by the reduce kernel)
     moe_synth.Spec("bf16_prefill_last_round_split", 1024, 512, 4, 2, 512),
     moe_synth.Spec("i8_prefill_last_round_split", 1024, 512, 4, 2, 512, w_dtype="i8"),
+    # W4A16: one case per int4 tile (prefill/mid 256 x BN, decode 64 x BN, for
+    # BN = 256, 128 and 64), with and without drops
+    moe_synth.Spec("i4_prefill_E4", 600, 512, 4, 2, 384, w_dtype="i4"),
+    moe_synth.Spec("i4_mid_H320_I192_cap1", 257, 320, 8, 2, 192, w_dtype="i4", capacity_factor=1.0),
+    moe_synth.Spec("i4_decode_E64", 16, 512, 64, 6, 256, w_dtype="i4"),
+    moe_synth.Spec("i4_decode_H384_I192", 8, 384, 32, 4, 192, w_dtype="i4"),
+    moe_synth.Spec("i4_decode_H320", 8, 320, 16, 2, 128, w_dtype="i4", zipf_s=1.1),
 ]
 
 
@@ -462,6 +472,25 @@ def test_combine_shared_without_extras_equals_combine():
     b = moe.combine_shared(y, p, w, T, k, torch.bfloat16, shared=None, shared_factor=3.0, bias=None)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# --------------------------------------------------------------- W4A16
+def test_pack_int4_layout():
+    """Packed byte j of a row = code 2j (low nibble) | code 2j+1 (high
+    nibble), two's complement nibbles; checked against that definition."""
+    moe = _moe()
+    rng = np.random.default_rng(8)
+    codes = rng.integers(-8, 8, size=(37, 192), dtype=np.int8)
+    got = moe.pack_int4(to_dev(codes)).cpu().numpy()
+    lo = codes[:, 0::2].astype(np.int64) & 0xF
+    hi = codes[:, 1::2].astype(np.int64) & 0xF
+    np.testing.assert_array_equal(got, (lo | (hi << 4)).astype(np.uint8))
+
+
+def test_w4a16_decode_workload():
+    """The 16-token, 256-expert, top-8 decode workload with int4 experts."""
+    spec = moe_synth.CONFIGS[4].replace(name="decode_w4a16_T16_H4096_E256_k8_I1024", w_dtype="i4")
+    _layer_case(Case(spec, 4000), np.arange(spec.T))
 
 
 # ------------------------------------------------------------------ layer
