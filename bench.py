@@ -31,10 +31,11 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s; grouped-GEMM % MFMA peak; route+combine % HBM BW"
 PEAK_HBM_GBPS = 8000.0
-PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3}
+# W4A16 ("i4") widens its int4 weights to bf16 and runs the bf16 MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3, "i4": 2500.0}
 RIDGE = {k: v * 1e12 / (PEAK_HBM_GBPS * 1e9) for k, v in PEAK_TFLOPS.items()}   # flop per byte
 CPU_SAMPLE = {1: 64, 2: 1024, 3: 64, 4: 16, 5: 512}
-BYTES = {"f32": 4, "bf16": 2, "i8": 1}
+BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}
 
 
 def log(msg: str) -> None:
@@ -47,6 +48,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, Mixtral-shaped prefill)")
+    ap.add_argument("--w-dtype", choices=("bf16", "i8", "i4"), default=None,
+                    help="run the workload with these expert weights instead of its own (i4: W4A16 with "
+                         "int4 codes and per-channel scales, packed on the device)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-library-ref", action="store_true",
                     help="skip the hipBLASLt (torch.bmm) reference on the same GEMM shapes")
@@ -177,10 +181,10 @@ def library_gemm_reference(torch, spec, d, N: int, D: int):
     return res
 
 
-def cpu_baseline(cfg: int, sample_n: int) -> dict:
+def cpu_baseline(cfg: int, sample_n: int, spec=None) -> dict:
     import moe_synth
     import oracle
-    inp = moe_synth.config_inputs(cfg)
+    inp = moe_synth.config_inputs(cfg) if spec is None else moe_synth.make_inputs(spec, 1000 * cfg)
     T = inp.spec.T
     S = min(sample_n, T)
     sample = np.sort(np.random.default_rng(7).choice(T, size=S, replace=False))
@@ -225,10 +229,18 @@ def main() -> int:
 
     cfg = args.config
     spec = moe_synth.CONFIGS[cfg]
+    if args.w_dtype and args.w_dtype != spec.w_dtype:
+        tag = {"bf16": "w16a16", "i8": "w8a8", "i4": "w4a16"}[args.w_dtype]
+        spec = spec.replace(w_dtype=args.w_dtype, name=f"{spec.name}_{tag}")
     T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
     log(f"workload {cfg}: {spec.name}; generating inputs")
-    inp = moe_synth.config_inputs(cfg)
+    inp = moe_synth.make_inputs(spec, 1000 * cfg)
     d = {n: to_dev(getattr(inp, n), torch) for n in ("x", "wg", "bias", "w13", "w2", "s13", "s2")}
+    if spec.w_dtype == "i4":
+        # offline weight preparation: int4 codes -> the packed layout
+        d["w13"], d["w2"] = moe.pack_int4(d["w13"]), moe.pack_int4(d["w2"])
+        inp.w13 = inp.w2 = None
+        torch.cuda.synchronize()
     C = moe.capacity(T, k, E, spec.capacity_factor) if spec.capacity_factor > 0 else 0
     layer = moe.Layer(T, H, I, E, k, d["x"].dtype, d["w13"].dtype)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
@@ -363,13 +375,14 @@ def main() -> int:
     if not args.no_cpu_baseline:
         n = args.cpu_sample or CPU_SAMPLE[cfg]
         log(f"timing the CPU oracle on {n} tokens")
-        cpu = cpu_baseline(cfg, n)
+        cpu = cpu_baseline(cfg, n, spec)
 
     rec = {
         "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "i8": "int8 (W8A8)", "f32": "f32"}[spec.w_dtype],
+        "dtype": {"bf16": "bf16", "i8": "int8 (W8A8)", "f32": "f32", "i4": "bf16 MFMA on int4 weights (W4A16)"}[
+            spec.w_dtype],
         "data": "synthetic (seeded; random-init weights of the workload's shapes)",
         "config": {"workload": spec.name, "T": T, "H": H, "E": E, "top_k": k, "I": I,
                    "capacity": C, "x_dtype": spec.x_dtype, "w_dtype": spec.w_dtype,

@@ -283,12 +283,15 @@ void gg_kernel(const GemmArgs a) {
   // issues no copies at all (those rows are never stored); any other wave
   // issues all of its copies per stage, so its vmcnt waits stay exact.
   bool copies = false;
-  // W4A16: this wave's B blocks (wv, wv + NW, ...)
+  // W4A16: this wave's B blocks (wv, wv + NW, ...), and the prefix of its A
+  // blocks that hold valid rows: only those are copied, and the per-stage
+  // count nva + nbw is what the waits use
   const int nbw = W4 ? LB + (wv < LBR ? 1 : 0) : 0;
+  int nva = 0;
   if constexpr (W4) {
-    copies = nbw > 0;
-#pragma unroll
-    for (int j = 0; j < LA; ++j) copies |= (wv * LA + j) * RPB < rows;
+    nva = (rows - wv * LA * RPB + RPB - 1) / RPB;
+    nva = nva < 0 ? 0 : (nva > LA ? LA : nva);
+    copies = nva + nbw > 0;
   } else {
 #pragma unroll
     for (int j = 0; j < L; ++j) {
@@ -340,8 +343,9 @@ void gg_kernel(const GemmArgs a) {
     if constexpr (W4) {
 #pragma unroll
       for (int j = 0; j < LA; ++j)
-        __builtin_amdgcn_global_load_lds((glb_void*)(abase + (size_t)kt * ROWB + goff[j]),
-                                         (lds_void*)(st + (wv * LA + j) * 1024), 16, 0, 0);
+        if (j < nva)
+          __builtin_amdgcn_global_load_lds((glb_void*)(abase + (size_t)kt * ROWB + goff[j]),
+                                           (lds_void*)(st + (wv * LA + j) * 1024), 16, 0, 0);
 #pragma unroll
       for (int j = 0; j < NG - LA; ++j)
         if (j < nbw)
@@ -359,13 +363,7 @@ void gg_kernel(const GemmArgs a) {
   // exact wait for stage kt with `after` later stages in flight
   auto wait_stage = [&](int after) {
     if constexpr (W4) {
-      if constexpr (LBR > 0) {
-        if (nbw > LB) {
-          wait_vm_stages<LA + LB + 1, S - 2>(after);
-          return;
-        }
-      }
-      wait_vm_stages<LA + LB, S - 2>(after);
+      wait_vm_dyn<LA + LB + (LBR > 0 ? 1 : 0), S - 2>(nva + nbw, after);
     } else {
       wait_vm_stages<L, S - 2>(after);
     }
@@ -812,15 +810,23 @@ constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4,
                                 {256, 64, 2, 2, 3, 128, 8},   {256, 64, 2, 2, 3, 128, 8},
                                 {64, 64, 1, 2, 6, 64, 8}};
 
-// W4A16 tiles: packed B stages are a quarter of the bf16 ones, so the
-// prefill/mid tile keeps 256 x 256 with 8 waves of 128 x 64 (each B fragment
-// is widened by two waves, not four) and three 40 KiB stages; decode keeps
-// 64 x BN with eight 8 KiB stages in flight for weight streaming.
-constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 3, 128, 4}, {64, 256, 1, 4, 8, 64, 8},
-                                {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 8, 64, 8}};
-constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {64, 256, 1, 4, 8, 64, 8},
-                                  {256, 128, 2, 2, 3, 128, 8}, {64, 128, 1, 2, 8, 64, 8},
-                                  {256, 64, 2, 2, 3, 128, 8},  {64, 64, 1, 2, 8, 64, 8}};
+// W4A16 tiles, three per N family (BN = 256, 128, 64): prefill, mid, decode.
+// Packed B stages are a quarter of the bf16 ones and each B fragment is
+// widened by every wave that uses it, so waves own 128 x 64 (two waves share
+// a fragment in the prefill tile, one in the others).  All stages are
+// 128-byte A rows (64 values of K), which halves the barriers per byte of
+// weights against 64-byte rows.  Mid tiles are 128 rows (one per expert at
+// ~128 rows); decode tiles are 64 rows with two stages, so five workgroups
+// share a CU: at decode the K loop is latency-bound and more independent
+// workgroups stream faster than deeper pipelines (measured).
+constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 3, 128, 4}, {128, 256, 1, 4, 3, 128, 4},
+                                {64, 256, 1, 4, 2, 128, 8},  {256, 128, 2, 2, 3, 128, 8},
+                                {128, 128, 1, 2, 3, 128, 8}, {64, 128, 1, 2, 3, 128, 8}};
+constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {128, 256, 1, 4, 3, 128, 2},
+                                  {64, 256, 1, 4, 2, 128, 8},  {256, 128, 2, 2, 3, 128, 8},
+                                  {128, 128, 1, 2, 3, 128, 8}, {64, 128, 1, 2, 3, 128, 8},
+                                  {256, 64, 2, 2, 3, 128, 8},  {128, 64, 1, 2, 3, 128, 8},
+                                  {64, 64, 1, 2, 3, 128, 8}};
 
 #define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R, G) \
   case IDX:                                       \
@@ -869,20 +875,25 @@ hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
   if constexpr (UP) {
     switch (var) {
       MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 4)
-      MOE_GG4_CASE(1, 64, 256, 1, 4, 8, 64, 8)
-      MOE_GG4_CASE(2, 256, 128, 2, 2, 3, 128, 8)
-      MOE_GG4_CASE(3, 64, 128, 1, 2, 8, 64, 8)
+      MOE_GG4_CASE(1, 128, 256, 1, 4, 3, 128, 4)
+      MOE_GG4_CASE(2, 64, 256, 1, 4, 2, 128, 8)
+      MOE_GG4_CASE(3, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(4, 128, 128, 1, 2, 3, 128, 8)
+      MOE_GG4_CASE(5, 64, 128, 1, 2, 3, 128, 8)
       default:
         return hipErrorInvalidValue;
     }
   } else {
     switch (var) {
       MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 2)
-      MOE_GG4_CASE(1, 64, 256, 1, 4, 8, 64, 8)
-      MOE_GG4_CASE(2, 256, 128, 2, 2, 3, 128, 8)
-      MOE_GG4_CASE(3, 64, 128, 1, 2, 8, 64, 8)
-      MOE_GG4_CASE(4, 256, 64, 2, 2, 3, 128, 8)
-      MOE_GG4_CASE(5, 64, 64, 1, 2, 8, 64, 8)
+      MOE_GG4_CASE(1, 128, 256, 1, 4, 3, 128, 2)
+      MOE_GG4_CASE(2, 64, 256, 1, 4, 2, 128, 8)
+      MOE_GG4_CASE(3, 256, 128, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(4, 128, 128, 1, 2, 3, 128, 8)
+      MOE_GG4_CASE(5, 64, 128, 1, 2, 3, 128, 8)
+      MOE_GG4_CASE(6, 256, 64, 2, 2, 3, 128, 8)
+      MOE_GG4_CASE(7, 128, 64, 1, 2, 3, 128, 8)
+      MOE_GG4_CASE(8, 64, 64, 1, 2, 3, 128, 8)
       default:
         return hipErrorInvalidValue;
     }
@@ -1023,10 +1034,11 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     snprintf(p.up_name, sizeof p.up_name, "ffn_f32_kernel<up>");
     snprintf(p.down_name, sizeof p.down_name, "ffn_f32_kernel<down>");
   } else if (w_dtype == kI4) {
-    const bool decode = (double)n / E <= 24.0;
-    p.up_var = (I % 128 == 0 ? 0 : 2) + (decode ? 1 : 0);
-    p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 2 : 4)) + (decode ? 1 : 0);
-    p.block_m = decode ? 64 : 256;
+    const double mean_rows = (double)n / E;
+    const int cls = mean_rows <= 24.0 ? 2 : (mean_rows <= 192.0 ? 1 : 0);
+    p.up_var = (I % 128 == 0 ? 0 : 3) + cls;
+    p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 3 : 6)) + cls;
+    p.block_m = cls == 2 ? 64 : (cls == 1 ? 128 : 256);
     const Variant u = kUpVarW4[p.up_var], d = kDownVarW4[p.down_var];
     snprintf(p.up_name, sizeof p.up_name, "gg_kernel<w4a16,up,%dx%d,%dx%d,S%d,R%d,G%d>", u.bm, u.bn, u.wm,
              u.wn, u.stages, u.rowb, u.gn);

@@ -127,6 +127,19 @@ __device__ __forceinline__ void wait_vm_stages(int m) {
     wait_vmcnt<0>();
   }
 }
+// the same for a runtime per-stage count l in [0, LMAX] (wave-uniform)
+template <int LMAX, int MMAX>
+__device__ __forceinline__ void wait_vm_dyn(int l, int m) {
+  if constexpr (LMAX > 0) {
+    if (l == LMAX) {
+      wait_vm_stages<LMAX, MMAX>(m);
+      return;
+    }
+    wait_vm_dyn<LMAX - 1, MMAX>(l, m);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 // All of this wave's LDS reads have returned, then the workgroup barrier.
 // The memory clobber keeps every LDS access on its side of the barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }

@@ -390,6 +390,9 @@ SMALL = [
     moe_synth.Spec("i4_decode_E64", 16, 512, 64, 6, 256, w_dtype="i4"),
     moe_synth.Spec("i4_decode_H384_I192", 8, 384, 32, 4, 192, w_dtype="i4"),
     moe_synth.Spec("i4_decode_H320", 8, 320, 16, 2, 128, w_dtype="i4", zipf_s=1.1),
+    moe_synth.Spec("i4_mid_E8_T512", 512, 512, 8, 2, 256, w_dtype="i4"),
+    moe_synth.Spec("i4_prefill_H384_I192", 1024, 384, 4, 2, 192, w_dtype="i4"),
+    moe_synth.Spec("i4_prefill_H320_k1", 800, 320, 4, 1, 128, w_dtype="i4", capacity_factor=1.25),
 ]
 
 
