@@ -21,6 +21,13 @@
 //      by popcount of the lower lanes.  Ranks therefore come from an ordered
 //      scan, never from the order atomics return in, so every output is
 //      deterministic.
+// Up to kOneBlockSlots slots the three steps run in one workgroup of sixteen
+// waves instead (align_one_block_kernel): each wave loads a contiguous
+// sixteenth of the ids into registers at once (at most 16 per lane, so one
+// memory latency), counts them in its own LDS histogram, one barrier, the
+// experts' threads scan over waves and over experts, another barrier, and
+// each wave ranks its sixteenth from the same registers as above.  One launch
+// instead of three: at these sizes the launches cost more than the work.
 #include "moe_internal.h"
 
 namespace moe {
@@ -36,9 +43,17 @@ __global__ __launch_bounds__(kAlignThreads) void align_hist_kernel(const int32_t
   __syncthreads();
   const int64_t s0 = (int64_t)blockIdx.x * spb;
   const int64_t s1 = s0 + spb < n ? s0 + spb : n;
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += kAlignThreads) {
-    const int e = ids[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&h[e], 1);
+  // eight loads in flight per thread, then their LDS atomics
+  for (int64_t c = s0; c < s1; c += 8 * kAlignThreads) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t s = c + u * kAlignThreads + threadIdx.x;
+      ev[u] = s < s1 ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&h[ev[u]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kAlignThreads) bhist[(size_t)blockIdx.x * E + e] = h[e];
@@ -117,9 +132,20 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   const int64_t w1 = w0 + sub < s1 ? w0 + sub : s1;
   int32_t* my = wh + wv * kMaxE;
 
-  for (int64_t s = w0 + lane; s < w1; s += 64) {
-    const int e = ids[s];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&my[e], 1);
+  // this wave's ids, eight loads in flight per lane; kept for the ranking
+  // pass when the quarter fits (the usual 1024-slot blocks: four per lane)
+  constexpr int KEEP = 8;
+  int idv[KEEP];
+  const bool kept_regs = w1 - w0 <= 64 * KEEP;
+  for (int64_t c = w0; c < w1; c += 64 * KEEP) {
+#pragma unroll
+    for (int u = 0; u < KEEP; ++u) {
+      const int64_t s = c + 64 * u + lane;
+      idv[u] = s < w1 ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < KEEP; ++u)
+      if ((unsigned)idv[u] < (unsigned)E) atomicAdd(&my[idv[u]], 1);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
@@ -146,7 +172,15 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   for (int64_t base = w0; base < w1; base += 64) {
     const int64_t s = base + lane;
     const bool in_range = s < w1;
-    const int e = in_range ? ids[s] : -1;
+    int e = -1;
+    if (kept_regs) {
+      const int u = (int)((base - w0) >> 6);   // uniform, < KEEP
+#pragma unroll
+      for (int v = 0; v < KEEP; ++v)
+        if (v == u) e = idv[v];
+    } else if (in_range) {
+      e = ids[s];
+    }
     const bool valid = in_range && (unsigned)e < (unsigned)E;   // out-of-range ids are dropped
     // lanes holding the same expert: agree on every bit of the id
     uint64_t same = __ballot(valid);
@@ -172,6 +206,123 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   for (int64_t i = N + s0 + tid; i < f1; i += kAlignThreads) sorted_slot[i] = -1;
 }
 
+// ------------------------------------------------- one-workgroup variant --
+constexpr int kOneThreads = 1024;
+constexpr int kOneWaves = kOneThreads / 64;
+constexpr int kOneIds = 16;                        // ids per lane
+constexpr int64_t kOneBlockSlots = (int64_t)kOneThreads * kOneIds;
+
+__global__ __launch_bounds__(kOneThreads) void align_one_block_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int64_t cap, int bm, int64_t max_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ pos, int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles,
+    int32_t* __restrict__ num_dropped) {
+  __shared__ int32_t wh[kOneWaves * kMaxE];   // per-wave counts, then per-wave bases
+  __shared__ int32_t off_s[kMaxE];
+  __shared__ int tmp[kMaxE];
+  __shared__ int tot[2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < kOneWaves * kMaxE; i += kOneThreads) wh[i] = 0;
+  __syncthreads();
+  const int64_t sub = ((n + kOneWaves - 1) / kOneWaves + 63) / 64 * 64;
+  const int64_t w0 = (int64_t)wv * sub < n ? (int64_t)wv * sub : n;
+  const int64_t w1 = w0 + sub < n ? w0 + sub : n;
+  int32_t* my = wh + wv * kMaxE;
+  // this lane's ids, slot w0 + 64 j + lane (-1 past the range), all loads in flight at once
+  int idv[kOneIds];
+#pragma unroll
+  for (int j = 0; j < kOneIds; ++j) {
+    const int64_t s = w0 + 64 * j + lane;
+    idv[j] = s < w1 ? ids[s] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kOneIds; ++j)
+    if ((unsigned)idv[j] < (unsigned)E) atomicAdd(&my[idv[j]], 1);
+  __syncthreads();
+  // expert e: bases over waves (slot order), total, kept count
+  int kept = 0, ntile = 0;
+  const int e = tid;
+  if (e < kMaxE) {
+    int total = 0;
+    if (e < E) {
+      for (int q = 0; q < kOneWaves; ++q) {
+        const int v = wh[q * kMaxE + e];
+        wh[q * kMaxE + e] = total;
+        total += v;
+      }
+      counts[e] = total;
+      kept = cap > 0 && total > cap ? (int)cap : total;
+      ntile = (kept + bm - 1) / bm;
+    }
+  }
+  // exclusive scans over the experts of kept rows and of row tiles: the
+  // first four waves hold the experts; Hillis-Steele in LDS, packed as
+  // kept | ntile << 20 is not safe for large counts, so two passes
+  int offv = 0, tbase = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int v = pass == 0 ? kept : ntile;
+    if (tid < kMaxE) tmp[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < kMaxE; o <<= 1) {
+      const int add = (tid < kMaxE && tid >= o) ? tmp[tid - o] : 0;
+      __syncthreads();
+      if (tid < kMaxE) tmp[tid] += add;
+      __syncthreads();
+    }
+    if (tid < kMaxE) {
+      if (pass == 0)
+        offv = tmp[tid] - v;
+      else
+        tbase = tmp[tid] - v;
+    }
+    if (tid == kMaxE - 1) tot[pass] = tmp[tid];
+    __syncthreads();
+  }
+  const int n_kept = tot[0], n_tiles = tot[1];
+  if (e < E) {
+    offsets[e] = offv;
+    off_s[e] = offv;
+    for (int i = 0; i < ntile; ++i) {
+      const int r = kept - i * bm < bm ? kept - i * bm : bm;
+      *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tbase + i)) = make_int4(e, offv + i * bm, r, 0);
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = n_kept;
+    *num_dropped = (int32_t)(n - n_kept);
+    *num_tiles = n_tiles;
+  }
+  for (int64_t q = n_tiles + tid; q < max_tiles; q += kOneThreads)
+    *reinterpret_cast<int4*>(tiles + 4 * q) = make_int4(-1, 0, 0, 0);
+  __syncthreads();
+  // rank this wave's slots in slot order
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < kOneIds; ++j) {
+    if (w0 + 64 * j >= w1) break;                   // uniform
+    const int64_t s = w0 + 64 * j + lane;
+    const bool in_range = s < w1;
+    const int ex = idv[j];
+    const bool valid = in_range && (unsigned)ex < (unsigned)E;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (ex >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    int rank = 0;
+    if (valid) rank = my[ex] + __popcll(same & lt);
+    if (valid && (same & lt) == 0) my[ex] += __popcll(same);
+    if (in_range) {
+      const bool keep = valid && (cap <= 0 || rank < cap);
+      const int p = keep ? off_s[ex] + rank : -1;
+      pos[s] = p;
+      if (keep) sorted_slot[p] = (int32_t)s;
+    }
+  }
+  for (int64_t i = n_kept + tid; i < n; i += kOneThreads) sorted_slot[i] = -1;
+}
+
 }  // namespace
 
 int64_t align_max_tiles(int64_t T, int k, int E, int block_m) {
@@ -182,6 +333,12 @@ int64_t align_max_tiles(int64_t T, int k, int E, int block_m) {
 AlignPlan plan_align(int64_t T, int k, int E) {
   AlignPlan p;
   const int64_t n = T * k;
+  if (n <= kOneBlockSlots) {
+    p.slots_per_block = (int)(n > 0 ? n : 1);
+    p.nblocks = 0;   // one workgroup, no histogram workspace
+    p.ws_bytes = 0;
+    return p;
+  }
   // at most 1024 blocks: each scatter block sums the histograms before it
   p.slots_per_block = 1024;
   if (n > (int64_t)1024 * 1024) p.slots_per_block = (int)(((n + 1023) / 1024 + 255) / 256 * 256);
@@ -196,6 +353,13 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
                         int32_t* sorted_slot, int32_t* pos, int32_t* tiles, int32_t* num_tiles,
                         int32_t* num_dropped, void* ws, hipStream_t s) {
   const int64_t n = T * k;
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  if (p.nblocks == 0) {
+    align_one_block_kernel<<<1, kOneThreads, 0, s>>>(ids, n, E, ebits, cap, block_m, max_tiles, counts,
+                                                     offsets, sorted_slot, pos, tiles, num_tiles, num_dropped);
+    return hipGetLastError();
+  }
   int32_t* bhist = (int32_t*)ws;
   align_hist_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, p.slots_per_block, bhist);
   hipError_t err = hipGetLastError();
@@ -204,8 +368,6 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
                                                 counts, offsets, tiles, num_tiles, num_dropped);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int ebits = 0;
-  while ((1 << ebits) < E) ++ebits;
   align_scatter_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, ebits, p.slots_per_block, bhist,
                                                           offsets, cap, sorted_slot, pos);
   return hipGetLastError();

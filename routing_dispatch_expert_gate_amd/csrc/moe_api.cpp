@@ -283,8 +283,11 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, i
                                    (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_align launch");
   char b[128];
-  snprintf(b, sizeof b, "align_hist+align_scan+align_scatter(blocks=%d,slots/block=%d)", plan.nblocks,
-           plan.slots_per_block);
+  if (plan.nblocks == 0)
+    snprintf(b, sizeof b, "align_one_block_kernel(slots=%lld)", (long long)(T * k));
+  else
+    snprintf(b, sizeof b, "align_hist+align_scan+align_scatter(blocks=%d,slots/block=%d)", plan.nblocks,
+             plan.slots_per_block);
   return ok(b);
 }
 
@@ -552,7 +555,8 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn down launch");
   e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
-  return ok(route_name(c.rp) + " | align(blocks=" + std::to_string(c.ap.nblocks) + ") | " +
+  return ok(route_name(c.rp) + " | " + (c.ap.nblocks == 0 ? std::string("align(one block)")
+                                         : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
             c.fp.up_name + "+" + c.fp.down_name + "(block_m=" + std::to_string(c.fp.block_m) +
             ") | combine_kernel<pre-weighted>");
 }

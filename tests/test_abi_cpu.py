@@ -157,7 +157,11 @@ def test_align_validation(moe):
     assert call(k=3, E=2) == INVALID
     assert call(ids=None) == INVALID
     assert call(out=None) == INVALID
-    assert call() == WORKSPACE
+    # above 2^14 slots the three-launch path needs its histogram workspace;
+    # at or below it one workgroup needs none
+    assert call(T=2049, k=8) == WORKSPACE
+    assert L.moe_align_workspace_size(2049, 8, 8) > 0
+    assert L.moe_align_workspace_size(2048, 8, 8) == 0
     assert call(T=0) == OK
 
 

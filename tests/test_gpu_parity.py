@@ -254,6 +254,8 @@ def _check_align(ids, E, C, bm):
     moe = _moe()
     a = moe.align(to_dev(ids.astype(np.int32)), E, C or 0, bm)
     torch.cuda.synchronize()
+    # up to 2^14 slots one workgroup does all three steps, above them three launches
+    assert ("align_one_block_kernel" in moe.last_dispatch()) == (ids.size <= 1 << 14), moe.last_dispatch()
     ref = oracle.align(ids, E, C)
     np.testing.assert_array_equal(a["counts"].cpu().numpy(), ref["counts"])
     np.testing.assert_array_equal(a["offsets"].cpu().numpy(), ref["offsets"])
@@ -282,6 +284,8 @@ def test_align_bit_exact_on_workloads(cfg):
     (1, 8, 2, None, 128, 0.0), (3000, 8, 3, None, 128, 0.0), (1000, 64, 6, 30, 64, 1.5),
     (5000, 256, 8, 120, 128, 0.0), (4097, 256, 8, None, 256, 0.0), (2048, 4, 1, 100, 16, 3.0),
     (999, 1, 1, 500, 32, 0.0), (700, 7, 7, 650, 128, 0.0), (20000, 64, 6, 1920, 128, 1.1),
+    (2048, 256, 8, 80, 128, 0.0), (2049, 8, 8, None, 256, 0.0), (40000, 64, 6, 4000, 64, 1.1),
+    (4096, 4, 4, None, 16, 2.0),
 ])
 def test_align_bit_exact_edge_cases(T, E, k, C, bm, skew):
     rng = np.random.default_rng(T * 31 + E)
