@@ -5,12 +5,14 @@
 A step is one whole-layer call (moe_layer) over one batch of seeded synthetic
 inputs already resident in HBM.  The default workload is the Mixtral-8x7B
 shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  After the K
-timed steps, a staged pass runs the same layer through the per-step entry
-points with HIP events recorded between the launches on the stream the
-library launches on, to get each kernel's average duration; the dominant
-kernel's roofline is computed from those durations and its algorithmic
-flops/bytes.  The CPU oracle is timed on a bounded token sample of the same
-workload on the host cores (a baseline, not the target).
+timed steps, each step of the layer is launched through its own entry point K
+times back to back with HIP events around the run, on the stream the library
+launches on, to get each kernel's average duration (the host runs ahead of
+the GPU, so launch latency stays out of the small kernels' times); the
+dominant kernel's roofline is computed from those durations and its
+algorithmic flops/bytes.  A cold pass (after a 1 GiB write) gives each step's
+time with its inputs in HBM.  The CPU oracle is timed on a bounded token
+sample of the same workload on the host cores (a baseline, not the target).
 
 Prints exactly one JSON line.
 """
@@ -107,38 +109,67 @@ class Staged:
         self.P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
         self.DT = moe.binding._DT
 
-    def run(self, events=None):
+    def stages(self):
+        """(name, launch) for each step; each is idempotent once a full pass
+        has filled its inputs."""
         L, P, DT, s, d = self.moe.lib, self.P, self.DT, self.spec, self.d
         T, H, E, k, I = s.T, s.H, s.E, s.k, s.I
         st = self.moe.binding._stream(d["x"].device)
-        ev = events or [None] * 6
         chk = self.moe.binding._check
         ws = P(self.ws)
         act = self.xq if self.quant else d["x"]
 
-        def rec(i):
-            if ev[i] is not None:
-                ev[i].record()
+        def route():
+            chk(L.moe_route(P(d["x"]), DT[d["x"].dtype], P(d["wg"]), DT[d["wg"].dtype], P(d["bias"]), T, H, E, k,
+                            P(self.ids), P(self.w), None, P(self.xq), P(self.xs), ws, self.n_route, st))
 
-        rec(0)
-        chk(L.moe_route(P(d["x"]), DT[d["x"].dtype], P(d["wg"]), DT[d["wg"].dtype], P(d["bias"]), T, H, E, k,
-                        P(self.ids), P(self.w), None, P(self.xq), P(self.xs), ws, self.n_route, st))
-        rec(1)
-        chk(L.moe_align(P(self.ids), T, k, E, self.C, self.bm, P(self.counts), P(self.offsets),
-                        P(self.sorted_slot), P(self.pos), P(self.tiles), P(self.num_tiles),
-                        P(self.num_dropped), ws, self.n_align, st))
-        rec(2)
-        chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), DT[d["w13"].dtype], P(d["s13"]),
-                         P(self.sorted_slot), P(self.tiles), P(self.num_tiles), self.bm, T, H, I, E, k, ws,
-                         self.n_ffn, st))
-        rec(3)
-        chk(L.moe_ffn_down(P(d["w2"]), DT[d["w2"].dtype], P(d["s2"]), P(self.sorted_slot), P(self.tiles),
-                           P(self.num_tiles), self.bm, P(self.w), T, H, I, E, k, P(self.y), DT[self.y.dtype],
-                           ws, self.n_ffn, st))
-        rec(4)
-        chk(L.moe_combine(P(self.y), DT[self.y.dtype], P(self.pos), None, T, k, H, P(self.out),
-                          DT[self.out.dtype], st))
-        rec(5)
+        def align():
+            chk(L.moe_align(P(self.ids), T, k, E, self.C, self.bm, P(self.counts), P(self.offsets),
+                            P(self.sorted_slot), P(self.pos), P(self.tiles), P(self.num_tiles),
+                            P(self.num_dropped), ws, self.n_align, st))
+
+        def up():
+            chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), DT[d["w13"].dtype], P(d["s13"]),
+                             P(self.sorted_slot), P(self.tiles), P(self.num_tiles), self.bm, T, H, I, E, k, ws,
+                             self.n_ffn, st))
+
+        def down():
+            chk(L.moe_ffn_down(P(d["w2"]), DT[d["w2"].dtype], P(d["s2"]), P(self.sorted_slot), P(self.tiles),
+                               P(self.num_tiles), self.bm, P(self.w), T, H, I, E, k, P(self.y), DT[self.y.dtype],
+                               ws, self.n_ffn, st))
+
+        def combine():
+            chk(L.moe_combine(P(self.y), DT[self.y.dtype], P(self.pos), None, T, k, H, P(self.out),
+                              DT[self.out.dtype], st))
+
+        return [("route", route), ("align", align), ("ffn_up", up), ("ffn_down", down), ("combine", combine)]
+
+    def run(self, events=None):
+        ev = events or [None] * 6
+        if ev[0] is not None:
+            ev[0].record()
+        for i, (_, fn) in enumerate(self.stages()):
+            fn()
+            if ev[i + 1] is not None:
+                ev[i + 1].record()
+
+    def time_each(self, reps: int) -> dict:
+        """Average GPU time of each step launched `reps` times back to back
+        between two events: the host runs ahead of the GPU, so its launch
+        latency does not enter the small kernels' times."""
+        torch = self.torch
+        out = {}
+        for name, fn in self.stages():
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) / reps
+        return out
 
 
 def traffic_for(workload: str, kernel_src: str):
@@ -278,23 +309,20 @@ def main() -> int:
         f"(p10 {np.percentile(per_step, 10):.3f}, median {np.median(per_step):.3f}, "
         f"p90 {np.percentile(per_step, 90):.3f})")
 
-    # staged pass: per-kernel durations from events between launches
+    # per-kernel durations: each step (entry point) launched back to back
+    # `steps` times between two events on the library's stream
     st = Staged(moe, torch, spec, d, C)
     names = ["route", "align", "ffn_up", "ffn_down", "combine"]
-    acc = np.zeros(5)
     for _ in range(max(2, args.warmup)):
         st.run()
     torch.cuda.synchronize()
-    for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        st.run(evs)
-        torch.cuda.synchronize()
-        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
-    stage_ms = dict(zip(names, (acc / args.steps).tolist()))
+    stage_ms = st.time_each(args.steps)
     log("stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
 
     # isolated cold: a 1 GiB write before each staged pass evicts L2 and the
-    # last-level cache, so every stage reads its inputs from HBM
+    # last-level cache, so every stage reads its inputs from HBM (the host
+    # queues the pass's launches while the write runs, so events between them
+    # time the GPU)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     acc = np.zeros(5)
     for i in range(args.steps):

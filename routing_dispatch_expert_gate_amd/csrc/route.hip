@@ -289,7 +289,9 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
-  constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);   // rows per load batch
+  // rows per load batch (all sixteen at once costs occupancy: measured
+  // slower at large T)
+  constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);
   static_assert(kFmaTB % PF == 0, "batches");
   __shared__ float part[16][kFmaTB][EP];
   __shared__ float amax_s[16][kFmaTB];
