@@ -20,7 +20,7 @@ parallel and every chunk is reproducible on its own):
   ``clip(rint(N(0, 1) * 32), -127, 127)`` with per-output-channel fp32 scales
   ``0.02 / 32 * (0.75 + 0.5 * U(0, 1))``, i.e. weights of std ~0.02 already in
   their quantised storage form;
-* int4 expert weights (W4A16) are drawn the same way with
+* int4 expert weights (W4A16 and W4A8) are drawn the same way with
   ``clip(rint(N(0, 1) * 2.5), -8, 7)`` codes (stored one per int8, unpacked)
   and scales ``0.02 / 2.5 * (0.75 + 0.5 * U(0, 1))``;
 * the skewed workload adds per-expert logit offsets ``-s * ln(rank_e)`` with
@@ -54,7 +54,7 @@ class Spec:
     I: int
     x_dtype: str = "bf16"      # "f32" | "bf16"
     wg_dtype: str = "bf16"     # "f32" | "bf16"
-    w_dtype: str = "bf16"      # "f32" | "bf16" | "i8" | "i4" (codes in int8 storage)
+    w_dtype: str = "bf16"      # "f32" | "bf16" | "i8" | "i4", "i4a8" (int4 codes in int8 storage)
     out_dtype: str = "bf16"    # "f32" | "bf16"
     capacity_factor: float = 0.0   # <= 0: no capacity limit
     zipf_s: float = 0.0            # > 0: per-expert Zipf(s) logit offsets
@@ -117,7 +117,7 @@ def _int8_into(q_out: np.ndarray, s_out: np.ndarray, rng_q, rng_s, std: float, b
 
 
 def _storage(dtype: str):
-    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.int8}[dtype]
+    return {"f32": np.float32, "bf16": np.uint16, "i8": np.int8, "i4": np.int8, "i4a8": np.int8}[dtype]
 
 
 @dataclass
@@ -153,7 +153,7 @@ def make_inputs(spec: Spec, seed_base: int, threads: int | None = None,
     if with_experts:
         w13 = np.empty((E, 2 * I, H), dtype=_storage(spec.w_dtype))
         w2 = np.empty((E, H, I), dtype=_storage(spec.w_dtype))
-        if spec.w_dtype in ("i8", "i4"):
+        if spec.w_dtype in ("i8", "i4", "i4a8"):
             s13 = np.empty((E, 2 * I), dtype=np.float32)
             s2 = np.empty((E, H), dtype=np.float32)
 
@@ -162,7 +162,7 @@ def make_inputs(spec: Spec, seed_base: int, threads: int | None = None,
         _normal_into(out, dt, _rng(seed_base, tid, chunk), std)
 
     def run_expert(e):
-        if spec.w_dtype in ("i8", "i4"):
+        if spec.w_dtype in ("i8", "i4", "i4a8"):
             b = 8 if spec.w_dtype == "i8" else 4
             _int8_into(w13[e], s13[e], _rng(seed_base, TENSOR_W13, e), _rng(seed_base, TENSOR_S13, e), spec.w_std, b)
             _int8_into(w2[e], s2[e], _rng(seed_base, TENSOR_W2, e), _rng(seed_base, TENSOR_S2, e), spec.w_std, b)

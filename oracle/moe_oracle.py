@@ -59,6 +59,9 @@ R10 W4A16 ([LightOP] section 4.3, the quantisation matrix: INT4 weights with
     weight is code * scale; activations stay in their 16-bit storage type and
     the FFN is the R6 SwiGLU on those weights.  How the codes are made from
     real weights is offline and outside the hot path.
+R11 W4A8 ([LightOP] section 4.3, INT4 weights with INT8 activations): R7 with
+    the weight codes of R10, i.e. per-token int8 activations, int4 codes with
+    per-output-channel scales, integer accumulation, h re-quantised per row.
 """
 from __future__ import annotations
 
@@ -373,7 +376,7 @@ def layer(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capacity_factor,
     res = {"route": r, "align": a, "capacity": C, "tokens": tok}
 
     xq = xs = None
-    if w_dtype == "i8":
+    if w_dtype in ("i8", "i4a8"):
         xq, xs = quant_per_token_int8(_to_f32(x, x_dtype))
         res["xq"], res["xs"] = xq, xs
 
@@ -387,7 +390,7 @@ def layer(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capacity_factor,
             continue
         rows = pos_s[sel]
         tokens_e = tok[np.nonzero(sel)[0]]
-        if w_dtype == "i8":
+        if w_dtype in ("i8", "i4a8"):
             y_rows[rows] = _w8a8_ffn(xq[tokens_e], xs[tokens_e], w13[e], s13[e], w2[e], s2[e], I)
         elif w_dtype == "i4":
             w13e = dequant_rows(w13[e], s13[e])
@@ -418,7 +421,7 @@ def layer_token_major(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capac
     C = capacity(T, k, E, capacity_factor)
     seen = [0] * E
     out = np.zeros((T, H), dtype=np.float64)
-    if w_dtype == "i8":
+    if w_dtype in ("i8", "i4a8"):
         xq, xs = quant_per_token_int8(_to_f32(x, x_dtype))
     for t in range(T):
         for j in range(k):
@@ -427,7 +430,7 @@ def layer_token_major(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capac
             seen[e] += 1
             if not kept:
                 continue
-            if w_dtype == "i8":
+            if w_dtype in ("i8", "i4a8"):
                 y = _w8a8_ffn(xq[t:t + 1], xs[t:t + 1], w13[e], s13[e], w2[e], s2[e], I)[0]
             elif w_dtype == "i4":
                 # element by element in Python floats (binary64)

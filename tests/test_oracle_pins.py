@@ -277,7 +277,7 @@ def test_k_equals_e_is_dense_soft_mixture():
 
 
 @pytest.mark.parametrize("w_dtype,cap", [("f32", 0.0), ("f32", 0.6), ("i8", 0.0), ("i8", 0.7), ("bf16", 1.0),
-                                         ("i4", 0.0), ("i4", 0.6)])
+                                         ("i4", 0.0), ("i4", 0.6), ("i4a8", 0.6)])
 def test_expert_major_equals_token_major(w_dtype, cap):
     inp = _small_inputs(48, 32, 8, 3, 16, w_dtype=w_dtype, cap=cap,
                         x_dtype="bf16" if w_dtype != "f32" else "f32")
@@ -532,3 +532,18 @@ def test_int4_codes_in_range():
         assert q.dtype == np.int8 and q.min() >= -8 and q.max() <= 7
         assert q.min() == -8 and q.max() == 7      # both ends occur
     assert inp.s13.shape == (4, 128) and inp.s2.shape == (4, 128)
+
+
+# -------------------------------------------------------------------- W4A8
+def test_w4a8_is_w8a8_on_int4_codes():
+    """W4A8 (R11) is the W8A8 pipeline (R7) run on int4 codes: the same
+    numbers when the same codes are given as int8 weights; and it differs
+    from W4A16 only by the activation and h quantisation (small)."""
+    inp = _small_inputs(40, 64, 8, 2, 32, w_dtype="i4a8", x_dtype="bf16", cap=0.8)
+    a = oracle.layer(**_layer(inp))["out"]
+    b = oracle.layer(**_layer(inp, w_dtype="i8"))["out"]
+    np.testing.assert_array_equal(a, b)
+    c = oracle.layer(**_layer(inp, w_dtype="i4"))["out"]
+    rel = np.linalg.norm(a - c) / np.linalg.norm(c)
+    assert 0 < rel < 5e-2, rel
+    assert inp.w13.min() >= -8 and inp.w13.max() <= 7
