@@ -34,10 +34,11 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s; grouped-GEMM % MFMA peak; route+combine % HBM BW"
 PEAK_HBM_GBPS = 8000.0
 # W4A16 ("i4") widens its int4 weights to bf16 and runs the bf16 MFMA
-PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3, "i4": 2500.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3, "i4": 2500.0, "i4a8": 5000.0}
 RIDGE = {k: v * 1e12 / (PEAK_HBM_GBPS * 1e9) for k, v in PEAK_TFLOPS.items()}   # flop per byte
 CPU_SAMPLE = {1: 64, 2: 1024, 3: 64, 4: 16, 5: 512}
-BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5}
+BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "i4a8": 0.5}
+A8 = ("i8", "i4a8")                  # schemes that quantise activations per token
 
 
 def log(msg: str) -> None:
@@ -50,9 +51,10 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2, Mixtral-shaped prefill)")
-    ap.add_argument("--w-dtype", choices=("bf16", "i8", "i4"), default=None,
+    ap.add_argument("--w-dtype", choices=("bf16", "i8", "i4", "i4a8"), default=None,
                     help="run the workload with these expert weights instead of its own (i4: W4A16 with "
-                         "int4 codes and per-channel scales, packed on the device)")
+                         "int4 codes and per-channel scales, packed on the device; i4a8: the same weights "
+                         "with per-token int8 activations, W4A8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-library-ref", action="store_true",
                     help="skip the hipBLASLt (torch.bmm) reference on the same GEMM shapes")
@@ -83,8 +85,9 @@ class Staged:
         n = T * k
         dev = "cuda"
         i32, f32 = torch.int32, torch.float32
-        wdt = d["w13"].dtype
-        self.quant = spec.w_dtype == "i8"
+        wdt = "w4a8" if spec.w_dtype == "i4a8" else d["w13"].dtype
+        self.wd = moe.binding._DT[wdt]
+        self.quant = spec.w_dtype in A8
         self.ids = torch.empty((T, k), dtype=i32, device=dev)
         self.w = torch.empty((T, k), dtype=f32, device=dev)
         self.xq = torch.empty((T, H), dtype=torch.int8, device=dev) if self.quant else None
@@ -103,7 +106,7 @@ class Staged:
         self.out = torch.empty((T, H), dtype=d["x"].dtype, device=dev)
         self.n_route = int(L.moe_route_workspace_size(T, H, E, k))
         self.n_align = int(L.moe_align_workspace_size(T, k, E))
-        self.n_ffn = int(L.moe_ffn_workspace_size(T, H, I, E, k, moe.binding._DT[wdt]))
+        self.n_ffn = int(L.moe_ffn_workspace_size(T, H, I, E, k, self.wd))
         mx = max(self.n_route, self.n_align, self.n_ffn, 1)
         self.ws = torch.empty(mx, dtype=torch.uint8, device=dev)
         self.P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
@@ -129,12 +132,12 @@ class Staged:
                             P(self.num_dropped), ws, self.n_align, st))
 
         def up():
-            chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), DT[d["w13"].dtype], P(d["s13"]),
+            chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), self.wd, P(d["s13"]),
                              P(self.sorted_slot), P(self.tiles), P(self.num_tiles), self.bm, T, H, I, E, k, ws,
                              self.n_ffn, st))
 
         def down():
-            chk(L.moe_ffn_down(P(d["w2"]), DT[d["w2"].dtype], P(d["s2"]), P(self.sorted_slot), P(self.tiles),
+            chk(L.moe_ffn_down(P(d["w2"]), self.wd, P(d["s2"]), P(self.sorted_slot), P(self.tiles),
                                P(self.num_tiles), self.bm, P(self.w), T, H, I, E, k, P(self.y), DT[self.y.dtype],
                                ws, self.n_ffn, st))
 
@@ -261,19 +264,19 @@ def main() -> int:
     cfg = args.config
     spec = moe_synth.CONFIGS[cfg]
     if args.w_dtype and args.w_dtype != spec.w_dtype:
-        tag = {"bf16": "w16a16", "i8": "w8a8", "i4": "w4a16"}[args.w_dtype]
+        tag = {"bf16": "w16a16", "i8": "w8a8", "i4": "w4a16", "i4a8": "w4a8"}[args.w_dtype]
         spec = spec.replace(w_dtype=args.w_dtype, name=f"{spec.name}_{tag}")
     T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
     log(f"workload {cfg}: {spec.name}; generating inputs")
     inp = moe_synth.make_inputs(spec, 1000 * cfg)
     d = {n: to_dev(getattr(inp, n), torch) for n in ("x", "wg", "bias", "w13", "w2", "s13", "s2")}
-    if spec.w_dtype == "i4":
+    if spec.w_dtype in ("i4", "i4a8"):
         # offline weight preparation: int4 codes -> the packed layout
         d["w13"], d["w2"] = moe.pack_int4(d["w13"]), moe.pack_int4(d["w2"])
         inp.w13 = inp.w2 = None
         torch.cuda.synchronize()
     C = moe.capacity(T, k, E, spec.capacity_factor) if spec.capacity_factor > 0 else 0
-    layer = moe.Layer(T, H, I, E, k, d["x"].dtype, d["w13"].dtype)
+    layer = moe.Layer(T, H, I, E, k, d["x"].dtype, "w4a8" if spec.w_dtype == "i4a8" else d["w13"].dtype)
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     out = torch.empty((T, H), dtype=d["x"].dtype, device="cuda")
@@ -350,13 +353,13 @@ def main() -> int:
     bx, bg, bw = BYTES[spec.x_dtype], BYTES[spec.wg_dtype], BYTES[spec.w_dtype]
     by = 4 if spec.w_dtype == "f32" else 2
     bo = BYTES[spec.out_dtype]
-    ba = 1 if spec.w_dtype == "i8" else bx                  # activation bytes the up GEMM reads
-    bh = 1 if spec.w_dtype == "i8" else by                  # h bytes the down GEMM reads
+    ba = 1 if spec.w_dtype in A8 else bx                    # activation bytes the up GEMM reads
+    bh = 1 if spec.w_dtype in A8 else by                    # h bytes the down GEMM reads
     up_flops = 4.0 * N * H * I
     down_flops = 2.0 * N * H * I
-    up_bytes = D * 2 * I * H * bw + N * H * ba + N * I * (4 if spec.w_dtype == "i8" else by)
+    up_bytes = D * 2 * I * H * bw + N * H * ba + N * I * (4 if spec.w_dtype in A8 else by)
     down_bytes = D * H * I * bw + N * I * bh + N * H * by
-    route_bytes = T * H * bx + E * H * bg + 8 * T * k + (T * H + 4 * T if spec.w_dtype == "i8" else 0)
+    route_bytes = T * H * bx + E * H * bg + 8 * T * k + (T * H + 4 * T if spec.w_dtype in A8 else 0)
     align_bytes = 12 * T * k
     combine_bytes = N * H * by + T * H * bo + 4 * T * k
     dt = spec.w_dtype
@@ -364,7 +367,7 @@ def main() -> int:
     ai = up_flops / up_bytes
     if ai >= RIDGE[dt]:
         roof = {"bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": PEAK_TFLOPS[dt],
-                "unit": "TFLOP/s" if dt != "i8" else "TOP/s"}
+                "unit": "TFLOP/s" if dt not in A8 else "TOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": up_bytes / up_s / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -409,8 +412,8 @@ def main() -> int:
         "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "i8": "int8 (W8A8)", "f32": "f32", "i4": "bf16 MFMA on int4 weights (W4A16)"}[
-            spec.w_dtype],
+        "dtype": {"bf16": "bf16", "i8": "int8 (W8A8)", "f32": "f32", "i4": "bf16 MFMA on int4 weights (W4A16)",
+                  "i4a8": "int8 MFMA on int4 weights (W4A8)"}[spec.w_dtype],
         "data": "synthetic (seeded; random-init weights of the workload's shapes)",
         "config": {"workload": spec.name, "T": T, "H": H, "E": E, "top_k": k, "I": I,
                    "capacity": C, "x_dtype": spec.x_dtype, "w_dtype": spec.w_dtype,

@@ -54,7 +54,8 @@ typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
   MOE_I8 = 2,
-  MOE_I4 = 3   /* int4 codes packed two per byte (see moe_pack_int4); weights only */
+  MOE_I4 = 3,  /* int4 codes packed two per byte (see moe_pack_int4); weights only */
+  MOE_I4A8 = 4 /* the same packed int4 weights, run with int8 activations (W4A8) */
 } moe_dtype;
 
 /* Limits shared by all entry points: 1 <= E <= 256, 1 <= k <= min(E, 8),
@@ -166,12 +167,14 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  *     per-output-channel scale s13[e][n] or s2[e][n]; bf16 MFMA with fp32
  *     accumulation, the channel scale applied to the sum (before SwiGLU in
  *     the up GEMM); h is bf16 as in W16A16
- *   x        [T, H] act_dtype;  xs [T] fp32 (MOE_I8 only, else NULL)
+ *   act_dtype MOE_I8 with w_dtype MOE_I4A8 (W4A8, [LightOP] section 4.3):
+ *     the W8A8 rule above with the packed int4 codes as the int8 weights
+ *   x        [T, H] act_dtype;  xs [T] fp32 (act_dtype MOE_I8 only, else NULL)
  *   w13      [E, 2I, H] w_dtype: rows 0..I-1 are W1[e], rows I..2I-1 W3[e]
- *            (MOE_I4: [E, 2I, H/2] bytes as written by moe_pack_int4)
- *   w2       [E, H, I] w_dtype (MOE_I4: [E, H, I/2] packed bytes)
- *   s13, s2  [E, 2I], [E, H] fp32 per-output-channel scales (MOE_I8 and
- *            MOE_I4 only)
+ *            (MOE_I4, MOE_I4A8: [E, 2I, H/2] bytes as written by moe_pack_int4)
+ *   w2       [E, H, I] w_dtype (MOE_I4, MOE_I4A8: [E, H, I/2] packed bytes)
+ *   s13, s2  [E, 2I], [E, H] fp32 per-output-channel scales (MOE_I8,
+ *            MOE_I4 and MOE_I4A8 only)
  *   sorted_slot, tiles, num_tiles: from moe_align with the same block_m;
  *   block_m must equal moe_ffn_block_m() for this shape
  *   y_sorted [T*k, H] y_dtype out (MOE_F32 for f32 activations, else
@@ -249,7 +252,8 @@ moe_status moe_combine_shared(const void* y_sorted, int32_t y_dtype, const int32
  *   w13/w2/s13/s2 as in moe_expert_ffn, capacity as in moe_align
  *   (<= 0: none), out [T, H] with out_dtype == x_dtype.
  *   w_dtype MOE_I8 quantises x per token inside the route step (W8A8);
- *   w_dtype MOE_I4 (packed int4 weights, with s13/s2) needs bf16 x (W4A16).
+ *   w_dtype MOE_I4 (packed int4 weights, with s13/s2) needs bf16 x (W4A16);
+ *   w_dtype MOE_I4A8 (the same weights) quantises x per token (W4A8).
  * aux (host struct, may be NULL; each member may be NULL) names device
  * buffers the layer writes its intermediates to instead of the workspace:
  * topk_ids/topk_w/topk_p [T,k], counts [E], offsets [E+1], sorted_slot and

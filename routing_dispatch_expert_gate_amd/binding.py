@@ -16,9 +16,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_I8, MOE_I4 = 0, 1, 2, 3
-# torch.uint8 expert weights are int4 codes packed by pack_int4 (W4A16)
-_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8, torch.uint8: MOE_I4}
+MOE_F32, MOE_BF16, MOE_I8, MOE_I4, MOE_I4A8 = 0, 1, 2, 3, 4
+# torch.uint8 expert weights are int4 codes packed by pack_int4: W4A16, or
+# W4A8 where a call says so (w4a8=True, or the weight dtype given as "w4a8")
+_DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.int8: MOE_I8, torch.uint8: MOE_I4, "w4a8": MOE_I4A8}
+
+
+def _wdt(w: torch.Tensor, w4a8: bool) -> int:
+    if w4a8:
+        if w.dtype != torch.uint8:
+            raise ValueError("W4A8 takes packed int4 weights (uint8, from pack_int4)")
+        return MOE_I4A8
+    return _DT[w.dtype]
 
 _vp, _i32, _i64, _sz, _f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
 _st = ctypes.c_int
@@ -191,15 +200,18 @@ def pack_int4(codes: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def ffn_block_m(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype) -> int:
+def ffn_block_m(T: int, H: int, I: int, E: int, k: int, w_dtype) -> int:
     return int(lib.moe_ffn_block_m(T, H, I, E, k, _DT[w_dtype]))
 
 
 def expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, sorted_slot: torch.Tensor,
                tiles: torch.Tensor, num_tiles: torch.Tensor, block_m: int, k: int,
                topk_w: torch.Tensor | None = None, xs: torch.Tensor | None = None,
-               s13: torch.Tensor | None = None, s2: torch.Tensor | None = None) -> torch.Tensor:
-    """moe_expert_ffn: returns y_sorted [T*k, H] (rows >= N unwritten)."""
+               s13: torch.Tensor | None = None, s2: torch.Tensor | None = None,
+               w4a8: bool = False) -> torch.Tensor:
+    """moe_expert_ffn: returns y_sorted [T*k, H] (rows >= N unwritten).
+    Packed int4 weights run W4A16 with bf16 x, or W4A8 with ``w4a8`` (x = int8
+    codes, xs their scales)."""
     for t, nme in ((x, "x"), (w13, "w13"), (w2, "w2"), (sorted_slot, "sorted_slot"), (tiles, "tiles")):
         _dev(t, nme)
     T, H = x.shape
@@ -207,9 +219,10 @@ def expert_ffn(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, sorted_slot
     dev = x.device
     ydt = torch.float32 if w13.dtype == torch.float32 else torch.bfloat16
     y = torch.empty((T * k, H), dtype=ydt, device=dev)
-    nws = lib.moe_ffn_workspace_size(T, H, I, E, k, _DT[w13.dtype])
+    wd = _wdt(w13, w4a8)
+    nws = lib.moe_ffn_workspace_size(T, H, I, E, k, wd)
     ws = _ws(nws, dev)
-    _check(lib.moe_expert_ffn(_p(x), _DT[x.dtype], _p(xs), _p(w13), _p(w2), _DT[w13.dtype], _p(s13), _p(s2),
+    _check(lib.moe_expert_ffn(_p(x), _DT[x.dtype], _p(xs), _p(w13), _p(w2), wd, _p(s13), _p(s2),
                               _p(sorted_slot), _p(tiles), _p(num_tiles), block_m, _p(topk_w), T, H, I, E, k,
                               _p(y), _DT[ydt], _p(ws), nws, _stream(dev)))
     return y
@@ -221,18 +234,18 @@ def ffn_workspace(T: int, H: int, I: int, E: int, k: int, w_dtype: torch.dtype, 
     return _ws(n, device), n
 
 
-def ffn_up(x, w13, sorted_slot, tiles, num_tiles, block_m, k, E, I, ws, xs=None, s13=None):
+def ffn_up(x, w13, sorted_slot, tiles, num_tiles, block_m, k, E, I, ws, xs=None, s13=None, w4a8=False):
     """moe_ffn_up into the workspace ``ws`` = (tensor, nbytes) from ffn_workspace."""
     T, H = x.shape
-    _check(lib.moe_ffn_up(_p(x), _DT[x.dtype], _p(xs), _p(w13), _DT[w13.dtype], _p(s13), _p(sorted_slot),
+    _check(lib.moe_ffn_up(_p(x), _DT[x.dtype], _p(xs), _p(w13), _wdt(w13, w4a8), _p(s13), _p(sorted_slot),
                           _p(tiles), _p(num_tiles), block_m, T, H, I, E, k, _p(ws[0]), ws[1],
                           _stream(x.device)))
 
 
-def ffn_down(w2, sorted_slot, tiles, num_tiles, block_m, k, T, ws, y, topk_w=None, s2=None):
+def ffn_down(w2, sorted_slot, tiles, num_tiles, block_m, k, T, ws, y, topk_w=None, s2=None, w4a8=False):
     """moe_ffn_down from the workspace filled by ffn_up into ``y`` [T*k, H]."""
     E, H, I = w2.shape[0], w2.shape[1], _inner(w2)
-    _check(lib.moe_ffn_down(_p(w2), _DT[w2.dtype], _p(s2), _p(sorted_slot), _p(tiles), _p(num_tiles),
+    _check(lib.moe_ffn_down(_p(w2), _wdt(w2, w4a8), _p(s2), _p(sorted_slot), _p(tiles), _p(num_tiles),
                             block_m, _p(topk_w), T, H, I, E, k, _p(y), _DT[y.dtype], _p(ws[0]), ws[1],
                             _stream(y.device)))
 
@@ -275,7 +288,7 @@ class Layer:
     """moe_layer with a workspace allocated once and re-used across calls."""
 
     def __init__(self, T: int, H: int, I: int, E: int, k: int, x_dtype: torch.dtype,
-                 w_dtype: torch.dtype, device="cuda"):
+                 w_dtype, device="cuda"):
         self.shape = (T, H, I, E, k)
         self.x_dtype, self.w_dtype = x_dtype, w_dtype
         self.nws = lib.moe_layer_workspace_size(T, H, I, E, k, _DT[x_dtype], _DT[w_dtype])
@@ -290,16 +303,18 @@ class Layer:
             aux_s = MoeLayerAux(**{n: (aux[n].data_ptr() if aux.get(n) is not None else None)
                                    for n, _ in MoeLayerAux._fields_})
         _check(lib.moe_layer(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), _p(w13), _p(w2),
-                             _DT[w13.dtype], _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out),
+                             _DT[self.w_dtype], _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out),
                              _DT[out.dtype], ctypes.byref(aux_s) if aux_s is not None else None,
                              _p(self.ws), self.nws, _stream(x.device)))
         return out
 
 
-def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None):
+def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None, w4a8=False):
     """One moe_layer call (allocates its workspace); ``aux`` maps moe_layer_aux
-    member names to device tensors that receive the intermediates."""
+    member names to device tensors that receive the intermediates; ``w4a8``
+    runs packed int4 weights with int8 activations."""
     T, H = x.shape
     E, I = w2.shape[0], _inner(w2)
-    return Layer(T, H, I, E, k, x.dtype, w13.dtype, x.device)(x, wg, w13, w2, capacity, bias, s13, s2,
-                                                             aux=aux)
+    _wdt(w13, w4a8)
+    wd = "w4a8" if w4a8 else w13.dtype
+    return Layer(T, H, I, E, k, x.dtype, wd, x.device)(x, wg, w13, w2, capacity, bias, s13, s2, aux=aux)

@@ -41,6 +41,11 @@
 //    eight codes as one 32-bit word and widens them exactly to bf16 in
 //    registers, and the MFMAs are the bf16 ones; the epilogue applies the
 //    channel scales (before SwiGLU in the up GEMM).
+//  * W4A8 (same section, INT4 weights with INT8 activations): the W8A8 path
+//    with the same packed int4 B tiles (half the int8 bytes); each lane reads
+//    its sixteen codes as one 64-bit word and widens them to int8 (nibbles
+//    masked into bytes, sign-extended by a multiply that cannot carry, and
+//    put back in K order with two byte permutes per word).
 #include <math.h>
 #include <stdio.h>
 
@@ -53,6 +58,7 @@ constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 constexpr int kI8 = 2;
 constexpr int kI4 = 3;
+constexpr int kI4A8 = 4;
 
 
 template <bool I8>
@@ -90,6 +96,25 @@ __device__ __forceinline__ u32x4 widen_i4(uint32_t w) {
     const float hi = (float)((int32_t)(w << (24 - 8 * j)) >> 28);
     const bf16x2 p = {(__bf16)lo, (__bf16)hi};
     r[j] = __builtin_bit_cast(uint32_t, p);
+  }
+  return r;
+}
+
+// Sixteen int4 codes (8 bytes, as above) to sixteen int8 values in K order.
+__device__ __forceinline__ uint32_t sext_nibble_bytes(uint32_t u) {
+  // bytes hold 4-bit two's complement values; 8 * 0x1E = 0xF0 stays in its byte
+  return u | ((u & 0x08080808u) * 0x1Eu);
+}
+__device__ __forceinline__ u32x4 widen_i4_i8(uint32_t p0, uint32_t p1) {
+  u32x4 r;
+  const uint32_t p[2] = {p0, p1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = sext_nibble_bytes(p[h] & 0x0F0F0F0Fu);          // codes 0, 2, 4, 6
+    const uint32_t hi = sext_nibble_bytes((p[h] >> 4) & 0x0F0F0F0Fu);   // codes 1, 3, 5, 7
+    // v_perm_b32 selects bytes of {hi, lo}: 0-3 are lo's, 4-7 hi's
+    r[2 * h] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    r[2 * h + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
   }
   return r;
 }
@@ -196,7 +221,6 @@ __attribute__((amdgpu_waves_per_eu(
     (BM / WM) * (BN / WN) <= 128 * 64 && 2 * S * (BM * ROWB + BN * (W4 ? ROWB / 4 : ROWB)) <= 160 * 1024 ? 2
                                                                                                         : 1)))
 void gg_kernel(const GemmArgs a) {
-  static_assert(!(I8 && W4), "W4A16 takes bf16 activations");
   constexpr int NT = WM * WN * 64, NW = WM * WN;
   constexpr int WROWS = BM / WM, FM = WROWS / 32;
   constexpr int WCOLS = BN / WN, NF = WCOLS / 32;
@@ -204,7 +228,9 @@ void gg_kernel(const GemmArgs a) {
   constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
   constexpr int RPB = 1024 / ROWB;                   // rows per 1 KiB copy block
   constexpr int SUB = ROWB / 32;                     // MFMA k-substeps per stage
-  constexpr int BROWB = W4 ? ROWB / 4 : ROWB;       // B bytes per row per stage
+  // B bytes per row per stage (packed int4: half the int8 bytes, a quarter
+  // of the bf16 ones for the same K)
+  constexpr int BROWB = W4 ? (I8 ? ROWB / 2 : ROWB / 4) : ROWB;
   constexpr int STAGE = BM * ROWB + BN * BROWB;
   constexpr int EB = I8 ? 1 : 2;
   // 1 KiB copy blocks per stage.  bf16/int8: A and B blocks are split evenly,
@@ -242,7 +268,7 @@ void gg_kernel(const GemmArgs a) {
   const int nt = __builtin_amdgcn_readfirstlane(*a.num_tiles);
   const int nwork = nt * a.n_blocks;
   const int64_t kbytes = (int64_t)(UP ? a.H : a.I) * EB;
-  const int64_t kbytes_b = W4 ? kbytes / 4 : kbytes;   // a packed int4 weight row
+  const int64_t kbytes_b = W4 ? kbytes / (I8 ? 2 : 4) : kbytes;   // a packed int4 weight row
   const int nk_all = (int)(kbytes / ROWB);
   TailPlan tp{nwork, 1};
   if constexpr (!UP) tp = tail_plan(nwork, a.conc, nk_all);
@@ -418,16 +444,25 @@ void gg_kernel(const GemmArgs a) {
       const uint8_t* As = smem + (kt % S) * STAGE;
       const uint8_t* Bs = As + BM * ROWB;
       if constexpr (V > 0 && W4) {
-        // packed B: lane's eight codes of row (lane % 32), k-chunk
-        // 2s + lane / 32, one 32-bit LDS read, widened in registers
+        // packed B: the lane's codes of row (lane % 32), k-chunk
+        // 2s + lane / 32 (eight for bf16, sixteen for int8), read as 32-bit
+        // LDS words and widened in registers.  (Read as one 64-bit word, the
+        // int8 case is merged with the next substep's read into a form after
+        // which the compiler drains every in-flight copy.)
+        constexpr int CB = I8 ? 8 : 4;                 // packed bytes per lane per substep
         u32x4 af[SUB][V];
-        uint32_t bw[SUB][NF];
+        uint2 bw[SUB][NF];
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf)
-            bw[s][nf] = *reinterpret_cast<const uint32_t*>(Bs + (brow_of(nf) + (lane & 31)) * BROWB +
-                                                           4 * (2 * s + (lane >> 5)));
+          for (int nf = 0; nf < NF; ++nf) {
+            const uint8_t* bp = Bs + (brow_of(nf) + (lane & 31)) * BROWB + CB * (2 * s + (lane >> 5));
+            if constexpr (I8)
+              bw[s][nf] = make_uint2(reinterpret_cast<const uint32_t*>(bp)[0],
+                                     reinterpret_cast<const uint32_t*>(bp)[1]);
+            else
+              bw[s][nf] = make_uint2(*reinterpret_cast<const uint32_t*>(bp), 0u);
+          }
 #pragma unroll
           for (int fm = 0; fm < V; ++fm)
             af[s][fm] = *reinterpret_cast<const u32x4*>(As + lo[s] + (wm * WROWS + fm * 32) * ROWB);
@@ -436,9 +471,13 @@ void gg_kernel(const GemmArgs a) {
         for (int s = 0; s < SUB; ++s)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
-            const u32x4 b = widen_i4(bw[s][nf]);
+            u32x4 b;
+            if constexpr (I8)
+              b = widen_i4_i8(bw[s][nf].x, bw[s][nf].y);
+            else
+              b = widen_i4(bw[s][nf].x);
 #pragma unroll
-            for (int fm = 0; fm < V; ++fm) acc[fm][nf] = Mma<false>::run(af[s][fm], b, acc[fm][nf]);
+            for (int fm = 0; fm < V; ++fm) acc[fm][nf] = Mma<I8>::run(af[s][fm], b, acc[fm][nf]);
           }
       } else if constexpr (V > 0) {
         u32x4 af[SUB][V], bfr[SUB][NF];
@@ -763,8 +802,9 @@ constexpr size_t kTailBytes = (size_t)kTailParts * 256 * 256 * 4;
 FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int down_var) {
   uint8_t* wsb = (uint8_t*)ws;
   FfnBufs b{wsb, nullptr, nullptr, nullptr, nullptr};
-  size_t off = align256((size_t)n * I * (w_dtype == kI8 ? 4 : 2));
-  if (w_dtype == kI8) {
+  const bool a8 = w_dtype == kI8 || w_dtype == kI4A8;   // int8 activations: fp32 h, then hq
+  size_t off = align256((size_t)n * I * (a8 ? 4 : 2));
+  if (a8) {
     b.rowmax = (uint32_t*)(wsb + off);
     off += align256((size_t)n * 4);
     b.hq = (int8_t*)(wsb + off);
@@ -866,10 +906,10 @@ hipError_t launch_gg(int var, const GemmArgs& a, hipStream_t s) {
 
 #define MOE_GG4_CASE(IDX, BM, BN, WM, WN, S, R, G) \
   case IDX:                                        \
-    gg_kernel<false, UP, BM, BN, WM, WN, S, R, G, true><<<grid, WM * WN * 64, 0, s>>>(a); \
+    gg_kernel<I8, UP, BM, BN, WM, WN, S, R, G, true><<<grid, WM * WN * 64, 0, s>>>(a); \
     break;
 
-template <bool UP>
+template <bool I8, bool UP>
 hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
   if constexpr (UP) {
@@ -902,46 +942,7 @@ hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
 }
 #undef MOE_GG4_CASE
 
-hipError_t launch_up_w4(const FfnPlan& p, const void* x, const void* w13, const float* s13,
-                        const int32_t* sorted_slot, const int32_t* tiles, const int32_t* num_tiles,
-                        int H, int I, int k, const FfnBufs& b, hipStream_t s) {
-  GemmArgs a{};
-  a.act = (const uint8_t*)x;
-  a.w = (const uint8_t*)w13;
-  a.sorted_slot = sorted_slot;
-  a.tiles = tiles;
-  a.num_tiles = num_tiles;
-  a.wscale = s13;
-  a.out = b.h;
-  a.H = H;
-  a.I = I;
-  a.k = k;
-  a.n_blocks = I / (kUpVarW4[p.up_var].bn / 2);
-  a.max_tiles = (int)p.max_tiles;
-  return launch_gg_w4<true>(p.up_var, a, s);
-}
-
-hipError_t launch_down_w4(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
-                          const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int H,
-                          int I, void* y, const FfnBufs& b, hipStream_t s) {
-  GemmArgs a{};
-  a.act = (const uint8_t*)b.h;
-  a.w = (const uint8_t*)w2;
-  a.sorted_slot = sorted_slot;
-  a.tiles = tiles;
-  a.num_tiles = num_tiles;
-  a.wscale = s2;
-  a.topk_w = topk_w;
-  a.out = y;
-  a.H = H;
-  a.I = I;
-  a.k = 1;
-  a.n_blocks = H / kDownVarW4[p.down_var].bn;
-  a.max_tiles = (int)p.max_tiles;
-  return launch_gg_w4<false>(p.down_var, a, s);
-}
-
-template <bool I8>
+template <bool I8, bool W4>
 hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const void* w13,
                      const float* s13, const int32_t* sorted_slot, const int32_t* tiles,
                      const int32_t* num_tiles, int64_t T, int H, int I, int k, const FfnBufs& b,
@@ -961,12 +962,13 @@ hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const v
   a.H = H;
   a.I = I;
   a.k = k;
-  a.n_blocks = I / (kUpVar[p.up_var].bn / 2);
+  a.n_blocks = I / ((W4 ? kUpVarW4 : kUpVar)[p.up_var].bn / 2);
   a.max_tiles = (int)p.max_tiles;
+  if constexpr (W4) return launch_gg_w4<I8, true>(p.up_var, a, s);
   return launch_gg<I8, true>(p.up_var, a, s);
 }
 
-template <bool I8>
+template <bool I8, bool W4>
 hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const int32_t* sorted_slot,
                        const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int64_t rows,
                        int H, int I, void* y, const FfnBufs& b, hipStream_t s) {
@@ -986,8 +988,9 @@ hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const 
   a.H = H;
   a.I = I;
   a.k = 1;
-  a.n_blocks = H / kDownVar[p.down_var].bn;
+  a.n_blocks = H / ((W4 ? kDownVarW4 : kDownVar)[p.down_var].bn);
   a.max_tiles = (int)p.max_tiles;
+  if constexpr (W4) return launch_gg_w4<I8, false>(p.down_var, a, s);
   a.partial = b.partial;
   a.conc = (p.down_var == 0 && b.partial) ? resident_tiles() : 0;
   hipError_t err = launch_gg<I8, false>(p.down_var, a, s);
@@ -1033,18 +1036,23 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     p.ws_bytes = align256((size_t)n * I * 4);
     snprintf(p.up_name, sizeof p.up_name, "ffn_f32_kernel<up>");
     snprintf(p.down_name, sizeof p.down_name, "ffn_f32_kernel<down>");
-  } else if (w_dtype == kI4) {
+  } else if (w_dtype == kI4 || w_dtype == kI4A8) {
     const double mean_rows = (double)n / E;
     const int cls = mean_rows <= 24.0 ? 2 : (mean_rows <= 192.0 ? 1 : 0);
     p.up_var = (I % 128 == 0 ? 0 : 3) + cls;
     p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 3 : 6)) + cls;
     p.block_m = cls == 2 ? 64 : (cls == 1 ? 128 : 256);
     const Variant u = kUpVarW4[p.up_var], d = kDownVarW4[p.down_var];
-    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<w4a16,up,%dx%d,%dx%d,S%d,R%d,G%d>", u.bm, u.bn, u.wm,
+    const char* t = w_dtype == kI4 ? "w4a16" : "w4a8";
+    snprintf(p.up_name, sizeof p.up_name, "gg_kernel<%s,up,%dx%d,%dx%d,S%d,R%d,G%d>", t, u.bm, u.bn, u.wm,
              u.wn, u.stages, u.rowb, u.gn);
-    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<w4a16,down,%dx%d,%dx%d,S%d,R%d,G%d>", d.bm, d.bn,
+    snprintf(p.down_name, sizeof p.down_name, "gg_kernel<%s,down,%dx%d,%dx%d,S%d,R%d,G%d>", t, d.bm, d.bn,
              d.wm, d.wn, d.stages, d.rowb, d.gn);
-    p.ws_bytes = align256((size_t)n * I * 2);
+    if (w_dtype == kI4)
+      p.ws_bytes = align256((size_t)n * I * 2);
+    else
+      p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
+                   align256((size_t)n * 4);
   } else {
     // shape class from the mean rows per expert: decode-sized (weight
     // streaming, short tiles), mid (one 256-row tile per expert, waves split
@@ -1085,10 +1093,13 @@ hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const
                                                         (float*)b.h);
     return hipGetLastError();
   }
-  if (w_dtype == kI4) return launch_up_w4(p, x, w13, s13, sorted_slot, tiles, num_tiles, H, I, k, b, s);
+  if (w_dtype == kI4)
+    return launch_up<false, true>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
+  if (w_dtype == kI4A8)
+    return launch_up<true, true>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
   if (w_dtype == kBF16)
-    return launch_up<false>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
-  return launch_up<true>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
+    return launch_up<false, false>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
+  return launch_up<true, false>(p, x, xs, w13, s13, sorted_slot, tiles, num_tiles, T, H, I, k, b, s);
 }
 
 hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const float* s2,
@@ -1104,10 +1115,12 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
     return hipGetLastError();
   }
   if (w_dtype == kI4)
-    return launch_down_w4(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, H, I, y, b, s);
+    return launch_down<false, true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
+  if (w_dtype == kI4A8)
+    return launch_down<true, true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
   if (w_dtype == kBF16)
-    return launch_down<false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
-  return launch_down<true>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
+    return launch_down<false, false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
+  return launch_down<true, false>(p, w2, s2, sorted_slot, tiles, num_tiles, topk_w, T * k, H, I, y, b, s);
 }
 
 }  // namespace moe

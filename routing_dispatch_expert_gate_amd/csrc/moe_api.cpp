@@ -122,14 +122,15 @@ moe_status ffn_checks(int32_t act_dtype, int32_t w_dtype, int32_t y_dtype, int64
   const bool ok_combo = (act_dtype == MOE_F32 && w_dtype == MOE_F32 && y_dtype == MOE_F32) ||
                         (act_dtype == MOE_BF16 && w_dtype == MOE_BF16 && y_dtype == MOE_BF16) ||
                         (act_dtype == MOE_I8 && w_dtype == MOE_I8 && y_dtype == MOE_BF16) ||
-                        (act_dtype == MOE_BF16 && w_dtype == MOE_I4 && y_dtype == MOE_BF16);
+                        (act_dtype == MOE_BF16 && w_dtype == MOE_I4 && y_dtype == MOE_BF16) ||
+                        (act_dtype == MOE_I8 && w_dtype == MOE_I4A8 && y_dtype == MOE_BF16);
   if (!ok_combo)
     return fail(MOE_ERR_UNSUPPORTED,
                 "expert FFN dtypes (act %d, w %d, y %d) not implemented: use f32/f32/f32, "
-                "bf16/bf16/bf16, i8/i8/bf16 or bf16/i4/bf16",
+                "bf16/bf16/bf16, i8/i8/bf16, bf16/i4/bf16 or i8/i4a8/bf16",
                 act_dtype, w_dtype, y_dtype);
-  if (w_dtype == MOE_I8 && (H % 128 != 0 || I % 128 != 0))
-    return fail(MOE_ERR_UNSUPPORTED, "W8A8 needs H and I multiples of 128 (got %d, %d)", H, I);
+  if ((w_dtype == MOE_I8 || w_dtype == MOE_I4A8) && (H % 128 != 0 || I % 128 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "W8A8 and W4A8 need H and I multiples of 128 (got %d, %d)", H, I);
   // the GEMM kernels address activations and one expert's weights with
   // 32-bit byte offsets
   const int64_t eb = act_dtype == MOE_F32 ? 4 : (act_dtype == MOE_BF16 ? 2 : 1);
@@ -172,8 +173,9 @@ LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
   c.tiles = take((size_t)c.fp.max_tiles * 16);
   c.num_tiles = take(4);
   c.num_dropped = take(4);
-  c.xq = take(w_dtype == MOE_I8 ? (size_t)T * H : 0);
-  c.xs = take(w_dtype == MOE_I8 ? (size_t)T * 4 : 0);
+  const bool a8 = w_dtype == MOE_I8 || w_dtype == MOE_I4A8;
+  c.xq = take(a8 ? (size_t)T * H : 0);
+  c.xs = take(a8 ? (size_t)T * 4 : 0);
   c.y = take(n * (size_t)H * (w_dtype == MOE_F32 ? 4 : 2));
   size_t scratch = c.rp.ws_bytes;
   if (c.ap.ws_bytes > scratch) scratch = c.ap.ws_bytes;
@@ -305,12 +307,12 @@ moe_status moe_pack_int4(const int8_t* codes, int64_t rows, int32_t K, uint8_t* 
 }
 
 int32_t moe_ffn_block_m(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
-  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_I8 && w_dtype != MOE_I4) return -1;
+  if (w_dtype < MOE_F32 || w_dtype > MOE_I4A8) return -1;
   return moe::plan_ffn(T, H, I, E, k, w_dtype).block_m;
 }
 
 size_t moe_ffn_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t w_dtype) {
-  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_I8 && w_dtype != MOE_I4) return 0;
+  if (w_dtype < MOE_F32 || w_dtype > MOE_I4A8) return 0;
   return moe::plan_ffn(T, H, I, E, k, w_dtype).ws_bytes;
 }
 
@@ -340,8 +342,8 @@ moe_status up_checks(const void* x, const float* xs, const void* w13, int32_t w_
                      const float* s13) {
   MOE_NONNULL(x);
   MOE_NONNULL(w13);
-  if (w_dtype == MOE_I8) MOE_NONNULL(xs);
-  if (w_dtype == MOE_I8 || w_dtype == MOE_I4) MOE_NONNULL(s13);
+  if (w_dtype == MOE_I8 || w_dtype == MOE_I4A8) MOE_NONNULL(xs);
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) MOE_NONNULL(s13);
   MOE_ALIGNED(x, 16);
   MOE_ALIGNED(w13, 16);
   return MOE_OK;
@@ -350,7 +352,7 @@ moe_status up_checks(const void* x, const float* xs, const void* w13, int32_t w_
 moe_status down_checks(const void* w2, int32_t w_dtype, const float* s2, void* y) {
   MOE_NONNULL(w2);
   MOE_NONNULL(y);
-  if (w_dtype == MOE_I8 || w_dtype == MOE_I4) MOE_NONNULL(s2);
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) MOE_NONNULL(s2);
   MOE_ALIGNED(w2, 16);
   MOE_ALIGNED(y, 16);
   return MOE_OK;
@@ -382,8 +384,8 @@ moe_status moe_ffn_down(const void* w2, int32_t w_dtype, const float* s2,
                         int32_t H, int32_t I, int32_t E, int32_t k, void* y_sorted, int32_t y_dtype,
                         void* workspace, size_t workspace_bytes, void* stream) {
   moe::FfnPlan plan;
-  // the activation dtype the up launch used (W4A16: bf16)
-  const int32_t act = w_dtype == MOE_I4 ? MOE_BF16 : w_dtype;
+  // the activation dtype the up launch used (W4A16: bf16, W4A8: int8)
+  const int32_t act = w_dtype == MOE_I4 ? MOE_BF16 : (w_dtype == MOE_I4A8 ? MOE_I8 : w_dtype);
   MOE_TRY(ffn_prologue(act, w_dtype, y_dtype, block_m, T, H, I, E, k, sorted_slot, tiles, num_tiles,
                        workspace, workspace_bytes, &plan));
   if (T == 0) return ok("none (T=0)");
@@ -485,14 +487,14 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
     act = MOE_F32;
   else if (w_dtype == MOE_BF16 && x_dtype == MOE_BF16)
     act = MOE_BF16;
-  else if (w_dtype == MOE_I8)
+  else if (w_dtype == MOE_I8 || w_dtype == MOE_I4A8)
     act = MOE_I8;
   else if (w_dtype == MOE_I4 && x_dtype == MOE_BF16)
     act = MOE_BF16;
   else
     return fail(MOE_ERR_UNSUPPORTED,
-                "layer dtypes (x %d, w %d) not implemented: f32/f32, bf16/bf16, W8A8 (any x, i8 w) or "
-                "W4A16 (bf16 x, i4 w)",
+                "layer dtypes (x %d, w %d) not implemented: f32/f32, bf16/bf16, W8A8 (any x, i8 w), "
+                "W4A16 (bf16 x, i4 w) or W4A8 (any x, i4a8 w)",
                 x_dtype, w_dtype);
   const int32_t ydt = w_dtype == MOE_F32 ? MOE_F32 : MOE_BF16;
   MOE_TRY(ffn_checks(act, w_dtype, ydt, T, H, I, E, k));
@@ -507,7 +509,7 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   MOE_NONNULL(w13);
   MOE_NONNULL(w2);
   MOE_NONNULL(out);
-  if (w_dtype == MOE_I8 || w_dtype == MOE_I4) {
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) {
     MOE_NONNULL(s13);
     MOE_NONNULL(s2);
   }

@@ -21,7 +21,7 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"bf16": 2e-2, "i8": 5e-2, "f32": 1e-4, "i4": 2e-2}
+TOL = {"bf16": 2e-2, "i8": 5e-2, "f32": 1e-4, "i4": 2e-2, "i4a8": 5e-2}
 SAMPLE = {1: None, 2: 192, 3: 24, 4: None, 5: 128}
 
 
@@ -48,7 +48,7 @@ class Case:
         i = self.inp
         self.x, self.wg, self.bias = to_dev(i.x), to_dev(i.wg), to_dev(i.bias)
         self.w13, self.w2, self.s13, self.s2 = to_dev(i.w13), to_dev(i.w2), to_dev(i.s13), to_dev(i.s2)
-        if spec.w_dtype == "i4" and self.w13 is not None:
+        if spec.w_dtype in ("i4", "i4a8") and self.w13 is not None:
             # int4 codes -> the kernels' packed layout (two per byte)
             self.w13, self.w2 = _moe().pack_int4(self.w13), _moe().pack_int4(self.w2)
         s = spec
@@ -336,18 +336,21 @@ def _ffn_combine_case(c, sample):
     the oracle layer on ``sample``."""
     moe = _moe()
     s = c.spec
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8}[s.w_dtype]
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8,
+           "i4a8": "w4a8"}[s.w_dtype]
+    a8 = s.w_dtype in ("i8", "i4a8")
     bm = moe.ffn_block_m(s.T, s.H, s.I, s.E, s.k, wdt)
     ids = to_dev(c.route["ids"])
     w = to_dev(c.route["w"].astype(np.float32))
     a = moe.align(ids, s.E, c.C or 0, bm)
-    if s.w_dtype == "i8":
+    if a8:
         xq, xs = oracle.quant_per_token_int8(moe_synth.bf16_bits_as_f32(c.inp.x))
         act, xs_d = to_dev(xq), to_dev(xs)
     else:
         act, xs_d = c.x, None
+    w4a8 = s.w_dtype == "i4a8"
     y = moe.expert_ffn(act, c.w13, c.w2, a["sorted_slot"], a["tiles"], a["num_tiles"], bm, s.k,
-                       topk_w=w, xs=xs_d, s13=c.s13, s2=c.s2)
+                       topk_w=w, xs=xs_d, s13=c.s13, s2=c.s2, w4a8=w4a8)
     out = moe.combine(y, a["pos"], None, s.T, s.k, torch.float32 if s.out_dtype == "f32" else torch.bfloat16)
     torch.cuda.synchronize()
     print(moe.last_dispatch())
@@ -358,7 +361,7 @@ def _ffn_combine_case(c, sample):
     assert rel <= TOL[s.w_dtype], rel
     # weighted combine path (rows unweighted, weights applied in combine)
     y2 = moe.expert_ffn(act, c.w13, c.w2, a["sorted_slot"], a["tiles"], a["num_tiles"], bm, s.k,
-                        topk_w=None, xs=xs_d, s13=c.s13, s2=c.s2)
+                        topk_w=None, xs=xs_d, s13=c.s13, s2=c.s2, w4a8=w4a8)
     out2 = moe.combine(y2, a["pos"], w, s.T, s.k, torch.float32 if s.out_dtype == "f32" else torch.bfloat16)
     torch.cuda.synchronize()
     rel2 = _rel(out2.float().cpu().numpy().astype(np.float64)[sample], ref["out"])
@@ -397,6 +400,12 @@ SMALL = [
     moe_synth.Spec("i4_mid_E8_T512", 512, 512, 8, 2, 256, w_dtype="i4"),
     moe_synth.Spec("i4_prefill_H384_I192", 1024, 384, 4, 2, 192, w_dtype="i4"),
     moe_synth.Spec("i4_prefill_H320_k1", 800, 320, 4, 1, 128, w_dtype="i4", capacity_factor=1.25),
+    # W4A8: the int8 MFMA path on packed int4 weights (prefill, mid, decode;
+    # BN = 256 and 128; H and I multiples of 128)
+    moe_synth.Spec("i4a8_prefill_E4", 600, 512, 4, 2, 384, w_dtype="i4a8"),
+    moe_synth.Spec("i4a8_mid_H384_cap1", 300, 384, 8, 2, 256, w_dtype="i4a8", capacity_factor=1.0, zipf_s=1.1),
+    moe_synth.Spec("i4a8_decode_E64", 16, 512, 64, 6, 256, w_dtype="i4a8"),
+    moe_synth.Spec("i4a8_decode_H384", 8, 384, 32, 4, 128, w_dtype="i4a8"),
 ]
 
 
@@ -494,6 +503,13 @@ def test_pack_int4_layout():
     np.testing.assert_array_equal(got, (lo | (hi << 4)).astype(np.uint8))
 
 
+def test_w4a8_skewed_workload():
+    """The skewed 16384-token, 64-expert workload with int4 weights and int8
+    activations (W4A8), on a token sample."""
+    spec = moe_synth.CONFIGS[5].replace(name="skewed_w4a8_T16384_H2048_E64_k6_I1408_cap1.25", w_dtype="i4a8")
+    _layer_case(Case(spec, 5000), _sample(spec.T, 96, 13))
+
+
 def test_w4a16_decode_workload():
     """The 16-token, 256-expert, top-8 decode workload with int4 experts."""
     spec = moe_synth.CONFIGS[4].replace(name="decode_w4a16_T16_H4096_E256_k8_I1024", w_dtype="i4")
@@ -514,7 +530,8 @@ def _layer_case(c, sample, check_aux=True):
         "pos": torch.empty((T, k), dtype=torch.int32, device="cuda"),
         "num_dropped": torch.empty(1, dtype=torch.int32, device="cuda"),
     }
-    out = moe.layer(c.x, c.wg, c.w13, c.w2, k, capacity=c.C or 0, bias=c.bias, s13=c.s13, s2=c.s2, aux=aux)
+    out = moe.layer(c.x, c.wg, c.w13, c.w2, k, capacity=c.C or 0, bias=c.bias, s13=c.s13, s2=c.s2, aux=aux,
+                    w4a8=s.w_dtype == "i4a8")
     torch.cuda.synchronize()
     print(moe.last_dispatch())
     ids_g = aux["topk_ids"].cpu().numpy()
