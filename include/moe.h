@@ -150,6 +150,27 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
                      int32_t* num_dropped, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* ------------------------------------------------------ route + align -----
+ * moe_route followed by moe_align, in one launch where one workgroup can
+ * take every token (the route step's own workgroup for E <= 16 and T <= 16;
+ * the top-k workgroup for E > 16 and T <= 64: decode-sized batches), which
+ * then aligns the T*k slots it has just routed (the MoE FlashAttention page's
+ * first fusion, routing fused with grouping by expert, [FA-MoE] "融合一").
+ * Larger batches run the two steps back to back.  Arguments, outputs and
+ * errors are those of moe_route and moe_align (capacity, block_m and the
+ * align outputs as in moe_align); every output equals what the two calls
+ * give.  moe_last_dispatch() says whether the launch was fused.  The
+ * workspace (moe_route_align_workspace_size bytes) serves both steps.
+ * The fused launch saves the host one launch; on the GPU it is no faster
+ * (one workgroup takes every token's top-k), so moe_layer does not use it. */
+size_t moe_route_align_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k);
+moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, const float* bias,
+                           int64_t T, int32_t H, int32_t E, int32_t k, int64_t capacity, int32_t block_m,
+                           int32_t* topk_ids, float* topk_w, float* topk_p, int8_t* xq, float* xs,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* pos, int32_t* tiles,
+                           int32_t* num_tiles, int32_t* num_dropped, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* ---------------------------------------------------------- expert FFN ---
  * Per-expert SwiGLU on the expert-sorted rows as a grouped GEMM pair
  * ([FA-MoE] step 4 and its fused call with stacked expert weights and

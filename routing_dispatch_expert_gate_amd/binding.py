@@ -53,6 +53,9 @@ SIGNATURES = {
     "moe_ffn_down": (_st, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i32, _vp,
                            _i32, _vp, _sz, _vp]),
     "moe_pack_int4": (_st, [_vp, _i64, _i32, _vp, _vp]),
+    "moe_route_align_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
+    "moe_route_align": (_st, [_vp, _i32, _vp, _i32, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, _i32, _vp]),
     "moe_combine_shared": (_st, [_vp, _i32, _vp, _vp, _i64, _i32, _i32, _vp, ctypes.c_float, _vp, _vp,
                                  _i32, _vp]),
@@ -157,6 +160,38 @@ def route(x: torch.Tensor, wg: torch.Tensor, k: int, bias: torch.Tensor | None =
                                      int(n_group), int(topk_group), _p(ids), _p(w), _p(p), _p(xq), _p(xs),
                                      _p(ws), nws, _stream(dev)))
     return {"ids": ids, "w": w, "p": p, "xq": xq, "xs": xs}
+
+
+def route_align(x: torch.Tensor, wg: torch.Tensor, k: int, capacity: int = 0, block_m: int = 128,
+                bias: torch.Tensor | None = None, want_p: bool = True, quant: bool = False) -> dict:
+    """moe_route_align: the outputs of route() and align() from one call."""
+    _dev(x, "x"), _dev(wg, "wg")
+    T, H = x.shape
+    E = wg.shape[0]
+    dev = x.device
+    n = T * k
+    mt = int(lib.moe_align_max_tiles(T, k, E, block_m))
+    i32 = torch.int32
+    o = {
+        "ids": torch.empty((T, k), dtype=i32, device=dev), "w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "p": torch.empty((T, k), dtype=torch.float32, device=dev) if want_p else None,
+        "xq": torch.empty((T, H), dtype=torch.int8, device=dev) if quant else None,
+        "xs": torch.empty((T,), dtype=torch.float32, device=dev) if quant else None,
+        "counts": torch.empty(E, dtype=i32, device=dev), "offsets": torch.empty(E + 1, dtype=i32, device=dev),
+        "sorted_slot": torch.empty(n, dtype=i32, device=dev), "pos": torch.empty((T, k), dtype=i32, device=dev),
+        "tiles": torch.empty((max(mt, 1), 4), dtype=i32, device=dev), "num_tiles": torch.empty(1, dtype=i32, device=dev),
+        "num_dropped": torch.empty(1, dtype=i32, device=dev),
+    }
+    if bias is not None:
+        _dev(bias, "bias")
+    nws = lib.moe_route_align_workspace_size(T, H, E, k)
+    ws = _ws(nws, dev)
+    _check(lib.moe_route_align(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), T, H, E, k, int(capacity),
+                               block_m, _p(o["ids"]), _p(o["w"]), _p(o["p"]), _p(o["xq"]), _p(o["xs"]),
+                               _p(o["counts"]), _p(o["offsets"]), _p(o["sorted_slot"]), _p(o["pos"]),
+                               _p(o["tiles"]), _p(o["num_tiles"]), _p(o["num_dropped"]), _p(ws), nws,
+                               _stream(dev)))
+    return o
 
 
 def align(ids: torch.Tensor, E: int, capacity: int = 0, block_m: int = 128) -> dict:

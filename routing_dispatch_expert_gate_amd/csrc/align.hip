@@ -22,12 +22,12 @@
 //      scan, never from the order atomics return in, so every output is
 //      deterministic.
 // Up to kOneBlockSlots slots the three steps run in one workgroup of sixteen
-// waves instead (align_one_block_kernel): each wave loads a contiguous
-// sixteenth of the ids into registers at once (at most 16 per lane, so one
-// memory latency), counts them in its own LDS histogram, one barrier, the
-// experts' threads scan over waves and over experts, another barrier, and
-// each wave ranks its sixteenth from the same registers as above.  One launch
-// instead of three: at these sizes the launches cost more than the work.
+// waves instead (align_one_block_kernel, block_align.h): each wave loads a
+// contiguous sixteenth of the ids into registers at once, counts them in its
+// own LDS histogram, wave 0 scans, and each wave ranks its sixteenth from the
+// same registers.  One launch instead of three: at these sizes the launches
+// cost more than the work.
+#include "block_align.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -209,118 +209,15 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
 // ------------------------------------------------- one-workgroup variant --
 constexpr int kOneThreads = 1024;
 constexpr int kOneWaves = kOneThreads / 64;
-constexpr int kOneIds = 16;                        // ids per lane
-constexpr int64_t kOneBlockSlots = (int64_t)kOneThreads * kOneIds;
+constexpr int64_t kOneBlockSlots = (int64_t)kOneThreads * kBlockIds;
 
 __global__ __launch_bounds__(kOneThreads) void align_one_block_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int64_t cap, int bm, int64_t max_tiles,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
     int32_t* __restrict__ pos, int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles,
     int32_t* __restrict__ num_dropped) {
-  __shared__ int32_t wh[kOneWaves * kMaxE];   // per-wave counts, then per-wave bases
-  __shared__ int32_t off_s[kMaxE];
-  __shared__ int tmp[kMaxE];
-  __shared__ int tot[2];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int i = tid; i < kOneWaves * kMaxE; i += kOneThreads) wh[i] = 0;
-  __syncthreads();
-  const int64_t sub = ((n + kOneWaves - 1) / kOneWaves + 63) / 64 * 64;
-  const int64_t w0 = (int64_t)wv * sub < n ? (int64_t)wv * sub : n;
-  const int64_t w1 = w0 + sub < n ? w0 + sub : n;
-  int32_t* my = wh + wv * kMaxE;
-  // this lane's ids, slot w0 + 64 j + lane (-1 past the range), all loads in flight at once
-  int idv[kOneIds];
-#pragma unroll
-  for (int j = 0; j < kOneIds; ++j) {
-    const int64_t s = w0 + 64 * j + lane;
-    idv[j] = s < w1 ? ids[s] : -1;
-  }
-#pragma unroll
-  for (int j = 0; j < kOneIds; ++j)
-    if ((unsigned)idv[j] < (unsigned)E) atomicAdd(&my[idv[j]], 1);
-  __syncthreads();
-  // expert e: bases over waves (slot order), total, kept count
-  int kept = 0, ntile = 0;
-  const int e = tid;
-  if (e < kMaxE) {
-    int total = 0;
-    if (e < E) {
-      for (int q = 0; q < kOneWaves; ++q) {
-        const int v = wh[q * kMaxE + e];
-        wh[q * kMaxE + e] = total;
-        total += v;
-      }
-      counts[e] = total;
-      kept = cap > 0 && total > cap ? (int)cap : total;
-      ntile = (kept + bm - 1) / bm;
-    }
-  }
-  // exclusive scans over the experts of kept rows and of row tiles: the
-  // first four waves hold the experts; Hillis-Steele in LDS, packed as
-  // kept | ntile << 20 is not safe for large counts, so two passes
-  int offv = 0, tbase = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int v = pass == 0 ? kept : ntile;
-    if (tid < kMaxE) tmp[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < kMaxE; o <<= 1) {
-      const int add = (tid < kMaxE && tid >= o) ? tmp[tid - o] : 0;
-      __syncthreads();
-      if (tid < kMaxE) tmp[tid] += add;
-      __syncthreads();
-    }
-    if (tid < kMaxE) {
-      if (pass == 0)
-        offv = tmp[tid] - v;
-      else
-        tbase = tmp[tid] - v;
-    }
-    if (tid == kMaxE - 1) tot[pass] = tmp[tid];
-    __syncthreads();
-  }
-  const int n_kept = tot[0], n_tiles = tot[1];
-  if (e < E) {
-    offsets[e] = offv;
-    off_s[e] = offv;
-    for (int i = 0; i < ntile; ++i) {
-      const int r = kept - i * bm < bm ? kept - i * bm : bm;
-      *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tbase + i)) = make_int4(e, offv + i * bm, r, 0);
-    }
-  }
-  if (tid == 0) {
-    offsets[E] = n_kept;
-    *num_dropped = (int32_t)(n - n_kept);
-    *num_tiles = n_tiles;
-  }
-  for (int64_t q = n_tiles + tid; q < max_tiles; q += kOneThreads)
-    *reinterpret_cast<int4*>(tiles + 4 * q) = make_int4(-1, 0, 0, 0);
-  __syncthreads();
-  // rank this wave's slots in slot order
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-#pragma unroll
-  for (int j = 0; j < kOneIds; ++j) {
-    if (w0 + 64 * j >= w1) break;                   // uniform
-    const int64_t s = w0 + 64 * j + lane;
-    const bool in_range = s < w1;
-    const int ex = idv[j];
-    const bool valid = in_range && (unsigned)ex < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < ebits; ++b) {
-      const bool bit = (ex >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      same &= bit ? m : ~m;
-    }
-    int rank = 0;
-    if (valid) rank = my[ex] + __popcll(same & lt);
-    if (valid && (same & lt) == 0) my[ex] += __popcll(same);
-    if (in_range) {
-      const bool keep = valid && (cap <= 0 || rank < cap);
-      const int p = keep ? off_s[ex] + rank : -1;
-      pos[s] = p;
-      if (keep) sorted_slot[p] = (int32_t)s;
-    }
-  }
-  for (int64_t i = n_kept + tid; i < n; i += kOneThreads) sorted_slot[i] = -1;
+  block_align<kOneWaves>([&](int64_t s) { return ids[s]; }, n, E, ebits, cap, bm, max_tiles, counts, offsets,
+                         sorted_slot, pos, tiles, num_tiles, num_dropped);
 }
 
 }  // namespace

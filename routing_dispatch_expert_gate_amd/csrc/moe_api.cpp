@@ -293,6 +293,53 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, i
   return ok(b);
 }
 
+size_t moe_route_align_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k) {
+  // the two steps run one after the other and share the workspace
+  const size_t r = moe_route_workspace_size(T, H, E, k), a = moe_align_workspace_size(T, k, E);
+  return r > a ? r : a;
+}
+
+moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, const float* bias,
+                           int64_t T, int32_t H, int32_t E, int32_t k, int64_t capacity, int32_t block_m,
+                           int32_t* topk_ids, float* topk_w, float* topk_p, int8_t* xq, float* xs,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_slot, int32_t* pos, int32_t* tiles,
+                           int32_t* num_tiles, int32_t* num_dropped, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  moe::RoutePlan plan;
+  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, topk_ids, topk_w, xq, xs, &plan));
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_INVALID_ARG, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
+  if (T == 0) return ok("none (T=0)");
+  MOE_NONNULL(counts);
+  MOE_NONNULL(offsets);
+  MOE_NONNULL(sorted_slot);
+  MOE_NONNULL(pos);
+  MOE_NONNULL(tiles);
+  MOE_NONNULL(num_tiles);
+  MOE_NONNULL(num_dropped);
+  MOE_ALIGNED(tiles, 16);
+  MOE_TRY(check_ws(workspace, workspace_bytes, moe_route_align_workspace_size(T, H, E, k)));
+  const int64_t mt = moe::align_max_tiles(T, k, E, block_m);
+  const int64_t cap = capacity > 0 ? capacity : 0;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (moe::route_align_fusable(plan, T, k)) {
+    e = moe::launch_route_align_fused(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p,
+                                      xq, xs, workspace, cap, block_m, mt, counts, offsets, sorted_slot, pos,
+                                      tiles, num_tiles, num_dropped, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_align launch");
+    return ok(route_name(plan) + "+align (one launch)");
+  }
+  e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p, xq, xs,
+                        workspace, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_align route launch");
+  const moe::AlignPlan ap = moe::plan_align(T, k, E);
+  e = moe::launch_align(ap, topk_ids, T, k, E, cap, block_m, mt, counts, offsets, sorted_slot, pos, tiles,
+                        num_tiles, num_dropped, workspace, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_route_align align launch");
+  return ok(route_name(plan) + " | align");
+}
+
 moe_status moe_pack_int4(const int8_t* codes, int64_t rows, int32_t K, uint8_t* packed, void* stream) {
   if (rows < 0) return fail(MOE_ERR_INVALID_ARG, "rows must be >= 0 (got %lld)", (long long)rows);
   if (K < 1 || K % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "K must be a positive multiple of 64 (got %d)", K);
@@ -542,13 +589,24 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   void* scratch = base + c.scratch;
   hipStream_t s = (hipStream_t)stream;
 
-  hipError_t e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq,
-                                   xs, scratch, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
-  e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m,
-                        c.fp.max_tiles, counts, offsets, sorted_slot, pos, tiles, num_tiles,
-                        num_dropped, scratch, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
+  // the fused route + align (moe_route_align) saves a launch but puts every
+  // token's top-k on one workgroup: measured ~2 us slower on the GPU at
+  // decode than route_topk's four workgroups plus the align launch, so the
+  // layer, which runs GPU-bound, keeps the two launches
+  const bool fused = false;
+  hipError_t e;
+  if (fused) {
+    e = moe::launch_route_align_fused(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch,
+                                      capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts, offsets,
+                                      sorted_slot, pos, tiles, num_tiles, num_dropped, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer route+align launch");
+  } else {
+    e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
+    e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts,
+                          offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, scratch, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
+  }
   e = moe::launch_ffn_up(c.fp, act == MOE_I8 ? (const void*)xq : x, xs, w13, w_dtype, s13,
                          sorted_slot, tiles, num_tiles, T, H, I, k, scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn up launch");
@@ -557,8 +615,9 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn down launch");
   e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
-  return ok(route_name(c.rp) + " | " + (c.ap.nblocks == 0 ? std::string("align(one block)")
-                                         : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
+  return ok(route_name(c.rp) + " | " + (fused ? std::string("align(fused into route)")
+                                : c.ap.nblocks == 0 ? std::string("align(one block)")
+                                                    : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
             c.fp.up_name + "+" + c.fp.down_name + "(block_m=" + std::to_string(c.fp.block_m) +
             ") | combine_kernel<pre-weighted>");
 }

@@ -157,6 +157,15 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype);
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                         const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
                         float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s);
+// route and align in one launch where one workgroup can take every token
+// (route_align_fusable): the align outputs as in launch_align
+bool route_align_fusable(const RoutePlan& p, int64_t T, int k);
+hipError_t launch_route_align_fused(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
+                                    const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
+                                    float* prob, int8_t* xq, float* xs, void* ws, int64_t cap, int block_m,
+                                    int64_t max_tiles, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                    int32_t* pos, int32_t* tiles, int32_t* num_tiles, int32_t* num_dropped,
+                                    hipStream_t s);
 // group-limited variant (kind 2 plans only): n_group contiguous groups,
 // the topk_group best by their two largest probabilities
 hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* wg, const float* bias,

@@ -26,6 +26,7 @@
 //           selection, serves the group-limited router.
 #include <math.h>
 
+#include "block_align.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -284,11 +285,11 @@ struct Raw8<float> {
 // A workgroup's token rows are loaded in batches of PF rows, each batch before
 // its first FMA; each token's E partial logits are reduced over the wave by
 // wave_reduce_quads.
-template <int EP, bool WIDE, typename XT, typename WT, bool QUANT>
+template <int EP, bool WIDE, typename XT, typename WT, bool QUANT, bool ALIGN>
 __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
-    float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs) {
+    float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs, const AlignArgs al) {
   // rows per load batch (all sixteen at once costs occupancy: measured
   // slower at large T)
   constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);
@@ -395,6 +396,12 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
         if (threadIdx.x == 0) xs[t0 + tt] = s;
       }
     }
+  }
+  if constexpr (ALIGN) {
+    // a single workgroup routed every token: align its T*k slots here
+    __syncthreads();
+    block_align<16>([&](int64_t sl) { return ids[sl]; }, T * k, E, al.ebits, al.cap, al.bm, al.max_tiles,
+                    al.counts, al.offsets, al.sorted_slot, al.pos, al.tiles, al.num_tiles, al.num_dropped);
   }
 }
 
@@ -528,17 +535,16 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
 // splits' loads in flight), adds the bias, selects the top-k (by rank from an
 // LDS row when E <= 64, else by argmax rounds) and, with quantisation, writes
 // the token's codes with the absmax the logits kernel folded.
+// One wave: the top-k (and, with quantisation, the int8 codes) of token t.
+// lrow: this wave's 64-float LDS row; grow/gscore: its 256- and 64-float rows
+// for the group-limited selection.
 template <bool QUANT, bool GROUPED>
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
-    const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
-    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
-    float* __restrict__ xs, int n_group, int topk_group) {
-  __shared__ __attribute__((aligned(16))) float lrow[4][64];
+__device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
+                           const float* __restrict__ bias, int64_t T, int E, int k, int H,
+                           const uint16_t* __restrict__ x, int32_t* __restrict__ ids, float* __restrict__ w,
+                           float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs,
+                           int n_group, int topk_group, float* lrow, float* grow, float* gscore) {
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
-  if (t >= T) return;
   float v[4] = {0.f, 0.f, 0.f, 0.f};
   for (int z0 = 0; z0 < ks; z0 += 8) {
     float q[4][8];
@@ -559,13 +565,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : -INFINITY;
   }
   if constexpr (GROUPED) {
-    __shared__ __attribute__((aligned(16))) float grow[4][256];
-    __shared__ float gscore[4][64];
-    wave_grouped_topk_store(v, grow[wv], gscore[wv], E, k, n_group, topk_group, t, ids, w, prob);
+    wave_grouped_topk_store(v, grow, gscore, E, k, n_group, topk_group, t, ids, w, prob);
   } else if (E <= 64) {
-    lrow[wv][lane] = v[0];
+    lrow[lane] = v[0];
     __builtin_amdgcn_wave_barrier();
-    wave_topk_rank_store(lrow[wv], E, k, t, ids, w, prob);
+    wave_topk_rank_store(lrow, E, k, t, ids, w, prob);
   } else {
     wave_topk_store(v, E, k, t, ids, w, prob);
   }
@@ -590,38 +594,90 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
+template <bool QUANT, bool GROUPED>
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
+    const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
+    float* __restrict__ xs, int n_group, int topk_group) {
+  __shared__ __attribute__((aligned(16))) float lrow[4][64];
+  __shared__ __attribute__((aligned(16))) float grow[GROUPED ? 4 : 1][256];
+  __shared__ float gscore[GROUPED ? 4 : 1][64];
+  const int wv = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  topk_token<QUANT, GROUPED>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob, xq, xs, n_group,
+                             topk_group, lrow[wv], grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+}
+
+// Route and align fused for small batches (T <= kFusedTopkT): one workgroup
+// of sixteen waves takes the tokens' top-k in turn, then the same workgroup
+// aligns the T*k slots (block_align.h), reading back the ids its own waves
+// wrote (visible after the barrier).  One launch instead of two.
+constexpr int kFusedTopkT = 64;
+
+template <bool QUANT, bool GROUPED>
+__global__ __launch_bounds__(1024) void route_topk_align_kernel(
+    const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
+    const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
+    float* __restrict__ xs, int n_group, int topk_group, const AlignArgs al) {
+  __shared__ __attribute__((aligned(16))) float lrow[16][64];
+  __shared__ __attribute__((aligned(16))) float grow[GROUPED ? 16 : 1][256];
+  __shared__ float gscore[GROUPED ? 16 : 1][64];
+  const int wv = threadIdx.x >> 6;
+  for (int64_t t = wv; t < T; t += 16)
+    topk_token<QUANT, GROUPED>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob, xq, xs, n_group,
+                               topk_group, lrow[wv], grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+  __syncthreads();
+  block_align<16>([&](int64_t s) { return ids[s]; }, T * k, E, al.ebits, al.cap, al.bm, al.max_tiles, al.counts,
+                  al.offsets, al.sorted_slot, al.pos, al.tiles, al.num_tiles, al.num_dropped);
+}
+
 template <int EP, bool WIDE, typename XT, typename WT>
 hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                       int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
-                      int8_t* xq, float* xs, hipStream_t s) {
+                      int8_t* xq, float* xs, const AlignArgs* al, hipStream_t s) {
   const dim3 grid((unsigned)((T + kFmaTB - 1) / kFmaTB));
   const dim3 block(64 * p.nw);
-  if (xq)
-    route_fma_kernel<EP, WIDE, XT, WT, true><<<grid, block, 0, s>>>(
-        (const XT*)x, (const WT*)wg, bias, T, H, E, k, ids, w, prob, xq, xs);
-  else
-    route_fma_kernel<EP, WIDE, XT, WT, false><<<grid, block, 0, s>>>(
-        (const XT*)x, (const WT*)wg, bias, T, H, E, k, ids, w, prob, xq, xs);
+  const AlignArgs none{};
+#define MOE_FMA(Q, A)                                                                        \
+  route_fma_kernel<EP, WIDE, XT, WT, Q, A><<<grid, block, 0, s>>>((const XT*)x, (const WT*)wg, bias, \
+                                                                  T, H, E, k, ids, w, prob, xq, xs,   \
+                                                                  al ? *al : none)
+  if (al) {
+    if (xq)
+      MOE_FMA(true, true);
+    else
+      MOE_FMA(false, true);
+  } else {
+    if (xq)
+      MOE_FMA(true, false);
+    else
+      MOE_FMA(false, false);
+  }
+#undef MOE_FMA
   return hipGetLastError();
 }
 
 template <int EP, bool WIDE>
 hipError_t launch_fma_dt(const RoutePlan& p, const void* x, int xd, const void* wg, int wd,
                          const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
-                         float* prob, int8_t* xq, float* xs, hipStream_t s) {
+                         float* prob, int8_t* xq, float* xs, const AlignArgs* al, hipStream_t s) {
   if (xd == kF32 && wd == kF32)
-    return launch_fma<EP, WIDE, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
   if (xd == kF32 && wd == kBF16)
-    return launch_fma<EP, WIDE, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
   if (xd == kBF16 && wd == kF32)
-    return launch_fma<EP, WIDE, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-  return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    return launch_fma<EP, WIDE, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+  return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
 }
 
 template <bool GROUPED>
 hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                        int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
-                       int8_t* xq, float* xs, void* ws, int n_group, int topk_group, hipStream_t s) {
+                       int8_t* xq, float* xs, void* ws, int n_group, int topk_group, const AlignArgs* al,
+                       hipStream_t s) {
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)wg;
   float* part = (float*)ws;
@@ -633,6 +689,15 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
     route_gemm_kernel<false><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (al) {
+    if (xq)
+      route_topk_align_kernel<true, GROUPED><<<1, 1024, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
+                                                                prob, xq, xs, n_group, topk_group, *al);
+    else
+      route_topk_align_kernel<false, GROUPED><<<1, 1024, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids,
+                                                                 w, prob, xq, xs, n_group, topk_group, *al);
+    return hipGetLastError();
+  }
   const dim3 g2((unsigned)((T + 3) / 4));
   if (xq)
     route_topk_kernel<true, GROUPED><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
@@ -669,21 +734,47 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
   return p;
 }
 
+namespace {
+hipError_t route_any(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
+                     const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
+                     int8_t* xq, float* xs, void* ws, const AlignArgs* al, hipStream_t s) {
+  if (p.kind == 0) {
+    if (E <= 8 && p.nw > 8)
+      return launch_fma_dt<8, true>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+    if (E <= 8)
+      return launch_fma_dt<8, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+    return launch_fma_dt<16, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+  }
+  return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, al, s);
+}
+}  // namespace
+
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg,
                         int wg_dtype, const float* bias, int64_t T, int H, int E, int k,
                         int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
                         hipStream_t s) {
-  if (p.kind == 0) {
-    if (E <= 8 && p.nw > 8)
-      return launch_fma_dt<8, true>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
-                                    xs, s);
-    if (E <= 8)
-      return launch_fma_dt<8, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
-                                 xs, s);
-    return launch_fma_dt<16, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq,
-                                xs, s);
-  }
-  return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, s);
+  return route_any(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, ws, nullptr, s);
+}
+
+bool route_align_fusable(const RoutePlan& p, int64_t T, int k) {
+  // kind 0: one workgroup routes every token; kind 2: one workgroup takes
+  // every token's top-k.  Either then aligns the T*k slots itself.
+  if (p.kind == 0) return T <= kFmaTB && T * k <= (int64_t)p.nw * 64 * kBlockIds;
+  return T <= kFusedTopkT;
+}
+
+hipError_t launch_route_align_fused(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
+                                    const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
+                                    float* prob, int8_t* xq, float* xs, void* ws, int64_t cap, int block_m,
+                                    int64_t max_tiles, int32_t* counts, int32_t* offsets, int32_t* sorted_slot,
+                                    int32_t* pos, int32_t* tiles, int32_t* num_tiles, int32_t* num_dropped,
+                                    hipStream_t s) {
+  if (!route_align_fusable(p, T, k)) return hipErrorInvalidValue;
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  const AlignArgs al{cap, block_m, ebits, max_tiles, counts, offsets, sorted_slot, pos, tiles, num_tiles,
+                     num_dropped};
+  return route_any(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, ws, &al, s);
 }
 
 hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* wg, const float* bias,
@@ -691,7 +782,8 @@ hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* w
                                 int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
                                 hipStream_t s) {
   if (p.kind != 2) return hipErrorInvalidValue;
-  return launch_mfma<true>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, n_group, topk_group, s);
+  return launch_mfma<true>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, n_group, topk_group, nullptr,
+                           s);
 }
 
 }  // namespace moe

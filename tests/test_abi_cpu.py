@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -107,6 +107,23 @@ def test_route_grouped_validation(moe):
     assert rg() == WORKSPACE
     assert rg(T=0) == OK
     assert L.moe_route_workspace_size(64, 512, 256, 8) > 0
+
+
+def test_route_align_validation(moe):
+    L = moe.lib
+
+    def ra(T=16, E=256, k=8, bm=64, H=512, o=P, ws=None, nws=0, wd=BF16):
+        return L.moe_route_align(P, BF16, P, wd, None, T, H, E, k, 0, bm, P, P, None, None, None, o, o, o, o, o, o, o,
+                                 ws, nws, None)
+
+    assert ra(bm=100) == INVALID
+    assert ra(o=None) == INVALID
+    assert ra(k=9) == UNSUPPORTED
+    assert ra(wd=F32) == UNSUPPORTED           # E > 16 needs bf16 wg
+    assert ra() == WORKSPACE                   # the logits workspace
+    assert ra(T=0) == OK
+    assert L.moe_route_align_workspace_size(16, 512, 256, 8) >= L.moe_route_workspace_size(16, 512, 256, 8)
+    assert L.moe_route_align_workspace_size(4096, 512, 8, 8) >= L.moe_align_workspace_size(4096, 8, 8) > 0
 
 
 def test_pack_int4_and_w4a16_validation(moe):

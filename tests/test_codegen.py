@@ -68,3 +68,26 @@ def test_gemm_variants_do_not_spill(asm):
                 m = re.search(re.escape(key) + r": (\d+)", line)
                 if m:
                     assert int(m.group(1)) == 0, f"{cur}: {key} = {m.group(1)}"
+
+
+@pytest.mark.parametrize("src", ["route.hip", "align.hip", "combine.hip"])
+def test_small_kernels_use_no_scratch(src, tmp_path):
+    """Route, align and combine kernels keep everything in registers and LDS:
+    a device function left out of line (a call) spills to scratch."""
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-fhip-fp32-correctly-rounded-divide-sqrt", "-x", "hip",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-c", os.path.join(CSRC, src), "--cuda-device-only",
+           "-o", str(tmp_path / "k.o"), "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    cur = None
+    seen = 0
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            cur = m.group(1)
+            seen += 1
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m:
+            assert int(m.group(1)) == 0, f"{cur} uses scratch"
+    assert seen > 0

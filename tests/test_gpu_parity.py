@@ -249,6 +249,50 @@ def test_route_grouped_all_groups_equals_plain_route():
     assert torch.equal(a["w"], b["w"]) and torch.equal(a["p"], b["p"])
 
 
+# ---------------------------------------------------------- route + align
+ROUTE_ALIGN = [
+    # spec, capacity, block_m, quant, fused
+    (moe_synth.Spec("ra_e256_T16", 16, 4096, 256, 8, 64), 0, 64, True, True),
+    (moe_synth.Spec("ra_e64_T64_cap", 64, 1024, 64, 6, 64, zipf_s=1.1), 7, 64, False, True),
+    (moe_synth.Spec("ra_e32_T1", 1, 256, 32, 4, 64), 0, 16, True, True),
+    (moe_synth.Spec("ra_e8_T16_f32wg", 16, 4096, 8, 2, 64, wg_dtype="f32"), 0, 64, False, True),
+    (moe_synth.Spec("ra_e16_T10_cap", 10, 256, 16, 4, 64, x_dtype="f32", wg_dtype="f32"), 2, 32, True, True),
+    (moe_synth.Spec("ra_e64_T300", 300, 512, 64, 6, 64), 30, 128, False, False),
+    (moe_synth.Spec("ra_e8_T100", 100, 512, 8, 2, 64), 0, 256, True, False),
+]
+
+
+@pytest.mark.parametrize("spec,C,bm,quant,fused", ROUTE_ALIGN, ids=[r[0].name for r in ROUTE_ALIGN])
+def test_route_align_equals_route_then_align(spec, C, bm, quant, fused):
+    """moe_route_align gives exactly the outputs of moe_route followed by
+    moe_align (one launch where one workgroup takes every token), and those
+    match the oracle."""
+    moe = _moe()
+    i = moe_synth.make_inputs(spec, 31, with_experts=False)
+    x, wg, b = to_dev(i.x), to_dev(i.wg), to_dev(i.bias)
+    ra = moe.route_align(x, wg, spec.k, capacity=C, block_m=bm, bias=b, want_p=True, quant=quant)
+    torch.cuda.synchronize()
+    d = moe.last_dispatch()
+    print(d)
+    assert ("(one launch)" in d) == fused, d
+    r = moe.route(x, wg, spec.k, bias=b, want_p=True, quant=quant)
+    a = moe.align(r["ids"], spec.E, C, bm)
+    torch.cuda.synchronize()
+    for key in ("ids", "w", "p") + (("xq", "xs") if quant else ()):
+        assert torch.equal(ra[key], r[key]), key
+    nt = int(a["num_tiles"].item())
+    assert int(ra["num_tiles"].item()) == nt
+    for key in ("counts", "offsets", "sorted_slot", "pos", "num_dropped"):
+        assert torch.equal(ra[key], a[key]), key
+    assert torch.equal(ra["tiles"][:nt], a["tiles"][:nt]) and (ra["tiles"][nt:, 0] == -1).all()
+    ro = oracle.route(oracle.to_f64(i.x, spec.x_dtype), oracle.to_f64(i.wg, spec.wg_dtype), spec.k, i.bias)
+    check_ids(ra["ids"].cpu().numpy(), ro)
+    al = oracle.align(ra["ids"].cpu().numpy(), spec.E, C or None)
+    np.testing.assert_array_equal(ra["pos"].cpu().numpy(), al["pos"])
+    np.testing.assert_array_equal(ra["sorted_slot"].cpu().numpy(), al["sorted_slot"])
+    np.testing.assert_array_equal(ra["offsets"].cpu().numpy(), al["offsets"])
+
+
 # ------------------------------------------------------------------ align
 def _check_align(ids, E, C, bm):
     moe = _moe()
