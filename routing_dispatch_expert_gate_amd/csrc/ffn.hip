@@ -100,6 +100,16 @@ __device__ __forceinline__ u32x4 widen_i4(uint32_t w) {
   return r;
 }
 
+// Packed int4 B rows in LDS (32 bytes per stage row for bf16 activations, 64
+// for int8) hold 2 or 4 16-byte chunks; chunk c of row r is stored at
+// c ^ swz4(r), so that the sixteen rows a 16-lane pass reads at one logical
+// chunk fall on sixteen distinct 16-byte slots of a 256-byte bank row.
+template <bool I8>
+__device__ __forceinline__ int swz4(int r) {
+  if constexpr (I8) return (r >> 2) & 3;
+  return (r >> 3) & 1;
+}
+
 // Sixteen int4 codes (8 bytes, as above) to sixteen int8 values in K order.
 __device__ __forceinline__ uint32_t sext_nibble_bytes(uint32_t u) {
   // bytes hold 4-bit two's complement values; 8 * 0x1E = 0xF0 stays in its byte
@@ -347,7 +357,7 @@ void gg_kernel(const GemmArgs a) {
     for (int j = 0; j < NG - LA; ++j) {
       const int qb = wv + NW * j;                      // B block (may not exist)
       const int trow = (qb < BBLK ? qb : 0) * RPBB + lane / CPRB;
-      goff[LA + j] = b_row(trow) * (uint32_t)kbytes_b + (lane % CPRB) * 16;
+      goff[LA + j] = b_row(trow) * (uint32_t)kbytes_b + ((lane % CPRB) ^ swz4<I8>(trow)) * 16;
     }
   } else {
 #pragma unroll
@@ -423,10 +433,17 @@ void gg_kernel(const GemmArgs a) {
   };
   // fragment rows start at multiples of 32 (the swizzle period), so a lane's
   // address within a fragment depends on the lane and the substep only
+  // The MFMA's K slots may be fed in any order that A and B share.  bf16 and
+  // int8 tiles: substep s, lane half h takes 16-byte chunk 2s + h of the stage
+  // row.  Packed int4 B (W4): half h takes the contiguous half [h/2, (h+1)/2)
+  // of the stage's K and substep s its s-th quarter, i.e. A chunk 4h + s, so
+  // a lane's packed codes for all substeps are one (bf16) or two (int8)
+  // contiguous 16-byte chunks.
+  static_assert(!W4 || (ROWB == 128 && SUB == 4), "W4 tiles use 128-byte A rows");
   int lo[SUB];
 #pragma unroll
   for (int s = 0; s < SUB; ++s) {
-    const int r = lane & 31, c = 2 * s + (lane >> 5);
+    const int r = lane & 31, c = W4 ? 4 * (lane >> 5) + s : 2 * s + (lane >> 5);
     lo[s] = r * ROWB + ((c ^ swr<ROWB>(r)) << 4);
   }
 
@@ -444,38 +461,37 @@ void gg_kernel(const GemmArgs a) {
       const uint8_t* As = smem + (kt % S) * STAGE;
       const uint8_t* Bs = As + BM * ROWB;
       if constexpr (V > 0 && W4) {
-        // packed B: the lane's codes of row (lane % 32), k-chunk
-        // 2s + lane / 32 (eight for bf16, sixteen for int8), read as 32-bit
-        // LDS words and widened in registers.  (Read as one 64-bit word, the
-        // int8 case is merged with the next substep's read into a form after
-        // which the compiler drains every in-flight copy.)
-        constexpr int CB = I8 ? 8 : 4;                 // packed bytes per lane per substep
+        // packed B: row (lane % 32), lane half h's codes for all four
+        // substeps, one (bf16: 4 bytes per substep) or two (int8: 8 bytes)
+        // 16-byte chunks, widened in registers per substep
+        constexpr int NCH = I8 ? 2 : 1;
+        const int h = lane >> 5, sw = swz4<I8>(lane & 31);
         u32x4 af[SUB][V];
-        uint2 bw[SUB][NF];
+        u32x4 bq[NF][NCH];
 #pragma unroll
-        for (int s = 0; s < SUB; ++s) {
+        for (int nf = 0; nf < NF; ++nf)
 #pragma unroll
-          for (int nf = 0; nf < NF; ++nf) {
-            const uint8_t* bp = Bs + (brow_of(nf) + (lane & 31)) * BROWB + CB * (2 * s + (lane >> 5));
-            if constexpr (I8)
-              bw[s][nf] = make_uint2(reinterpret_cast<const uint32_t*>(bp)[0],
-                                     reinterpret_cast<const uint32_t*>(bp)[1]);
-            else
-              bw[s][nf] = make_uint2(*reinterpret_cast<const uint32_t*>(bp), 0u);
-          }
+          for (int j = 0; j < NCH; ++j)
+            bq[nf][j] = *reinterpret_cast<const u32x4*>(Bs + (brow_of(nf) + (lane & 31)) * BROWB +
+                                                        16 * ((NCH * h + j) ^ sw));
+#pragma unroll
+        for (int s = 0; s < SUB; ++s)
 #pragma unroll
           for (int fm = 0; fm < V; ++fm)
             af[s][fm] = *reinterpret_cast<const u32x4*>(As + lo[s] + (wm * WROWS + fm * 32) * ROWB);
-        }
 #pragma unroll
         for (int s = 0; s < SUB; ++s)
 #pragma unroll
           for (int nf = 0; nf < NF; ++nf) {
             u32x4 b;
-            if constexpr (I8)
-              b = widen_i4_i8(bw[s][nf].x, bw[s][nf].y);
-            else
-              b = widen_i4(bw[s][nf].x);
+            if constexpr (I8) {
+              const u32x4 q = bq[nf][s >> 1];
+              const uint32_t w0 = (s & 1) ? q[2] : q[0], w1 = (s & 1) ? q[3] : q[1];
+              b = widen_i4_i8(w0, w1);
+            } else {
+              const u32x4 q = bq[nf][0];
+              b = widen_i4(q[s]);
+            }
 #pragma unroll
             for (int fm = 0; fm < V; ++fm) acc[fm][nf] = Mma<I8>::run(af[s][fm], b, acc[fm][nf]);
           }
