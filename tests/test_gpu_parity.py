@@ -626,6 +626,56 @@ def test_layer_is_deterministic_and_permutation_equivariant():
     assert _rel(p.float().cpu().numpy(), a[perm].float().cpu().numpy()) < 1e-2
 
 
+GRAPH_CASES = [
+    moe_synth.Spec("graph_bf16_E64_cap", 300, 512, 64, 6, 256, capacity_factor=1.0),
+    moe_synth.Spec("graph_w8a8_E16", 257, 256, 16, 2, 256, w_dtype="i8", capacity_factor=1.25),
+    moe_synth.Spec("graph_w4a8_decode", 16, 512, 64, 6, 256, w_dtype="i4a8"),
+]
+
+
+@pytest.mark.parametrize("spec", GRAPH_CASES, ids=[s.name for s in GRAPH_CASES])
+def test_layer_replays_from_a_hip_graph(spec):
+    """moe_layer allocates nothing and enqueues only kernels, so a captured
+    graph of it replays the eager result bit for bit, replay after replay,
+    with other eager work (another layer call on other inputs) in between."""
+    moe = _moe()
+    c = Case(spec, 2024)
+    other = Case(spec.replace(name=spec.name + "_other"), 2025)
+    w4a8 = spec.w_dtype == "i4a8"
+    L = moe.Layer(spec.T, spec.H, spec.I, spec.E, spec.k, c.x.dtype, "w4a8" if w4a8 else c.w13.dtype)
+    out = torch.empty((spec.T, spec.H), dtype=c.x.dtype, device="cuda")
+    C = c.C or 0
+
+    def call(case, dst):
+        L(case.x, case.wg, case.w13, case.w2, C, case.bias, case.s13, case.s2, out=dst)
+
+    ref = torch.empty_like(out)
+    call(c, ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(c, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(c, out)
+    scratch = torch.empty_like(out)
+    for i in range(3):
+        out.zero_()
+        call(other, scratch)            # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref), f"replay {i}"
+    ref_other = moe.layer(other.x, other.wg, other.w13, other.w2, spec.k, capacity=C, bias=other.bias,
+                          s13=other.s13, s2=other.s2, w4a8=w4a8)
+    torch.cuda.synchronize()
+    assert torch.equal(scratch, ref_other)
+
+
 def test_empty_batch_is_a_noop():
     moe = _moe()
     x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
