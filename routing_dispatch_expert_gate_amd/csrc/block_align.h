@@ -84,15 +84,7 @@ __device__ void block_align(LoadId load_id, int64_t n, int E, int ebits, int64_t
         kept = cap > 0 && total > cap ? (int)cap : total;
         ntile = (kept + bm - 1) / bm;
       }
-      int ik = kept, it = ntile;   // inclusive scans over the 64 lanes
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(ik, o, kWave), b = __shfl_up(it, o, kWave);
-        if (lane >= o) {
-          ik += a;
-          it += b;
-        }
-      }
+      const int ik = wave_incl_scan(kept), it = wave_incl_scan(ntile);   // inclusive, over the 64 lanes
       const int offv = run_k + ik - kept, tbase = run_t + it - ntile;
       if (e < E) {
         offsets[e] = offv;
@@ -102,8 +94,8 @@ __device__ void block_align(LoadId load_id, int64_t n, int E, int ebits, int64_t
           *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tbase + i)) = make_int4(e, offv + i * bm, r, 0);
         }
       }
-      run_k += __shfl(ik, 63, kWave);
-      run_t += __shfl(it, 63, kWave);
+      run_k += __builtin_amdgcn_readlane(ik, 63);
+      run_t += __builtin_amdgcn_readlane(it, 63);
     }
     if (lane == 0) {
       offsets[E] = run_k;

@@ -626,8 +626,8 @@ void gg_kernel(const GemmArgs a) {
           if (valid) h[(int64_t)(r0 + row) * a.I + col] = hv;
           m = fmaxf(m, fabsf(hv));
         }
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        m = row_max16(m);                              // 16 lanes by DPP,
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));        // then the other row of the half
         if (valid && (lane & 31) == 0) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
       }
     }

@@ -77,15 +77,55 @@ __device__ __forceinline__ int quant_code(float x, float s, float rs) {
 }
 
 // ------------------------------------------------------------- wave utils
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// 64-lane reductions without LDS round trips: DPP inside each row of 16 lanes
+// (two butterfly steps inside quads, then rotations by 4 and 8 lanes, after
+// which lanes 0, 16, 32 and 48 hold their row's result), then four readlanes.
+// The result is wave-uniform and the same on every lane; the sum's
+// association order is fixed, so it is deterministic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:4, row_ror:8
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x124>(v);
+  return v + dpp_f32<0x128>(v);
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x124>(v));
+  return fmaxf(v, dpp_f32<0x128>(v));
+}
+// inclusive prefix sum over the 64 lanes (Kogge-Stone by DPP row shifts
+// inside rows, then the row totals carried by row broadcasts); lanes whose
+// DPP source lies outside the row keep the old value 0
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ int dpp0_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp0_i32<0x111>(v);          // row_shr:1
+  v += dpp0_i32<0x112>(v);          // row_shr:2
+  v += dpp0_i32<0x114>(v);          // row_shr:4
+  v += dpp0_i32<0x118>(v);          // row_shr:8
+  v += dpp0_i32<0x142, 0xA>(v);     // row_bcast:15 into rows 1 and 3
+  v += dpp0_i32<0x143, 0xC>(v);     // row_bcast:31 into rows 2 and 3
   return v;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = row_max16(v);
+  return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 // ------------------------------------------- direct-to-LDS copy pipeline

@@ -47,22 +47,15 @@ __device__ void wave_topk_select_store(float v[4], int k, float m, float s, int6
   int my_id = 0;
   float my_l = -INFINITY;
   for (int i = 0; i < k; ++i) {
-    float bv = v[0];
-    int bi = lane;
+    // the largest remaining logit (DPP and readlanes: wave-uniform), then the
+    // lowest expert id holding it: experts are lane + 64 j, so the first j
+    // whose ballot is not empty, and its lowest lane
+    const float bv = wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    int bi = -1;
 #pragma unroll
-    for (int j = 1; j < 4; ++j)
-      if (v[j] > bv) {
-        bv = v[j];
-        bi = lane + 64 * j;
-      }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t hit = __ballot(v[j] == bv);
+      if (bi < 0 && hit != 0ull) bi = 64 * j + __ffsll((unsigned long long)hit) - 1;
     }
     if (lane == i) {
       my_id = bi;
