@@ -304,6 +304,38 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
                      const moe_layer_aux* aux, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* moe_layer with the gate and sum variants of [LightOP] section 3 folded in:
+ * group-limited routing (section 3.1, Moe Fuse Gate; as in
+ * moe_route_grouped) and the shared expert's term plus a bias merged into
+ * the combine (section 3.2, MoE Sum; as in moe_combine_shared).
+ *   options (host struct, may be NULL = moe_layer):
+ *     n_group      0: plain top-k; else group-limited routing with
+ *                  topk_group kept groups (limits and supported shapes as in
+ *                  moe_route_grouped: 16 < E <= 256, bf16 x and wg);
+ *     shared       [T, H] device buffer in out_dtype, 16-byte aligned, or
+ *                  NULL; it may be out itself (read before the write) but
+ *                  must not otherwise overlap it;
+ *     shared_factor  finite, scales shared;
+ *     out_bias     [H] fp32 device buffer, 16-byte aligned, or NULL.
+ * Workspace size as moe_layer_workspace_size; all other arguments and
+ * errors as in moe_layer.  An invalid option is MOE_ERR_INVALID_ARG (an
+ * unsupported routing shape MOE_ERR_UNSUPPORTED) before anything is
+ * enqueued. */
+typedef struct moe_layer_options {
+  int32_t n_group;
+  int32_t topk_group;
+  const void* shared;
+  float shared_factor;
+  const float* out_bias;
+} moe_layer_options;
+
+moe_status moe_layer_ex(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                        const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                        const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                        int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                        const moe_layer_aux* aux, const moe_layer_options* options, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------- diagnostics -----
  * moe_last_error: message of this thread's last failed call ("" if none).
  * moe_last_dispatch: kernel variants this thread's last successful call

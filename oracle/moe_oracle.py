@@ -357,19 +357,25 @@ def combine_shared(y_rows: np.ndarray, pos: np.ndarray, w: np.ndarray, shared: n
 
 
 def layer(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capacity_factor,
-          s13=None, s2=None, sample_tokens=None) -> dict:
+          s13=None, s2=None, sample_tokens=None, n_group=0, topk_group=0, shared=None, shared_factor=1.0,
+          out_bias=None) -> dict:
     """The whole layer, expert-major (the method's grouping).
 
     Routing and alignment always run over all T tokens (drops depend on every
     earlier token); the expert FFN and combine run for ``sample_tokens`` only
     when given (all tokens otherwise).  Returns intermediates and ``out``
-    (float64, [len(sample), H]).
+    (float64, [len(sample), H]).  With ``n_group`` > 0 the routing is
+    group-limited (R9); ``shared`` [T, H] (values), ``shared_factor`` and
+    ``out_bias`` [H] enter the merge as in combine_shared (R8).
     """
     T, H = x.shape
     E = wg.shape[0]
     I = w2.shape[2]
     x64 = to_f64(x, x_dtype)
-    r = route(x64, to_f64(wg, wg_dtype), k, bias)
+    if n_group:
+        r = route_grouped(x64, to_f64(wg, wg_dtype), k, n_group, topk_group, bias)
+    else:
+        r = route(x64, to_f64(wg, wg_dtype), k, bias)
     C = capacity(T, k, E, capacity_factor)
     a = align(r["ids"], E, C)
     tok = np.arange(T) if sample_tokens is None else np.asarray(sample_tokens)
@@ -398,7 +404,11 @@ def layer(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, k, capacity_factor,
         else:
             w13e = to_f64(w13[e], w_dtype)
             y_rows[rows] = swiglu_ffn(x64[tokens_e], w13e[:I], w13e[I:], to_f64(w2[e], w_dtype))
-    res["out"] = combine(y_rows, pos_s, r["w"][tok])
+    if shared is not None or out_bias is not None:
+        sh = None if shared is None else np.asarray(shared, dtype=np.float64)[tok]
+        res["out"] = combine_shared(y_rows, pos_s, r["w"][tok], sh, shared_factor, out_bias)
+    else:
+        res["out"] = combine(y_rows, pos_s, r["w"][tok])
     return res
 
 

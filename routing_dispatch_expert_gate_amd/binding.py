@@ -62,6 +62,8 @@ SIGNATURES = {
     "moe_layer_workspace_size": (_sz, [_i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_layer": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
                         _i32, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "moe_layer_ex": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
+                           _i32, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_last_dispatch": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
@@ -71,6 +73,11 @@ SIGNATURES = {
 class MoeLayerAux(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("topk_ids", "topk_w", "topk_p", "counts", "offsets", "sorted_slot",
                                    "pos", "num_dropped", "xq", "xs")]
+
+
+class MoeLayerOptions(ctypes.Structure):
+    _fields_ = [("n_group", _i32), ("topk_group", _i32), ("shared", _vp), ("shared_factor", ctypes.c_float),
+                ("out_bias", _vp)]
 
 
 class MoeError(RuntimeError):
@@ -329,7 +336,10 @@ class Layer:
         self.nws = lib.moe_layer_workspace_size(T, H, I, E, k, _DT[x_dtype], _DT[w_dtype])
         self.ws = _ws(self.nws, device)
 
-    def __call__(self, x, wg, w13, w2, capacity=0, bias=None, s13=None, s2=None, out=None, aux=None):
+    def __call__(self, x, wg, w13, w2, capacity=0, bias=None, s13=None, s2=None, out=None, aux=None,
+                 options: dict | None = None):
+        """``options`` (a dict of moe_layer_options members: n_group,
+        topk_group, shared, shared_factor, out_bias) selects moe_layer_ex."""
         T, H, I, E, k = self.shape
         if out is None:
             out = torch.empty((T, H), dtype=x.dtype, device=x.device)
@@ -337,19 +347,36 @@ class Layer:
         if aux is not None:
             aux_s = MoeLayerAux(**{n: (aux[n].data_ptr() if aux.get(n) is not None else None)
                                    for n, _ in MoeLayerAux._fields_})
-        _check(lib.moe_layer(_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), _p(w13), _p(w2),
-                             _DT[self.w_dtype], _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out),
-                             _DT[out.dtype], ctypes.byref(aux_s) if aux_s is not None else None,
-                             _p(self.ws), self.nws, _stream(x.device)))
+        args = [_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), _p(w13), _p(w2), _DT[self.w_dtype],
+                _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out), _DT[out.dtype],
+                ctypes.byref(aux_s) if aux_s is not None else None]
+        if options is None:
+            _check(lib.moe_layer(*args, _p(self.ws), self.nws, _stream(x.device)))
+            return out
+        o = dict(options)
+        sh, ob = o.get("shared"), o.get("out_bias")
+        if sh is not None:
+            _dev(sh, "shared")
+            if sh.dtype != out.dtype or tuple(sh.shape) != (T, H):
+                raise ValueError(f"shared must be [{T}, {H}] {out.dtype}")
+        if ob is not None:
+            _dev(ob, "out_bias")
+            if ob.dtype != torch.float32 or tuple(ob.shape) != (H,):
+                raise ValueError(f"out_bias must be [{H}] float32")
+        opt = MoeLayerOptions(int(o.get("n_group", 0)), int(o.get("topk_group", 0)), _p(sh),
+                              float(o.get("shared_factor", 1.0)), _p(ob))
+        _check(lib.moe_layer_ex(*args, ctypes.byref(opt), _p(self.ws), self.nws, _stream(x.device)))
         return out
 
 
-def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None, w4a8=False):
+def layer(x, wg, w13, w2, k, capacity=0, bias=None, s13=None, s2=None, aux=None, w4a8=False, options=None):
     """One moe_layer call (allocates its workspace); ``aux`` maps moe_layer_aux
     member names to device tensors that receive the intermediates; ``w4a8``
-    runs packed int4 weights with int8 activations."""
+    runs packed int4 weights with int8 activations; ``options`` (dict of
+    moe_layer_options members) calls moe_layer_ex."""
     T, H = x.shape
     E, I = w2.shape[0], _inner(w2)
     _wdt(w13, w4a8)
     wd = "w4a8" if w4a8 else w13.dtype
-    return Layer(T, H, I, E, k, x.dtype, wd, x.device)(x, wg, w13, w2, capacity, bias, s13, s2, aux=aux)
+    return Layer(T, H, I, E, k, x.dtype, wd, x.device)(x, wg, w13, w2, capacity, bias, s13, s2, aux=aux,
+                                                         options=options)

@@ -521,12 +521,22 @@ size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int3
   return carve_layer(T, H, I, E, k, x_dtype, wgd, w_dtype).total;
 }
 
-moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
-                     const float* bias, const void* w13, const void* w2, int32_t w_dtype,
-                     const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
-                     int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
-                     const moe_layer_aux* aux, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused layer behind moe_layer and moe_layer_ex (opt NULL: plain top-k,
+// no shared term, no bias).
+moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                      const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                      const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                      int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                      const moe_layer_aux* aux, const moe_layer_options* opt, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const moe_layer_options no_opt{0, 0, nullptr, 1.0f, nullptr};
+  const moe_layer_options& o = opt ? *opt : no_opt;
+  const bool grouped = o.n_group != 0;
+  const bool merge = o.shared != nullptr || o.out_bias != nullptr;
   if (!is_act(x_dtype)) return fail(MOE_ERR_UNSUPPORTED, "x dtype must be MOE_F32 or MOE_BF16");
   if (out_dtype != x_dtype) return fail(MOE_ERR_UNSUPPORTED, "out dtype must equal x dtype");
   int32_t act;
@@ -552,6 +562,19 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   moe::RoutePlan rp;
   MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, si, (float*)si,
                        act == MOE_I8 ? (int8_t*)si : nullptr, act == MOE_I8 ? (float*)si : nullptr, &rp));
+  if (grouped) {
+    const int32_t ng = o.n_group, tg = o.topk_group;
+    if (ng < 1 || ng > 64 || E % ng != 0)
+      return fail(MOE_ERR_INVALID_ARG, "n_group (%d) must divide E (%d) and be in [1, 64]", ng, E);
+    if (tg < 1 || tg > ng)
+      return fail(MOE_ERR_INVALID_ARG, "topk_group (%d) must be in [1, n_group=%d]", tg, ng);
+    if ((int64_t)k > (int64_t)tg * (E / ng))
+      return fail(MOE_ERR_INVALID_ARG, "k (%d) exceeds the %d experts of the kept groups", k, tg * (E / ng));
+    if (rp.kind != 2)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "group-limited routing needs 16 < E <= 256, E %% 16 == 0, bf16 x and bf16 wg (got E=%d)", E);
+  }
+  if (!std::isfinite(o.shared_factor)) return fail(MOE_ERR_INVALID_ARG, "shared_factor must be finite");
   if (T == 0) return ok("none (T=0)");
   MOE_NONNULL(w13);
   MOE_NONNULL(w2);
@@ -563,6 +586,16 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   MOE_ALIGNED(w13, 16);
   MOE_ALIGNED(w2, 16);
   MOE_ALIGNED(out, 16);
+  if (o.shared) {
+    MOE_ALIGNED(o.shared, 16);
+    if (o.shared != out) {
+      const size_t bytes = (size_t)T * (size_t)H * (out_dtype == MOE_BF16 ? 2 : 4);
+      const char *sa = (const char*)o.shared, *oa = (const char*)out;
+      if (sa < oa + bytes && oa < sa + bytes)
+        return fail(MOE_ERR_INVALID_ARG, "shared overlaps out without being out");
+    }
+  }
+  if (o.out_bias) MOE_ALIGNED(o.out_bias, 16);
   const LayerCarve c = carve_layer(T, H, I, E, k, x_dtype, wg_dtype, w_dtype);
   MOE_TRY(check_ws(workspace, workspace_bytes, c.total));
 
@@ -601,7 +634,11 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
                                       sorted_slot, pos, tiles, num_tiles, num_dropped, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route+align launch");
   } else {
-    e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s);
+    if (grouped)
+      e = moe::launch_route_grouped(c.rp, x, wg, bias, T, H, E, k, o.n_group, o.topk_group, ids, w, p, xq, xs,
+                                    scratch, s);
+    else
+      e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
     e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts,
                           offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, scratch, s);
@@ -613,13 +650,41 @@ moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_
   e = moe::launch_ffn_down(c.fp, w2, w_dtype, s2, sorted_slot, tiles, num_tiles, w, T, H, I, k, y,
                            scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn down launch");
-  e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
+  if (merge)
+    e = moe::launch_combine_shared(y, ydt, pos, nullptr, T, k, H, o.shared, o.shared_factor, o.out_bias, out,
+                                   out_dtype, s);
+  else
+    e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
-  return ok(route_name(c.rp) + " | " + (fused ? std::string("align(fused into route)")
+  return ok(route_name(c.rp) + (grouped ? "<grouped>" : "") + " | " + (fused ? std::string("align(fused into route)")
                                 : c.ap.nblocks == 0 ? std::string("align(one block)")
                                                     : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
             c.fp.up_name + "+" + c.fp.down_name + "(block_m=" + std::to_string(c.fp.block_m) +
-            ") | combine_kernel<pre-weighted>");
+            ") | combine_kernel<pre-weighted" + (merge ? ",shared+bias>" : ">"));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                     const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                     const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                     int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                     const moe_layer_aux* aux, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return layer_impl(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, s13, s2, T, H, I, E, k, capacity, out,
+                    out_dtype, aux, nullptr, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_layer_ex(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                        const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                        const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                        int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                        const moe_layer_aux* aux, const moe_layer_options* options, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return layer_impl(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, s13, s2, T, H, I, E, k, capacity, out,
+                    out_dtype, aux, options, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

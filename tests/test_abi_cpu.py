@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -227,3 +227,27 @@ def test_combine_and_layer_validation(moe):
     assert layer(wd=I8) == INVALID                     # scales missing
     assert layer() == WORKSPACE
     assert layer(T=0) == OK
+
+
+def test_layer_options_validation(moe):
+    """moe_layer_ex checks its options before anything is enqueued."""
+    L = moe.lib
+
+    def ex(ng=0, tg=0, shared=None, f=1.0, ob=None, T=64, E=32, k=2, opts=True):
+        o = moe.binding.MoeLayerOptions(ng, tg, shared, f, ob)
+        return L.moe_layer_ex(P, BF16, P, BF16, None, P, P, BF16, None, None, T, 128, 128, E, k, 0, P, BF16,
+                              None, ctypes.byref(o) if opts else None, None, 0, None)
+
+    assert ex(opts=False) == WORKSPACE               # NULL options: moe_layer
+    assert ex() == WORKSPACE
+    assert ex(ng=4, tg=2) == WORKSPACE
+    assert ex(ng=3, tg=1) == INVALID                 # n_group must divide E
+    assert ex(ng=4, tg=5) == INVALID                 # topk_group > n_group
+    assert ex(ng=8, tg=1, k=5) == INVALID            # k above the kept groups' experts
+    assert ex(ng=2, tg=1, E=8) == UNSUPPORTED        # group-limited routing needs 16 < E <= 256
+    assert ex(f=float("nan")) == INVALID
+    assert ex(f=float("inf"), T=0) == INVALID        # checked even for T == 0
+    assert ex(ob=ctypes.c_void_p(260)) == INVALID    # out_bias must be 16-byte aligned
+    assert ex(shared=ctypes.c_void_p(272)) == INVALID  # overlaps out without being out
+    assert ex(shared=P) == WORKSPACE                 # shared may be out itself
+    assert ex(T=0, ng=4, tg=2) == OK

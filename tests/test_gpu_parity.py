@@ -686,3 +686,80 @@ def test_empty_batch_is_a_noop():
     torch.cuda.synchronize()
     assert out.shape == (0, 128)
     assert moe.last_dispatch() == "none (T=0)"
+
+
+# ------------------------------------------- layer with gate/sum options
+# (spec, n_group, topk_group, shared, shared_factor, out_bias, in place):
+# group-limited routing with a shared expert and an output bias in one call
+LAYER_EX = [
+    (moe_synth.Spec("lx_e64_G8_TG3_cap", 200, 256, 64, 6, 128, capacity_factor=1.25, zipf_s=1.0),
+     8, 3, True, 0.5, True, False),
+    (moe_synth.Spec("lx_e32_G4_TG2_i8_cap", 130, 256, 32, 4, 128, w_dtype="i8", capacity_factor=1.25),
+     4, 2, True, 1.0, False, True),
+    (moe_synth.Spec("lx_e64_plain_w4a8", 96, 256, 64, 4, 128, w_dtype="i4a8"), 0, 0, True, 2.0, True, False),
+    (moe_synth.Spec("lx_e256_G8_TG4_T1", 1, 512, 256, 8, 128), 8, 4, False, 1.0, True, False),
+    (moe_synth.Spec("lx_e256_G8_TG4_w4a16", 64, 512, 256, 8, 128, w_dtype="i4"), 8, 4, True, -1.0, True, True),
+]
+
+
+@pytest.mark.parametrize("case", LAYER_EX, ids=[c[0].name for c in LAYER_EX])
+def test_layer_ex_matches_composition_and_oracle(case):
+    """moe_layer_ex is bit for bit its steps called one by one (grouped route,
+    align, expert FFN, combine with the shared term and bias), and matches
+    the oracle layer with the same options on every token whose routing the
+    fp32 logits decide as the fp64 oracle does."""
+    moe = _moe()
+    spec, G, TG, with_s, f, with_b, in_place = case
+    c = Case(spec, 5151)
+    s = c.spec
+    T, H, k = s.T, s.H, s.k
+    rng = np.random.default_rng(T + 17 * s.E)
+    S = moe_synth.f32_to_bf16_bits((0.01 * rng.standard_normal((T, H))).astype(np.float32)) if with_s else None
+    b = (0.01 * rng.standard_normal(H)).astype(np.float32) if with_b else None
+    S_d, b_d = to_dev(S), to_dev(b)
+    opts = dict(n_group=G, topk_group=TG, shared=S_d, shared_factor=f, out_bias=b_d)
+    aux = {"topk_ids": torch.empty((T, k), dtype=torch.int32, device="cuda"),
+           "pos": torch.empty((T, k), dtype=torch.int32, device="cuda")}
+    w4a8 = s.w_dtype == "i4a8"
+    a8 = s.w_dtype in ("i8", "i4a8")
+    out_buf = S_d.clone() if in_place else None
+    if in_place:
+        opts["shared"] = out_buf
+    L = moe.Layer(T, H, s.I, s.E, k, c.x.dtype, "w4a8" if w4a8 else c.w13.dtype)
+    out = L(c.x, c.wg, c.w13, c.w2, capacity=c.C or 0, bias=c.bias, s13=c.s13, s2=c.s2, out=out_buf, aux=aux,
+            options=opts)
+    torch.cuda.synchronize()
+    d = moe.last_dispatch()
+    print(d)
+    assert ("<grouped>" in d) == (G > 0)
+    assert ("shared+bias" in d) == (with_s or with_b)
+    if in_place:
+        assert out.data_ptr() == out_buf.data_ptr()
+
+    # the same steps one by one
+    r = moe.route(c.x, c.wg, k, bias=c.bias, want_p=False, quant=a8, n_group=G or None, topk_group=TG or None)
+    wdt = {"bf16": torch.bfloat16, "i8": torch.int8, "i4": torch.uint8, "i4a8": "w4a8"}[s.w_dtype]
+    bm = moe.ffn_block_m(T, H, s.I, s.E, k, wdt)
+    a = moe.align(r["ids"], s.E, c.C or 0, bm)
+    y = moe.expert_ffn(r["xq"] if a8 else c.x, c.w13, c.w2, a["sorted_slot"], a["tiles"], a["num_tiles"], bm, k,
+                       topk_w=r["w"], xs=r["xs"], s13=c.s13, s2=c.s2, w4a8=w4a8)
+    ref_d = moe.combine_shared(y, a["pos"], None, T, k, torch.bfloat16, shared=S_d, shared_factor=f, bias=b_d)
+    torch.cuda.synchronize()
+    assert torch.equal(aux["topk_ids"], r["ids"])
+    assert torch.equal(out.view(torch.int16), ref_d.view(torch.int16))
+
+    # against the oracle
+    S64 = moe_synth.bf16_bits_as_f32(S).astype(np.float64) if with_s else None
+    ro = oracle.layer(c.inp.x, s.x_dtype, c.inp.wg, s.wg_dtype, c.inp.bias, c.inp.w13, c.inp.w2, s.w_dtype, k,
+                      s.capacity_factor, c.inp.s13, c.inp.s2, n_group=G, topk_group=TG, shared=S64,
+                      shared_factor=f, out_bias=b)
+    rr = ro["route"]
+    band = dict(rr, gap_p=np.minimum(rr["gap_p"], rr["gap_group"])) if G else rr
+    same = check_ids(aux["topk_ids"].cpu().numpy(), band)
+    pos_g = aux["pos"].cpu().numpy()
+    agree = same & ((pos_g >= 0) == (ro["align"]["pos"].reshape(T, k) >= 0)).all(axis=1)
+    assert agree.mean() > 0.97
+    got = out.float().cpu().numpy().astype(np.float64)
+    rel = _rel(got[agree], ro["out"][agree])
+    print(f"[layer_ex] {s.name}: rel-L2 {rel:.3e} over {int(agree.sum())}/{T} tokens")
+    assert rel <= TOL[s.w_dtype], rel

@@ -547,3 +547,22 @@ def test_w4a8_is_w8a8_on_int4_codes():
     rel = np.linalg.norm(a - c) / np.linalg.norm(c)
     assert 0 < rel < 5e-2, rel
     assert inp.w13.min() >= -8 and inp.w13.max() <= 7
+
+
+def test_layer_options_compose_the_pinned_steps():
+    """The layer with group-limited routing and a shared expert is the plain
+    composition of the pinned steps: route_grouped's ids and weights through
+    the same FFN, merged by combine_shared; with every group kept, no shared
+    term and no bias it is the plain layer."""
+    inp = _small_inputs(40, 32, 16, 3, 16, cap=0.9)
+    base = oracle.layer(**_layer(inp))
+    same = oracle.layer(**_layer(inp, n_group=4, topk_group=4))
+    np.testing.assert_array_equal(same["out"], base["out"])
+    rng = np.random.default_rng(4)
+    S = rng.standard_normal((40, 32))
+    b = rng.standard_normal(32)
+    res = oracle.layer(**_layer(inp, n_group=4, topk_group=2, shared=S, shared_factor=0.5, out_bias=b))
+    r = oracle.route_grouped(inp.x.astype(np.float64), inp.wg.astype(np.float64), 3, 4, 2)
+    np.testing.assert_array_equal(res["route"]["ids"], r["ids"])
+    plain = oracle.layer(**_layer(inp, n_group=4, topk_group=2))
+    np.testing.assert_allclose(res["out"], plain["out"] + 0.5 * S + b[None, :], rtol=1e-12, atol=1e-12)
