@@ -627,7 +627,7 @@ void gg_kernel(const GemmArgs a) {
           m = fmaxf(m, fabsf(hv));
         }
         m = row_max16(m);                              // 16 lanes by DPP,
-        m = fmaxf(m, __shfl_xor(m, 16, kWave));        // then the other row of the half
+        m = fmaxf(m, lane_xor16(m));                   // then the other row of the half
         if (valid && (lane & 31) == 0) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
       }
     }

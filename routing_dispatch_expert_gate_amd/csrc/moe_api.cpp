@@ -328,7 +328,9 @@ moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32
                                       xq, xs, workspace, cap, block_m, mt, counts, offsets, sorted_slot, pos,
                                       tiles, num_tiles, num_dropped, s);
     if (e != hipSuccess) return hip_fail(e, "moe_route_align launch");
-    return ok(route_name(plan) + "+align (one launch)");
+    moe::RoutePlan named = plan;
+    if (named.kind == 0) named.bt = (int)T;   // one workgroup takes every token
+    return ok(route_name(named) + "+align (one launch)");
   }
   e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p, xq, xs,
                         workspace, s);

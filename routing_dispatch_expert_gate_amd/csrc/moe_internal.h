@@ -87,6 +87,20 @@ __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
                                                                CTRL, 0xF, 0xF, false));
 }
+// The value of lane l ^ 16 (l ^ 32): gfx950's row-swap permutes exchange
+// odd and even 16-lane rows (the two 32-lane halves) of their two operands in
+// the VALU, without a trip through the LDS crossbar.  Given the same register
+// twice, the half that moved holds the partner lane's value.
+__device__ __forceinline__ float lane_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                  false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                  false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? r[0] : r[1]);
+}
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }

@@ -199,45 +199,69 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum of each of EP values over the 64 lanes.  Two butterfly steps inside
-// each quad (DPP xor 1, xor 2) halve the vector twice, so lane l keeps EP/4
-// values: indices (l & 1) * EP/2 + ((l >> 1) & 1) * EP/4 + i.  Lanes 4 apart
-// in a 16-lane row then hold the same indices: two DPP shift-adds (row_shr 4,
-// 8) leave each row's sums in its lanes 12..15, and two shuffles (xor 16, 32)
-// add the rows.  Only those two levels go through the LDS crossbar, and the
-// EP/4 chains are independent.  Lanes 12..15 end with the totals.
-template <int EP>
-__device__ __forceinline__ void wave_reduce_quads(float (&a)[EP], int lane) {
-  static_assert(EP % 4 == 0, "EP");
-  {
-    const bool up = (lane & 1) != 0;
+// Wave sums of N values per lane (N = tokens x experts of a load batch), by
+// a butterfly over the six lane bits, in the order 3, 2, 1, 0, 4, 5: the
+// partner of each step differs from the lane in that bit only (DPP
+// row_mirror, row_half_mirror, quad_perm xor 2 and xor 1, then the row-swap
+// permutes for 16 and 32), and while more than one value is left the lane
+// keeps the half its bit selects and adds the partner's copy of that half.
+// Lane l ends with max(N / 64, 1) totals a[0..], of the flat indices
+// bfly_base<N>(l) + i.  No step goes through the LDS crossbar and the N
+// chains are independent, so they pipeline.
+template <int S>
+__device__ __forceinline__ float bfly_partner(float v) {
+  if constexpr (S == 0) return dpp_f<0x140>(v);
+  else if constexpr (S == 1) return dpp_f<0x141>(v);
+  else if constexpr (S == 2) return dpp_f<0x4E>(v);
+  else if constexpr (S == 3) return dpp_f<0xB1>(v);
+  else if constexpr (S == 4) return lane_xor16(v);
+  else return lane_xor32(v);
+}
+__device__ __forceinline__ constexpr int bfly_bit(int s) { return s < 4 ? 3 - s : s; }
+
+template <int N, int S = 0>
+__device__ __forceinline__ void wave_sum_all(float (&a)[N], int lane) {
+  if constexpr (S < 6) {
+    constexpr int n = (N >> S) > 1 ? (N >> S) : 1;   // values left before this step
+    if constexpr (n >= 2) {
+      constexpr int h = n / 2;
+      const bool up = ((lane >> bfly_bit(S)) & 1) != 0;
 #pragma unroll
-    for (int i = 0; i < EP / 2; ++i) {
-      const float send = up ? a[i] : a[i + EP / 2];
-      const float keep = up ? a[i + EP / 2] : a[i];
-      a[i] = keep + dpp_f<0xB1>(send);
+      for (int i = 0; i < h; ++i) {
+        const float send = up ? a[i] : a[i + h];
+        const float keep = up ? a[i + h] : a[i];
+        a[i] = keep + bfly_partner<S>(send);
+      }
+    } else {
+      a[0] += bfly_partner<S>(a[0]);
     }
+    wave_sum_all<N, S + 1>(a, lane);
   }
-  {
-    const bool up = (lane & 2) != 0;
+}
+// first flat index of lane l's totals, and whether l is the one lane of its
+// duplicates (N < 64 leaves 64 / N lanes with the same totals) that stores
+template <int N>
+__device__ __forceinline__ int bfly_base(int lane) {
+  int b = 0;
 #pragma unroll
-    for (int i = 0; i < EP / 4; ++i) {
-      const float send = up ? a[i] : a[i + EP / 4];
-      const float keep = up ? a[i + EP / 4] : a[i];
-      a[i] = keep + dpp_f<0x4E>(send);
-    }
-  }
+  for (int s = 0; s < 6; ++s)
+    if ((N >> s) >= 2) b += ((lane >> bfly_bit(s)) & 1) * (N >> (s + 1));
+  return b;
+}
+template <int N>
+__device__ __forceinline__ bool bfly_writer(int lane) {
+  bool w = true;
 #pragma unroll
-  for (int i = 0; i < EP / 4; ++i) a[i] += dpp_f<0x114>(a[i]);
-#pragma unroll
-  for (int i = 0; i < EP / 4; ++i) a[i] += dpp_f<0x118>(a[i]);
-#pragma unroll
-  for (int i = 0; i < EP / 4; ++i) a[i] += __shfl_xor(a[i], 16, kWave);
-#pragma unroll
-  for (int i = 0; i < EP / 4; ++i) a[i] += __shfl_xor(a[i], 32, kWave);
+  for (int s = 0; s < 6; ++s)
+    if ((N >> s) < 2) w = w && ((lane >> bfly_bit(s)) & 1) == 0;
+  return w;
 }
 
-constexpr int kFmaTB = 16;   // tokens per workgroup
+// tokens per workgroup: 16 where the grid still fills the chip (and for the
+// fused route + align, whose one workgroup takes every token); fewer for
+// smaller batches, since a workgroup's E*H FMAs per token run on one CU
+constexpr int kFmaTB = 16;
+inline int fma_tokens_per_wg(int64_t T) { return T >= 16 * 256 ? 16 : T >= 4 * 256 ? 4 : 1; }
 
 // The raw bytes of 8 consecutive x values, loaded in one go and widened later
 // (so a batch of rows can be in flight before the first use).
@@ -276,20 +300,25 @@ struct Raw8<float> {
 // WIDE: more than 8 waves (H > 4096, E <= 8 only), 1024 threads and hence at
 // most 128 VGPRs: fewer rows in flight.
 // A workgroup's token rows are loaded in batches of PF rows, each batch before
-// its first FMA; each token's E partial logits are reduced over the wave by
-// wave_reduce_quads.
-template <int EP, bool WIDE, typename XT, typename WT, bool QUANT, bool ALIGN>
+// its first FMA; the partial logits of G rows at a time are summed over the
+// wave by wave_sum_all.
+template <int EP, bool WIDE, typename XT, typename WT, bool QUANT, bool ALIGN, int TB, int NVMAX = 64>
 __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
     float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs, const AlignArgs al) {
   // rows per load batch (all sixteen at once costs occupancy: measured
   // slower at large T)
-  constexpr int PF = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1);
-  static_assert(kFmaTB % PF == 0, "batches");
-  __shared__ float part[16][kFmaTB][EP];
-  __shared__ float amax_s[16][kFmaTB];
-  __shared__ __attribute__((aligned(16))) float lg[kFmaTB][16];
+  constexpr int PF0 = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1), PF = PF0 < TB ? PF0 : TB;
+  static_assert(TB % PF == 0, "batches");
+  static_assert(!ALIGN || TB == kFmaTB, "the fused align takes one workgroup of kFmaTB tokens");
+  // rows per wave reduction: at most NVMAX sums at once (64 measured best at
+  // one workgroup per CU, 32 with several resident)
+  constexpr int G = PF * EP <= NVMAX ? PF : NVMAX / EP, NV = G * EP;
+  static_assert(PF % G == 0, "reduction groups");
+  __shared__ float part[16][TB][EP];
+  __shared__ float amax_s[16][TB];
+  __shared__ __attribute__((aligned(16))) float lg[TB][16];
   const int nw = blockDim.x >> 6;
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -306,8 +335,8 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     for (int i = 0; i < 8; ++i) wr[e][i] = v[i];
   }
 
-  const int64_t t0 = (int64_t)blockIdx.x * kFmaTB;
-  const int ntok = (int)((T - t0) < kFmaTB ? (T - t0) : kFmaTB);
+  const int64_t t0 = (int64_t)blockIdx.x * TB;
+  const int ntok = (int)((T - t0) < TB ? (T - t0) : TB);
   for (int tb = 0; tb < ntok; tb += PF) {
     Raw8<XT> r[PF];
 #pragma unroll
@@ -317,41 +346,45 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
       else
         r[u].zero();
     }
+    // G rows at a time: their G x EP partial dot products (rows past ntok
+    // are zeros), summed over the wave together
 #pragma unroll
-    for (int ub = 0; ub < PF; ++ub) {
-      if (tb + ub >= ntok) break;
-      float acc[EP];
-      {
+    for (int g0 = 0; g0 < PF; g0 += G) {
+      float acc[NV];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
         float v[8];
-        r[ub].get(v);
+        r[g0 + u].get(v);
 #pragma unroll
         for (int e = 0; e < EP; ++e) {
           float a = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) a = fmaf(v[i], wr[e][i], a);
-          acc[e] = a;
+          acc[u * EP + e] = a;
         }
         if (QUANT) {
           float am = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
           am = wave_max(am);
-          if (lane == 0) amax_s[wv][tb + ub] = am;
+          if (lane == 0 && tb + g0 + u < ntok) amax_s[wv][tb + g0 + u] = am;
         }
       }
-      wave_reduce_quads<EP>(acc, lane);
-      if (lane >= 12 && lane < 16 && tb + ub < ntok) {
-        const int q = lane & 3;
-        const int base = (q & 1) * (EP / 2) + ((q >> 1) & 1) * (EP / 4);
+      wave_sum_all<NV>(acc, lane);
+      if (bfly_writer<NV>(lane)) {
+        const int base = bfly_base<NV>(lane);
 #pragma unroll
-        for (int i = 0; i < EP / 4; ++i) part[wv][tb + ub][base + i] = acc[i];
+        for (int i = 0; i < (NV >= 64 ? NV / 64 : 1); ++i) {
+          const int j = base + i, u = j / EP;
+          if (tb + g0 + u < ntok) part[wv][tb + g0 + u][j - u * EP] = acc[i];
+        }
       }
     }
   }
   __syncthreads();
 
   // logits (plus bias) of the block's tokens, rows padded with -inf
-  for (int i = threadIdx.x; i < kFmaTB * 16; i += blockDim.x) {
+  for (int i = threadIdx.x; i < TB * 16; i += blockDim.x) {
     const int tt = i >> 4, e = i & 15;
     float s = -INFINITY;
     if (tt < ntok && e < E) {
@@ -517,8 +550,8 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
     if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[v];
   }
   if constexpr (QUANT) {
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, kWave));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, kWave));
+    amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+    amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));   // lane ^ 2
     if (blockIdx.y == 0 && (tid & 3) == 0 && t0 + qrow < T)
       amax_part[(int64_t)blockIdx.z * T + t0 + qrow] = __uint_as_float(amax << 16);
   }
@@ -631,23 +664,39 @@ template <int EP, bool WIDE, typename XT, typename WT>
 hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                       int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                       int8_t* xq, float* xs, const AlignArgs* al, hipStream_t s) {
-  const dim3 grid((unsigned)((T + kFmaTB - 1) / kFmaTB));
+  const int tb = al ? kFmaTB : p.bt;
+  const dim3 grid((unsigned)((T + tb - 1) / tb));
   const dim3 block(64 * p.nw);
   const AlignArgs none{};
-#define MOE_FMA(Q, A)                                                                        \
-  route_fma_kernel<EP, WIDE, XT, WT, Q, A><<<grid, block, 0, s>>>((const XT*)x, (const WT*)wg, bias, \
-                                                                  T, H, E, k, ids, w, prob, xq, xs,   \
-                                                                  al ? *al : none)
+#define MOE_FMA(Q, A, TB, NVM)                                                                         \
+  route_fma_kernel<EP, WIDE, XT, WT, Q, A, TB, NVM><<<grid, block, 0, s>>>((const XT*)x, (const WT*)wg, bias, \
+                                                                           T, H, E, k, ids, w, prob, xq, xs,   \
+                                                                           al ? *al : none)
   if (al) {
     if (xq)
-      MOE_FMA(true, true);
+      MOE_FMA(true, true, kFmaTB, 64);
     else
-      MOE_FMA(false, true);
+      MOE_FMA(false, true, kFmaTB, 64);
+  } else if (tb == 16 && T >= 4 * 16 * 256) {
+    if (xq)
+      MOE_FMA(true, false, 16, 32);
+    else
+      MOE_FMA(false, false, 16, 32);
+  } else if (tb == 16) {
+    if (xq)
+      MOE_FMA(true, false, 16, 64);
+    else
+      MOE_FMA(false, false, 16, 64);
+  } else if (tb == 4) {
+    if (xq)
+      MOE_FMA(true, false, 4, 64);
+    else
+      MOE_FMA(false, false, 4, 64);
   } else {
     if (xq)
-      MOE_FMA(true, false);
+      MOE_FMA(true, false, 1, 64);
     else
-      MOE_FMA(false, false);
+      MOE_FMA(false, false, 1, 64);
   }
 #undef MOE_FMA
   return hipGetLastError();
@@ -711,7 +760,7 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
     const int nw = (H + 511) / 512;
     if (nw > (E <= 8 ? 16 : 8)) return p;
     p.kind = 0;
-    p.bt = kFmaTB;
+    p.bt = fma_tokens_per_wg(T);
     p.nw = nw;
     return p;
   }

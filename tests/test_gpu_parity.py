@@ -142,6 +142,11 @@ ROUTE_PATHS = [
     (moe_synth.Spec("fma_wide_f32", 21, 6144, 4, 2, 64, x_dtype="f32", wg_dtype="f32"), True,
      "route_fma_kernel"),
     (moe_synth.Spec("fma_e16_f32x", 50, 4096, 16, 4, 64, x_dtype="f32"), True, "route_fma_kernel"),
+    # one, four and sixteen tokens per workgroup (with a ragged last one)
+    (moe_synth.Spec("fma_tb1_bias", 300, 2048, 8, 2, 64, zipf_s=1.1), True, "tokens/wg=1,"),
+    (moe_synth.Spec("fma_tb4_e16", 2049, 1024, 12, 3, 64), True, "tokens/wg=4,"),
+    (moe_synth.Spec("fma_tb16_e8", 4099, 512, 8, 2, 64, wg_dtype="f32"), False, "tokens/wg=16,"),
+    (moe_synth.Spec("fma_tb16_many", 16411, 256, 8, 2, 64), True, "tokens/wg=16,"),
     (moe_synth.Spec("e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
      "route_gemm_kernel("),
     (moe_synth.Spec("e32_many_tokens", 128 * 64 + 1, 128, 32, 3, 64), False, "ksplit=1)"),
