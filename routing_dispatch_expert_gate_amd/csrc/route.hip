@@ -564,26 +564,54 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
 // One wave: the top-k (and, with quantisation, the int8 codes) of token t.
 // lrow: this wave's 64-float LDS row; grow/gscore: its 256- and 64-float rows
 // for the group-limited selection.
-template <bool QUANT, bool GROUPED>
+template <bool QUANT, bool GROUPED, int XPF, int ZC>
 __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
                            const float* __restrict__ bias, int64_t T, int E, int k, int H,
                            const uint16_t* __restrict__ x, int32_t* __restrict__ ids, float* __restrict__ w,
                            float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs,
                            int n_group, int topk_group, float* lrow, float* grow, float* gscore) {
   const int lane = threadIdx.x & 63;
+  // W8A8, XPF > 0 (small batches, latency-bound): the token's x row (its
+  // first XPF*512 values) and its per-split absmax are fetched before the
+  // selection, which they do not depend on, so their memory latency overlaps
+  // the partial-logit loads.  Large batches keep the registers for occupancy.
+  constexpr int QPF = QUANT ? XPF : 0;
+  uint4 xr[QPF > 0 ? QPF : 1];
+  float am = 0.f;
+  auto load_amax = [&]() {
+    for (int z0 = 0; z0 < ks; z0 += 8) {
+      float a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = z0 + u < ks ? amax_part[(size_t)(z0 + u) * T + t] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) am = fmaxf(am, a[u]);
+    }
+  };
+  if constexpr (QPF > 0) {
+    const uint16_t* xrow = x + t * H;
+#pragma unroll
+    for (int u = 0; u < QPF; ++u)
+      if (lane * 8 + u * 512 < H) xr[u] = *reinterpret_cast<const uint4*>(xrow + lane * 8 + u * 512);
+    load_amax();
+  }
+  // the K-split partial logits, ZC splits per batch of loads (one batch, so
+  // one memory latency, for up to ZC splits), summed in split order
   float v[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int z0 = 0; z0 < ks; z0 += 8) {
-    float q[4][8];
+  for (int z0 = 0; z0 < ks; z0 += ZC) {
+    float q[4][ZC];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < ZC; ++u) {
         const int e = lane + 64 * j;
         q[j][u] = (e < E && z0 + u < ks) ? part[((size_t)(z0 + u) * T + t) * E + e] : 0.f;
       }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      v[j] += ((q[j][0] + q[j][1]) + (q[j][2] + q[j][3])) + ((q[j][4] + q[j][5]) + (q[j][6] + q[j][7]));
+#pragma unroll
+      for (int u0 = 0; u0 < ZC; u0 += 8)
+        v[j] += ((q[j][u0] + q[j][u0 + 1]) + (q[j][u0 + 2] + q[j][u0 + 3])) +
+                ((q[j][u0 + 4] + q[j][u0 + 5]) + (q[j][u0 + 6] + q[j][u0 + 7]));
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -600,14 +628,27 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
     wave_topk_store(v, E, k, t, ids, w, prob);
   }
   if constexpr (QUANT) {
-    float am = 0.f;
-    for (int z = 0; z < ks; ++z) am = fmaxf(am, amax_part[(size_t)z * T + t]);
+    if constexpr (QPF == 0) load_amax();
     const float s = row_scale(am);
     const float rs = 1.f / s;
     const uint16_t* xrow = x + t * H;
     int8_t* qrow = xq + t * H;
-    // 4 chunks of 8 values per lane in flight
-    for (int h0 = lane * 8; h0 < H; h0 += 4 * 512) {
+#pragma unroll
+    for (int u = 0; u < QPF; ++u) {
+      const int h = lane * 8 + u * 512;
+      if (h < H) {
+        const uint32_t q4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+        float c[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[2 * i] = __uint_as_float(q4[i] << 16);
+          c[2 * i + 1] = __uint_as_float(q4[i] & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint2*>(qrow + h) = quant8(c, s, rs);
+      }
+    }
+    // the rest of a longer row: 4 chunks of 8 values per lane in flight
+    for (int h0 = lane * 8 + QPF * 512; h0 < H; h0 += 4 * 512) {
       float c[4][8];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -620,7 +661,10 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
   }
 }
 
-template <bool QUANT, bool GROUPED>
+// LAT: a batch small enough that the kernel is one dependent chain per token
+// (at most 256 workgroups): fetch all split partials at once and the x row
+// before the selection; otherwise keep registers for occupancy.
+template <bool QUANT, bool GROUPED, bool LAT>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
     const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
@@ -632,8 +676,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   const int wv = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wv;
   if (t >= T) return;
-  topk_token<QUANT, GROUPED>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob, xq, xs, n_group,
-                             topk_group, lrow[wv], grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+  topk_token<QUANT, GROUPED, LAT ? 8 : 0, LAT ? 16 : 8>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob,
+                                                         xq, xs, n_group, topk_group, lrow[wv],
+                                                         grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
 }
 
 // Route and align fused for small batches (T <= kFusedTopkT): one workgroup
@@ -653,8 +698,9 @@ __global__ __launch_bounds__(1024) void route_topk_align_kernel(
   __shared__ float gscore[GROUPED ? 16 : 1][64];
   const int wv = threadIdx.x >> 6;
   for (int64_t t = wv; t < T; t += 16)
-    topk_token<QUANT, GROUPED>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob, xq, xs, n_group,
-                               topk_group, lrow[wv], grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+    // (1024 threads: at most 128 VGPRs, so fewer x chunks held)
+    topk_token<QUANT, GROUPED, 2, 8>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob, xq, xs, n_group,
+                                  topk_group, lrow[wv], grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
   __syncthreads();
   block_align<16>([&](int64_t s) { return ids[s]; }, T * k, E, al.ebits, al.cap, al.bm, al.max_tiles, al.counts,
                   al.offsets, al.sorted_slot, al.pos, al.tiles, al.num_tiles, al.num_dropped);
@@ -741,12 +787,19 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
     return hipGetLastError();
   }
   const dim3 g2((unsigned)((T + 3) / 4));
-  if (xq)
-    route_topk_kernel<true, GROUPED><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
-                                                        prob, xq, xs, n_group, topk_group);
+#define MOE_TOPK(Q, LAT)                                                                                      \
+  route_topk_kernel<Q, GROUPED, LAT><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, \
+                                                        xq, xs, n_group, topk_group)
+  const bool lat = T <= 4 * 256;
+  if (xq && lat)
+    MOE_TOPK(true, true);
+  else if (xq)
+    MOE_TOPK(true, false);
+  else if (lat)
+    MOE_TOPK(false, true);
   else
-    route_topk_kernel<false, GROUPED><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w,
-                                                         prob, xq, xs, n_group, topk_group);
+    MOE_TOPK(false, false);
+#undef MOE_TOPK
   return hipGetLastError();
 }
 
