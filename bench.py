@@ -5,10 +5,10 @@
 A step is one whole-layer call (moe_layer) over one batch of seeded synthetic
 inputs already resident in HBM.  The default workload is the Mixtral-8x7B
 shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  After the K
-timed steps, each step of the layer is launched through its own entry point K
-times back to back with HIP events around the run, on the stream the library
-launches on, to get each kernel's average duration (the host runs ahead of
-the GPU, so launch latency stays out of the small kernels' times); the
+timed steps, K launches of each step of the layer (through its own entry
+point) are captured in a HIP graph and replayed between two HIP events on the
+replaying stream, to get each kernel's average duration without the host's
+per-call cost (which exceeds the small kernels' own times); the
 dominant kernel's roofline is computed from those durations and its
 algorithmic flops/bytes.  A cold pass (after a 1 GiB write) gives each step's
 time with its inputs in HBM.  The CPU oracle is timed on a bounded token
@@ -36,7 +36,7 @@ PEAK_HBM_GBPS = 8000.0
 # W4A16 ("i4") widens its int4 weights to bf16 and runs the bf16 MFMA
 PEAK_TFLOPS = {"bf16": 2500.0, "i8": 5000.0, "f32": 157.3, "i4": 2500.0, "i4a8": 5000.0}
 RIDGE = {k: v * 1e12 / (PEAK_HBM_GBPS * 1e9) for k, v in PEAK_TFLOPS.items()}   # flop per byte
-CPU_SAMPLE = {1: 64, 2: 1024, 3: 64, 4: 16, 5: 512}
+CPU_SAMPLE = {1: 64, 2: 4096, 3: 64, 4: 16, 5: 512}
 BYTES = {"f32": 4, "bf16": 2, "i8": 1, "i4": 0.5, "i4a8": 0.5}
 A8 = ("i8", "i4a8")                  # schemes that quantise activations per token
 
@@ -157,21 +157,29 @@ class Staged:
                 ev[i + 1].record()
 
     def time_each(self, reps: int) -> dict:
-        """Average GPU time of each step launched `reps` times back to back
-        between two events: the host runs ahead of the GPU, so its launch
-        latency does not enter the small kernels' times."""
+        """Average GPU time of each step: `reps` launches of it captured in one
+        HIP graph, replayed between two events on the replaying stream, so
+        the host's per-call cost (ctypes, launch) does not enter the small
+        kernels' times."""
         torch = self.torch
         out = {}
-        for name, fn in self.stages():
+        for i, (name, fn) in enumerate(self.stages()):
             fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = self.stages()[i][1]      # bound to the capturing stream
+                for _ in range(reps):
+                    cap()
+            g.replay()
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(reps):
-                fn()
+            g.replay()
             e1.record()
             torch.cuda.synchronize()
             out[name] = e0.elapsed_time(e1) / reps
+            del g
         return out
 
 
