@@ -11,11 +11,12 @@
 //
 // Two variants, picked on the host by shape (never silently):
 //   kind 0  E <= 16: fp32 FMA.  Each wave keeps its slice of Wg (8 values of
-//           H per lane, all experts) in registers and re-uses it for 16
-//           tokens, whose x chunks are loaded in batches before their FMAs;
-//           per-token partial logits are reduced across the 64 lanes with DPP
-//           inside quads and rows and two shuffles across rows, then across
-//           waves through LDS.  Logits never leave the chip.
+//           H per lane, all experts) in registers and re-uses it for the
+//           workgroup's 1, 4 or 16 tokens (by batch size), whose x chunks are
+//           loaded in batches before their FMAs; the partial logits of a
+//           group of rows are summed across the 64 lanes in one butterfly of
+//           DPP and row-swap permutes, then across waves through LDS.  Logits
+//           never leave the chip.
 //   kind 2  E > 16, bf16: MFMA 32x32x16 bf16 over 64-token x 64-expert tiles,
 //           K streamed through a deep direct-to-LDS pipeline (split while the
 //           grid is small), partial logits to the workspace; a second kernel,
