@@ -435,6 +435,11 @@ SMALL = [
     moe_synth.Spec("bf16_E1_k1", 200, 128, 1, 1, 128),
     moe_synth.Spec("bf16_k_eq_E", 90, 128, 4, 4, 64, wg_dtype="f32"),
     moe_synth.Spec("bf16_T1_E256", 1, 512, 256, 8, 128),
+    # the smallest hidden sizes the limits allow (H = I = 64), and H = 64 with fp32
+    moe_synth.Spec("bf16_H64_I64", 100, 64, 4, 2, 64, capacity_factor=1.25),
+    moe_synth.Spec("f32_H64_I128", 70, 64, 8, 3, 128, x_dtype="f32", wg_dtype="f32", w_dtype="f32",
+                   out_dtype="f32"),
+    moe_synth.Spec("i4_H128_I64", 90, 128, 4, 2, 64, w_dtype="i4"),
     # prefill tiles with a mostly empty last round: the down GEMM splits that
     # round's units over K (partial tiles summed by the reduce kernel)
     moe_synth.Spec("bf16_prefill_last_round_split", 1024, 512, 4, 2, 512),
