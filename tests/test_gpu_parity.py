@@ -153,6 +153,8 @@ ROUTE_PATHS = [
     (moe_synth.Spec("logits_e64_splitk", 16, 4096, 64, 6, 64), True, "route_gemm_kernel("),
     (moe_synth.Spec("logits_e128", 300, 1024, 128, 4, 64), False, "route_gemm_kernel("),
     (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel("),
+    # one expert tile and no K split (ragged last tile), with codes
+    (moe_synth.Spec("e48_codes_ragged", 1000, 128, 48, 6, 64, zipf_s=1.1), True, "route_gemm_kernel("),
 ]
 
 
