@@ -576,11 +576,15 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
   // first XPF*512 values) and its per-split absmax are fetched before the
   // selection, which they do not depend on, so their memory latency overlaps
   // the partial-logit loads.  Large batches keep the registers for occupancy.
+  // Every load of this prefetch is issued before the first use of any of
+  // them (loads complete in order, so an early use would wait for all).
   constexpr int QPF = QUANT ? XPF : 0;
+  constexpr int AMP = QPF >= 8 ? 16 : 1;   // per-split absmax values fetched early
   uint4 xr[QPF > 0 ? QPF : 1];
+  float amr[AMP];
   float am = 0.f;
-  auto load_amax = [&]() {
-    for (int z0 = 0; z0 < ks; z0 += 8) {
+  auto load_amax = [&](int z_begin) {
+    for (int z0 = z_begin; z0 < ks; z0 += 8) {
       float a[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) a[u] = z0 + u < ks ? amax_part[(size_t)(z0 + u) * T + t] : 0.f;
@@ -593,7 +597,15 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
 #pragma unroll
     for (int u = 0; u < QPF; ++u)
       if (lane * 8 + u * 512 < H) xr[u] = *reinterpret_cast<const uint4*>(xrow + lane * 8 + u * 512);
-    load_amax();
+#pragma unroll
+    for (int u = 0; u < AMP; ++u) amr[u] = u < ks ? amax_part[(size_t)u * T + t] : 0.f;
+  }
+  // the bias, fetched with the partial logits
+  float bv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    bv[j] = (bias && e < E) ? bias[e] : 0.f;
   }
   // the K-split partial logits, ZC splits per batch of loads (one batch, so
   // one memory latency, for up to ZC splits), summed in split order
@@ -617,7 +629,7 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? v[j] + (bias ? bias[e] : 0.f) : -INFINITY;
+    v[j] = e < E ? v[j] + bv[j] : -INFINITY;
   }
   if constexpr (GROUPED) {
     wave_grouped_topk_store(v, grow, gscore, E, k, n_group, topk_group, t, ids, w, prob);
@@ -629,7 +641,13 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
     wave_topk_store(v, E, k, t, ids, w, prob);
   }
   if constexpr (QUANT) {
-    if constexpr (QPF == 0) load_amax();
+    if constexpr (QPF == 0) {
+      load_amax(0);
+    } else {
+#pragma unroll
+      for (int u = 0; u < AMP; ++u) am = fmaxf(am, amr[u]);
+      load_amax(AMP);   // splits past the first 16, if any
+    }
     const float s = row_scale(am);
     const float rs = 1.f / s;
     const uint16_t* xrow = x + t * H;
