@@ -180,9 +180,10 @@ moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32
  *     Y[r]  = w * (W2[e] h[r]),  w = topk_w[s] (1 if topk_w is NULL)
  *   act_dtype MOE_F32 / MOE_BF16: a_t = x[t] (w_dtype must equal act_dtype)
  *   act_dtype MOE_I8 (W8A8, w_dtype MOE_I8): a_t = xq[t] with scale xs[t];
- *     int32 accumulation, dequantised by xs[t] * s13[e][n]; h is quantised
- *     per row with the per-token rule before the second GEMM, whose int32
- *     result is scaled by that row scale * s2[e][n]  ([LightOP] section 4.1)
+ *     int32 accumulation, dequantised by xs[t] * s13[e][n]; h, rounded to
+ *     bf16, is quantised per row with the per-token rule before the second
+ *     GEMM, whose int32 result is scaled by that row scale * s2[e][n]
+ *     ([LightOP] section 4.1)
  *   act_dtype MOE_BF16 with w_dtype MOE_I4 (W4A16, [LightOP] section 4.3):
  *     a_t = x[t]; each weight is its int4 code (in [-8, 7]) times the
  *     per-output-channel scale s13[e][n] or s2[e][n]; bf16 MFMA with fp32

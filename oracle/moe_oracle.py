@@ -40,7 +40,10 @@ R6  expert FFN is SwiGLU: W2 (silu(W1 x) * W3 x), no biases, silu(z)=z/(1+e^-z);
 R7  W8A8: activations quantised per token with the LightOP rule, int8 weights
     carry one fp32 scale per output channel, the int GEMM result is scaled by
     (activation scale of the row) * (weight scale of the column); the FFN's
-    second GEMM quantises h the same way, one scale per row of h.
+    second GEMM quantises h the same way, one scale per row of h.  The page
+    fixes no precision for h between the two GEMMs; h is taken in bf16, the
+    layer's activation dtype (formed in fp32, rounded to nearest even), and
+    the codes and row scale are those of the rounded values.
 R8  MoE Sum's fused shared-expert factor and bias ([LightOP] section 3.2) add
     shared_factor * S[t] (the shared expert's output for token t) and a
     per-column bias b to the routed sum; the page names the fusion only.
@@ -74,7 +77,7 @@ __all__ = [
     "to_f64", "gate_logits", "softmax_rows", "topk_rows", "renormalise", "route",
     "quant_per_token_int8", "capacity", "align", "tiles", "silu", "swiglu_ffn",
     "layer", "layer_from_inputs", "layer_token_major", "combine", "combine_shared",
-    "group_scores", "route_grouped", "dequant_rows",
+    "group_scores", "route_grouped", "dequant_rows", "round_bf16",
 ]
 
 
@@ -306,15 +309,25 @@ def _w8a8_ffn(xq: np.ndarray, xs: np.ndarray, w13q: np.ndarray, s13: np.ndarray,
     """One expert's SwiGLU in W8A8 (R7, [LightOP] section 4.1 w8a8_gemm_smooth).
 
     The integer products are exact in float64 (|acc| < 2^53); h is formed in
-    float64, rounded to fp32 and re-quantised per row with the same rule.
+    float64, rounded to fp32, then to bf16 (R7), and re-quantised per row
+    with the same rule.
     """
     acc1 = xq.astype(np.float64) @ w13q.astype(np.float64).T          # exact integers
     deq = acc1 * xs.astype(np.float64)[:, None] * s13.astype(np.float64)[None, :]
     g, u = deq[:, :I], deq[:, I:]
-    h32 = (silu(g) * u).astype(np.float32)
-    hq, hs = quant_per_token_int8(h32)
+    h16 = round_bf16((silu(g) * u).astype(np.float32))
+    hq, hs = quant_per_token_int8(h16)
     acc2 = hq.astype(np.float64) @ w2q.astype(np.float64).T           # exact integers
     return acc2 * hs.astype(np.float64)[:, None] * s2.astype(np.float64)[None, :]
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), as fp32: keep
+    the top 16 bits after adding half an ulp of bf16 plus the kept lsb.
+    Finite inputs only."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
 
 
 def dequant_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:

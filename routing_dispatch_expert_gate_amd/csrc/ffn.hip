@@ -31,9 +31,10 @@
 //  * The down GEMM multiplies each output row by its route weight before the
 //    single bf16 rounding, so the combine only sums.
 //  * W8A8: the up epilogue dequantises with the token and channel scales,
-//    writes h in fp32 and folds each row's max |h| in with an integer atomic
-//    max (non-negative floats order like their bit patterns); a row pass then
-//    quantises h with the per-token rule, and the down GEMM runs int8 MFMA.
+//    writes h in bf16 (the activation dtype of the layer) and folds the
+//    stored values' row max |h| in with an integer atomic max (non-negative
+//    floats order like their bit patterns); a row pass then quantises the
+//    stored h with the per-token rule, and the down GEMM runs int8 MFMA.
 //  * W4A16 (LightOP page, section 4.3, INT4 weights with 16-bit
 //    activations): weights are int4 codes, two per byte along K (low nibble
 //    first), with one fp32 scale per output channel.  B tiles are copied to
@@ -600,7 +601,7 @@ void gg_kernel(const GemmArgs a) {
       }
     }
   } else if constexpr (UP) {
-    float* h = reinterpret_cast<float*>(a.out);
+    uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
     float sg[NF / 2], su[NF / 2];
 #pragma unroll
     for (int f = 0; f < NF / 2; ++f) {
@@ -622,9 +623,10 @@ void gg_kernel(const GemmArgs a) {
           const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
           const float gv = (float)acc[fm][f][v] * xsr * sg[f];
           const float uv = (float)acc[fm][NF / 2 + f][v] * xsr * su[f];
-          const float hv = silu_f32(gv) * uv;
-          if (valid) h[(int64_t)(r0 + row) * a.I + col] = hv;
-          m = fmaxf(m, fabsf(hv));
+          // h is stored in bf16; the row maximum is that of the stored values
+          const uint32_t hb = f32_to_bf16_bits(silu_f32(gv) * uv);
+          if (valid) h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)hb;
+          m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
         }
         m = row_max16(m);                              // 16 lanes by DPP,
         m = fmaxf(m, lane_xor16(m));                   // then the other row of the half
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const GemmArgs a) {
 // One wave per sorted row: s = max|h| / 127 (1 if 0), q = round-half-even(h / s)
 // clamped to [-128, 127]; fp32 IEEE arithmetic.  The tile list covers rows
 // [0, N) in order, so N is the end of the last tile; waves past it exit.
-__global__ __launch_bounds__(256) void quant_h_kernel(const float* __restrict__ h,
+__global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict__ h,
                                                       const uint32_t* __restrict__ rowmax,
                                                       const int32_t* __restrict__ tiles,
                                                       const int32_t* __restrict__ num_tiles, int I,
@@ -818,8 +820,8 @@ constexpr size_t kTailBytes = (size_t)kTailParts * 256 * 256 * 4;
 FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int down_var) {
   uint8_t* wsb = (uint8_t*)ws;
   FfnBufs b{wsb, nullptr, nullptr, nullptr, nullptr};
-  const bool a8 = w_dtype == kI8 || w_dtype == kI4A8;   // int8 activations: fp32 h, then hq
-  size_t off = align256((size_t)n * I * (a8 ? 4 : 2));
+  const bool a8 = w_dtype == kI8 || w_dtype == kI4A8;   // int8 activations: bf16 h, then hq
+  size_t off = align256((size_t)n * I * (w_dtype == kF32 ? 4 : 2));
   if (a8) {
     b.rowmax = (uint32_t*)(wsb + off);
     off += align256((size_t)n * 4);
@@ -989,7 +991,7 @@ hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const 
                        const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int64_t rows,
                        int H, int I, void* y, const FfnBufs& b, hipStream_t s) {
   if (I8)
-    quant_h_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>((const float*)b.h, b.rowmax, tiles,
+    quant_h_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>((const uint16_t*)b.h, b.rowmax, tiles,
                                                               num_tiles, I, b.hq, b.hs);
   GemmArgs a{};
   a.act = I8 ? (const uint8_t*)b.hq : (const uint8_t*)b.h;
@@ -1067,7 +1069,7 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     if (w_dtype == kI4)
       p.ws_bytes = align256((size_t)n * I * 2);
     else
-      p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
+      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4) + align256((size_t)n * I) +
                    align256((size_t)n * 4);
   } else {
     // shape class from the mean rows per expert: decode-sized (weight
@@ -1089,7 +1091,7 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     if (w_dtype == kBF16)
       p.ws_bytes = align256((size_t)n * I * 2);
     else
-      p.ws_bytes = align256((size_t)n * I * 4) + align256((size_t)n * 4) + align256((size_t)n * I) +
+      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4) + align256((size_t)n * I) +
                    align256((size_t)n * 4);
     if (p.down_var == 0) p.ws_bytes += kTailBytes;
   }

@@ -566,3 +566,23 @@ def test_layer_options_compose_the_pinned_steps():
     np.testing.assert_array_equal(res["route"]["ids"], r["ids"])
     plain = oracle.layer(**_layer(inp, n_group=4, topk_group=2))
     np.testing.assert_allclose(res["out"], plain["out"] + 0.5 * S + b[None, :], rtol=1e-12, atol=1e-12)
+
+
+def test_round_bf16_is_nearest_with_ties_to_even():
+    """round_bf16 (R7's h storage) against brute force: of the two bf16
+    values around x (x truncated to 16 bits, and the next one up in
+    magnitude), the nearer, and the one with an even last bit on a tie."""
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(4000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 4000),
+                        np.float32([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), 0.0, -0.0])])
+    got = oracle.round_bf16(x)
+    for xi, gi in zip(x.tolist(), got.tolist()):
+        b = np.float32(xi).view(np.uint32)
+        lo = np.uint32(b & 0xFFFF0000)
+        hi = np.uint32(lo + 0x10000)
+        flo, fhi = float(lo.view(np.float32)), float(hi.view(np.float32))
+        dlo, dhi = abs(xi - flo), abs(fhi - xi)
+        want = flo if (dlo < dhi or (dlo == dhi and ((int(lo) >> 16) & 1) == 0)) else fhi
+        assert gi == want, (xi, gi, want)
+    assert oracle.round_bf16(np.float32([1 + 2.0 ** -8]))[0] == 1.0
+    assert oracle.round_bf16(np.float32([1 + 3 * 2.0 ** -8]))[0] == np.float32(1 + 2.0 ** -6)
