@@ -370,7 +370,7 @@ def main() -> int:
     bh = 1 if spec.w_dtype in A8 else by                    # h bytes the down GEMM reads
     up_flops = 4.0 * N * H * I
     down_flops = 2.0 * N * H * I
-    up_bytes = D * 2 * I * H * bw + N * H * ba + N * I * (4 if spec.w_dtype in A8 else by)
+    up_bytes = D * 2 * I * H * bw + N * H * ba + N * I * by      # h is written in bf16 (fp32 for f32)
     down_bytes = D * H * I * bw + N * I * bh + N * H * by
     route_bytes = T * H * bx + E * H * bg + 8 * T * k + (T * H + 4 * T if spec.w_dtype in A8 else 0)
     align_bytes = 12 * T * k
