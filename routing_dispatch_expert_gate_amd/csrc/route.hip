@@ -842,7 +842,9 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
   const int64_t blocks = ((T + kRT - 1) / kRT) * ((E + kRE - 1) / kRE);
   // split K while the grid is small: each split keeps >= 2 stages of 64 values
   int ks = 1;
-  while (blocks * ks < 256 && H % (128 * ks) == 0 && H >= 256 * ks) ks *= 2;
+  // (at most 16 splits: the top-k of a small batch loads 16 at once;
+  // T=16, E=256: 32 splits 11.2 us, 16 splits 9.6 us, 8 splits 10.6 us)
+  while (blocks * ks < 256 && H % (128 * ks) == 0 && H >= 256 * ks && ks < 16) ks *= 2;
   p.ks = ks;
   p.ws_bytes = route_part_bytes(T, E, ks) + (size_t)ks * (size_t)T * sizeof(float);
   return p;
