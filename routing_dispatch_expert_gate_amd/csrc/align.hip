@@ -21,12 +21,12 @@
 //      by popcount of the lower lanes.  Ranks therefore come from an ordered
 //      scan, never from the order atomics return in, so every output is
 //      deterministic.
-// Up to kOneBlockSlots slots the three steps run in one workgroup of sixteen
-// waves instead (align_one_block_kernel, block_align.h): each wave loads a
-// contiguous sixteenth of the ids into registers at once, counts them in its
-// own LDS histogram, wave 0 scans, and each wave ranks its sixteenth from the
-// same registers.  One launch instead of three: at these sizes the launches
-// cost more than the work.
+// Up to kOneBlockSlots slots the three steps run in one workgroup of up to
+// sixteen waves instead (align_one_block_kernel, block_align.h; one wave per
+// 512 slots): each wave loads a contiguous share of the ids into registers
+// at once, counts them in its own LDS histogram, wave 0 scans, and each wave
+// ranks its share from the same registers.  One launch instead of three: at
+// these sizes the launches cost more than the work.
 #include "block_align.h"
 #include "moe_internal.h"
 
@@ -253,8 +253,13 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
   int ebits = 0;
   while ((1 << ebits) < E) ++ebits;
   if (p.nblocks == 0) {
-    align_one_block_kernel<<<1, kOneThreads, 0, s>>>(ids, n, E, ebits, cap, block_m, max_tiles, counts,
-                                                     offsets, sorted_slot, pos, tiles, num_tiles, num_dropped);
+    // one wave per 512 slots (8 per lane), 1 to 16 waves: wave 0's scan
+    // over the per-wave counts is serial in the wave count, so a small batch
+    // (decode: 128 slots) runs in one wave
+    const int64_t nw = (n + 511) / 512 < 1 ? 1 : ((n + 511) / 512 > kOneWaves ? kOneWaves : (n + 511) / 512);
+    align_one_block_kernel<<<1, (unsigned)(64 * nw), 0, s>>>(ids, n, E, ebits, cap, block_m, max_tiles, counts,
+                                                             offsets, sorted_slot, pos, tiles, num_tiles,
+                                                             num_dropped);
     return hipGetLastError();
   }
   int32_t* bhist = (int32_t*)ws;
