@@ -38,15 +38,16 @@
 //  * W4A16 (LightOP page, section 4.3, INT4 weights with 16-bit
 //    activations): weights are int4 codes, two per byte along K (low nibble
 //    first), with one fp32 scale per output channel.  B tiles are copied to
-//    LDS packed (a quarter of the bf16 bytes), each lane reads its fragment's
-//    eight codes as one 32-bit word and widens them exactly to bf16 in
-//    registers, and the MFMAs are the bf16 ones; the epilogue applies the
-//    channel scales (before SwiGLU in the up GEMM).
+//    LDS packed (a quarter of the bf16 bytes); each lane reads its codes for
+//    all four K substeps of a stage as one swizzled 16-byte chunk (the MFMA's
+//    K slots are reordered alike for A and B), widens each substep's eight
+//    codes exactly to bf16 in registers, and the MFMAs are the bf16 ones;
+//    the epilogue applies the channel scales (before SwiGLU in the up GEMM).
 //  * W4A8 (same section, INT4 weights with INT8 activations): the W8A8 path
 //    with the same packed int4 B tiles (half the int8 bytes); each lane reads
-//    its sixteen codes as one 64-bit word and widens them to int8 (nibbles
-//    masked into bytes, sign-extended by a multiply that cannot carry, and
-//    put back in K order with two byte permutes per word).
+//    two swizzled 16-byte chunks per stage and widens each substep's sixteen
+//    codes to int8 (nibbles masked into bytes, sign-extended by a multiply
+//    that cannot carry, and put back in K order with two byte permutes).
 #include <math.h>
 #include <stdio.h>
 
@@ -164,7 +165,7 @@ struct GemmArgs {
   const float* wscale;         // W8A8: per-output-channel weight scale, [E, 2I] up / [E, H] down
   const float* hs;             // down, W8A8: per-row scale of h
   const float* topk_w;         // down: route weight per slot (NULL: 1)
-  void* out;                   // up: h [rows, I] (bf16; fp32 for W8A8); down: y [rows, H] bf16
+  void* out;                   // up: h [rows, I] bf16; down: y [rows, H] bf16
   uint32_t* rowmax;            // up, W8A8: max |h| of each row (bit pattern of a non-negative float)
                                // (W4A16: wscale as for W8A8, w packed two codes per byte)
   void* partial;               // down, last-round split: raw partial tiles [conc][BM * BN]
@@ -1074,7 +1075,7 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
   } else {
     // shape class from the mean rows per expert: decode-sized (weight
     // streaming, short tiles), mid (one 256-row tile per expert, waves split
-    // N), prefill (256 x 256 tiles, 2 x 2 waves of 128 x 128)
+    // N), prefill (256 x 256 tiles, 4 x 4 waves of 64 x 64)
     const double mean_rows = (double)n / E;
     const int cls = mean_rows <= 24.0 ? 2 : (mean_rows <= 192.0 ? 1 : 0);
     p.up_var = (I % 128 == 0 ? 0 : 3) + cls;
