@@ -558,13 +558,13 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
   }
 }
 
-// One wave per token: sums the K splits of its logits in a fixed order (8
-// splits' loads in flight), adds the bias, selects the top-k (by rank from an
-// LDS row when E <= 64, else by argmax rounds) and, with quantisation, writes
-// the token's codes with the absmax the logits kernel folded.
 // One wave: the top-k (and, with quantisation, the int8 codes) of token t.
-// lrow: this wave's 64-float LDS row; grow/gscore: its 256- and 64-float rows
-// for the group-limited selection.
+// Sums the K splits of its logits in a fixed order (ZC splits' loads in
+// flight), adds the bias, selects the top-k (by rank from an LDS row when
+// E <= 64, else by argmax rounds) and, with quantisation, writes the token's
+// codes with the absmax the logits kernel folded (XPF x chunks of the row
+// fetched before the selection).  lrow: this wave's 64-float LDS row;
+// grow/gscore: its 256- and 64-float rows for the group-limited selection.
 template <bool QUANT, bool GROUPED, int XPF, int ZC>
 __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
                            const float* __restrict__ bias, int64_t T, int E, int k, int H,
