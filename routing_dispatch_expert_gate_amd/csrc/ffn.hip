@@ -207,6 +207,35 @@ __device__ __forceinline__ int2 raster(int L0, int nt, int n_blocks) {
   return make_int2(tile, g * GN + (rem - tile * gs));
 }
 
+// Max of each of 16 values over the 16 lanes of each 16-lane row, by a
+// butterfly over lane bits 3, 2, 1, 0 (DPP row_mirror, row_half_mirror,
+// quad_perm xor 2 and xor 1; each step's partner differs in that bit): a lane
+// keeps the half of its values its bit selects and takes the partner's copy
+// of that half.  Lane l returns the max of value l % 16.
+template <int S>
+__device__ __forceinline__ float bfly16_partner(float v) {
+  if constexpr (S == 0) return dpp_f32<0x140>(v);
+  else if constexpr (S == 1) return dpp_f32<0x141>(v);
+  else if constexpr (S == 2) return dpp_f32<0x4E>(v);
+  else return dpp_f32<0xB1>(v);
+}
+template <int S = 0>
+__device__ __forceinline__ float rows_max16x16(float (&m)[16], int lane) {
+  if constexpr (S == 4) {
+    return m[0];
+  } else {
+    constexpr int h = 8 >> S;
+    const bool up = ((lane >> (3 - S)) & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = up ? m[i] : m[i + h];
+      const float keep = up ? m[i + h] : m[i];
+      m[i] = fmaxf(keep, bfly16_partner<S>(send));
+    }
+    return rows_max16x16<S + 1>(m, lane);
+  }
+}
+
 // One BM x BN output tile of one row tile (one expert).  Waves form a WM x WN
 // grid; each owns (BM/WM) x (BN/WN) outputs as 32x32 MFMA fragments; with
 // four waves per SIMD one wave's MFMAs cover another's copy and LDS waits.
@@ -613,6 +642,7 @@ void gg_kernel(const GemmArgs a) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
+      float mv[16];   // per accumulator row v: max |h| over this lane's columns
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
@@ -629,10 +659,17 @@ void gg_kernel(const GemmArgs a) {
           if (valid) h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)hb;
           m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
         }
-        m = row_max16(m);                              // 16 lanes by DPP,
-        m = fmaxf(m, lane_xor16(m));                   // then the other row of the half
-        if (valid && (lane & 31) == 0) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
+        mv[v] = m;
       }
+      // the 16 rows' maxima over the 32 columns of each half-wave at once:
+      // lane l ends with row v = l % 16 over its 16-lane row, the other
+      // 16-lane row of the half is folded in, and one atomic instruction
+      // (16 lanes per half) publishes them
+      const int v = lane & 15;
+      const float r16 = rows_max16x16(mv, lane);
+      const float m = fmaxf(r16, lane_xor16(r16));
+      const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
+      if ((lane & 16) == 0 && row < rows) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
     }
   } else {
     uint16_t* y = reinterpret_cast<uint16_t*>(a.out);
