@@ -21,14 +21,16 @@ constexpr int kMaxK = 8;
 // ---------------------------------------------------------------- numerics
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+// fp32 -> bf16 bit pattern, round to nearest even: gfx950's
+// v_cvt_pk_bf16_f32 (one instruction for two values)
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_hw r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp): the
