@@ -109,8 +109,8 @@ std::string route_name(const moe::RoutePlan& p) {
   if (p.kind == 0)
     snprintf(b, sizeof b, "route_fma_kernel(tokens/wg=%d,waves=%d)", p.bt, p.nw);
   else
-    snprintf(b, sizeof b, "route_gemm_kernel(tokens/wg=%d,experts/wg=64,ksplit=%d)+route_topk_kernel", p.bt,
-             p.ks);
+    snprintf(b, sizeof b, "route_gemm_kernel(tokens/wg=%d,experts/wg=%d,ksplit=%d)+route_topk_kernel", p.bt,
+             p.be, p.ks);
   return b;
 }
 

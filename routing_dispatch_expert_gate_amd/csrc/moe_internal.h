@@ -208,6 +208,7 @@ struct RoutePlan {
   int ks;        // K splits (kind 2)
   int nw;        // waves per workgroup (kind 0)
   size_t ws_bytes;
+  int be;        // experts per workgroup (kind 2)
 };
 RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype);
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,

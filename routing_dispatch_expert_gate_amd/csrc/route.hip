@@ -433,55 +433,64 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
 }
 
 // ------------------------------------------------------------ kind 2 -----
-// Gate logits on MFMA: one workgroup computes a 64-token x 64-expert tile of
-// x Wg^T over a K range (all of H unless split).  K is streamed 64 bf16 (128
-// bytes) per stage from global memory straight into LDS, kRS stages deep;
-// waves form a 2 x 2 grid, each owning one 32 x 32 MFMA 32x32x16 fragment.
-// Token rows past T and expert rows past E copy a valid row; their results
-// are never used.  The tile is written to the workspace; with quantisation
-// the first expert block also folds each token row's absmax over its K range
-// from the A stages as they pass through LDS.  route_topk_kernel then sums
-// the K splits, runs the top-k and writes the codes, one wave per token.
-constexpr int kRT = 64;                        // tokens per tile
-constexpr int kRE = 64;                        // experts per tile
+// Gate logits on MFMA: one workgroup computes an RT-token x RE-expert tile
+// of x Wg^T over a K range (all of H unless split).  K is streamed 64 bf16
+// (128 bytes) per stage from global memory straight into LDS, as many stages
+// deep as 128 KiB holds; waves form a 2 x 2 grid, each owning (RT/2) x (RE/2)
+// outputs as 32 x 32 MFMA 32x32x16 fragments.  Token rows past T and expert
+// rows past E copy a valid row; their results are never used.  The tile is
+// written to the workspace; with quantisation the first expert block also
+// folds each token row's absmax over its K range from the A stages as they
+// pass through LDS.  route_topk_kernel then sums the K splits, runs the top-k
+// and writes the codes, one wave per token.
+// Tiles: 64 x 64, K split while the grid is small; at large batches with E
+// a multiple of 128, 128 x 128 split in K back up to a full grid: each
+// workgroup then reads half the bytes per output of a 64 x 64 tile, which is
+// what bounds the step (each CU's copy rate), for more partial logits.
+constexpr int kRT = 64;                        // tokens per tile (small batches)
+constexpr int kRE = 64;                        // experts per tile (small batches)
 constexpr int kRRow = 128;                     // bytes of K per stage row
-constexpr int kRS = 8;                         // stages
-constexpr int kRStage = (kRT + kRE) * kRRow;   // 16 KiB
-constexpr int kRL = (kRT + kRE) * kRRow / 1024 / 4;   // 1 KiB copies per wave per stage
+constexpr int kRLds = 128 * 1024;              // bytes of stages
 
 // workspace: partial logits [ks][T][E] fp32, then per-split row absmax [ks][T]
 size_t route_part_bytes(int64_t T, int E, int ks) {
   return ((size_t)ks * (size_t)T * (size_t)E * sizeof(float) + 255) & ~(size_t)255;
 }
 
-template <bool QUANT>
+template <bool QUANT, int RT, int RE>
 __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restrict__ x,
                                                         const uint16_t* __restrict__ wg, int64_t T,
                                                         int H, int E, int kchunk,
                                                         float* __restrict__ part,
                                                         float* __restrict__ amax_part) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kRS * kRStage];
+  constexpr int STAGE = (RT + RE) * kRRow;
+  constexpr int RS = kRLds / STAGE;              // stages
+  constexpr int RL = STAGE / 1024 / 4;           // 1 KiB copies per wave per stage
+  constexpr int FR = RT / 64, FE = RE / 64;      // fragments per wave
+  static_assert(RL * 4 * 1024 == STAGE && RS >= 3, "stages");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
-  const int64_t t0 = (int64_t)blockIdx.x * kRT;
-  const int e0 = blockIdx.y * kRE;
+  const int64_t t0 = (int64_t)blockIdx.x * RT;
+  const int e0 = blockIdx.y * RE;
   const int64_t rowbytes = (int64_t)H * 2;
   const int nk = kchunk / kRRow;
 
-  // this wave's copies: 1 KiB block q = wv*kRL + j holds stage rows 8q..8q+7
-  // (rows 0..63 tokens, 64..127 experts); lane i copies row 8q + i/8, LDS
+  // this wave's copies: 1 KiB block q = wv*RL + j holds stage rows 8q..8q+7
+  // (rows [0, RT) tokens, then RE experts); lane i copies row 8q + i/8, LDS
   // chunk i%8, which holds logical chunk (i%8) ^ sw(row)
-  const uint8_t* src[kRL];
+  const uint8_t* src[RL];
 #pragma unroll
-  for (int j = 0; j < kRL; ++j) {
-    const int q = wv * kRL + j;
+  for (int j = 0; j < RL; ++j) {
+    const int q = wv * RL + j;
     const int srow = q * 8 + (lane >> 3);
-    const int trow = srow & 63;
+    const bool tok = srow < RT;
+    const int trow = tok ? srow : srow - RT;
     const int c = (lane & 7) ^ swr<kRRow>(trow);
     int64_t grow;
     const uint8_t* base;
-    if (srow < kRT) {
+    if (tok) {
       grow = t0 + trow < T ? t0 + trow : T - 1;
       base = reinterpret_cast<const uint8_t*>(x);
     } else {
@@ -491,11 +500,11 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
     src[j] = base + grow * rowbytes + (int64_t)blockIdx.z * kchunk + c * 16;
   }
   auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % kRS) * kRStage;
+    uint8_t* st = smem + (kt % RS) * STAGE;
 #pragma unroll
-    for (int j = 0; j < kRL; ++j)
+    for (int j = 0; j < RL; ++j)
       __builtin_amdgcn_global_load_lds((glb_void*)(src[j] + kt * kRRow),
-                                       (lds_void*)(st + (wv * kRL + j) * 1024), 16, 0, 0);
+                                       (lds_void*)(st + (wv * RL + j) * 1024), 16, 0, 0);
   };
   int lo[4];
 #pragma unroll
@@ -503,33 +512,43 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
     const int r = lane & 31;
     lo[s] = r * kRRow + (((2 * s + (lane >> 5)) ^ swr<kRRow>(r)) << 4);
   }
-  // quantisation: thread tid folds |x| of stage row tid/4, 16 values
-  const int qrow = tid >> 2;
-  int qoff[2];
+  // quantisation: TPR threads fold |x| of each stage token row, CPT 16-byte
+  // chunks each
+  constexpr int TPR = 256 / RT, CPT = 8 / TPR;
+  const int qrow = tid / TPR;
+  int qoff[CPT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) qoff[i] = qrow * kRRow + (((2 * (tid & 3) + i) ^ swr<kRRow>(qrow)) << 4);
+  for (int i = 0; i < CPT; ++i) qoff[i] = qrow * kRRow + (((CPT * (tid % TPR) + i) ^ swr<kRRow>(qrow)) << 4);
   uint32_t amax = 0;   // bf16 magnitude bits
 
-  f32x16 acc = {};
+  f32x16 acc[FR][FE];
 #pragma unroll
-  for (int p = 0; p < kRS - 1; ++p)
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FE; ++j) acc[i][j] = f32x16{};
+#pragma unroll
+  for (int p = 0; p < RS - 1; ++p)
     if (p < nk) issue(p);
   for (int kt = 0; kt < nk; ++kt) {
-    const int after = nk - 1 - kt < kRS - 2 ? nk - 1 - kt : kRS - 2;
-    wait_vm_stages<kRL, kRS - 2>(after);
+    const int after = nk - 1 - kt < RS - 2 ? nk - 1 - kt : RS - 2;
+    wait_vm_stages<RL, RS - 2>(after);
     lds_barrier();
-    if (kt + kRS - 1 < nk) issue(kt + kRS - 1);
-    const uint8_t* As = smem + (kt % kRS) * kRStage;
-    const uint8_t* Bs = As + kRT * kRRow;
-    u32x4 af[4], bf[4];
+    if (kt + RS - 1 < nk) issue(kt + RS - 1);
+    const uint8_t* As = smem + (kt % RS) * STAGE;
+    const uint8_t* Bs = As + RT * kRRow;
+    u32x4 af[4][FR], bf[4][FE];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      af[s] = *reinterpret_cast<const u32x4*>(As + wm * 32 * kRRow + lo[s]);
-      bf[s] = *reinterpret_cast<const u32x4*>(Bs + wn * 32 * kRRow + lo[s]);
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+        af[s][i] = *reinterpret_cast<const u32x4*>(As + (wm * (RT / 2) + 32 * i) * kRRow + lo[s]);
+#pragma unroll
+      for (int j = 0; j < FE; ++j)
+        bf[s][j] = *reinterpret_cast<const u32x4*>(Bs + (wn * (RE / 2) + 32 * j) * kRRow + lo[s]);
     }
     if constexpr (QUANT) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < CPT; ++i) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(As + qoff[i]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -540,20 +559,32 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[s]),
-                                                    __builtin_bit_cast(bf16x8, bf[s]), acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int j = 0; j < FE; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[s][i]),
+                                                              __builtin_bit_cast(bf16x8, bf[s][j]), acc[i][j], 0, 0,
+                                                              0);
   }
 
-  const int e = e0 + wn * 32 + (lane & 31);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t t = t0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[v];
+  for (int j = 0; j < FE; ++j) {
+    const int e = e0 + wn * (RE / 2) + 32 * j + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t t = t0 + wm * (RT / 2) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[i][j][v];
+      }
   }
   if constexpr (QUANT) {
+    // the TPR threads of a row are adjacent lanes
     amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-    amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));   // lane ^ 2
-    if (blockIdx.y == 0 && (tid & 3) == 0 && t0 + qrow < T)
+    if constexpr (TPR == 4)
+      amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    if (blockIdx.y == 0 && tid % TPR == 0 && t0 + qrow < T)
       amax_part[(int64_t)blockIdx.z * T + t0 + qrow] = __uint_as_float(amax << 16);
   }
 }
@@ -789,11 +820,18 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
   const uint16_t* wb = (const uint16_t*)wg;
   float* part = (float*)ws;
   float* amax_part = (float*)((uint8_t*)ws + route_part_bytes(T, E, p.ks));
-  const dim3 grid((unsigned)((T + kRT - 1) / kRT), (unsigned)((E + kRE - 1) / kRE), (unsigned)p.ks);
-  if (xq)
-    route_gemm_kernel<true><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
-  else
-    route_gemm_kernel<false><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
+  const dim3 grid((unsigned)((T + p.bt - 1) / p.bt), (unsigned)((E + p.be - 1) / p.be), (unsigned)p.ks);
+#define MOE_RG(RT, RE)                                                                                        \
+  if (xq)                                                                                                   \
+    route_gemm_kernel<true, RT, RE><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part); \
+  else                                                                                                      \
+    route_gemm_kernel<false, RT, RE><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
+  if (p.bt == 128) {
+    MOE_RG(128, 128)
+  } else {
+    MOE_RG(64, 64)
+  }
+#undef MOE_RG
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (al) {
@@ -838,8 +876,16 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
   }
   if (x_dtype != kBF16 || wg_dtype != kBF16 || E % 16 != 0 || E > kMaxE) return p;
   p.bt = kRT;
+  p.be = kRE;
   p.kind = 2;
-  const int64_t blocks = ((T + kRT - 1) / kRT) * ((E + kRE - 1) / kRE);
+  int64_t blocks = ((T + kRT - 1) / kRT) * ((E + kRE - 1) / kRE);
+  if (blocks >= 256 && E % 128 == 0) {
+    // large batch: 128 x 128 tiles, split in K back up to a full grid (at
+    // E = 64 the 128 x 64 tile measured no faster than 64 x 64)
+    p.bt = 128;
+    p.be = 128;
+    blocks = ((T + 127) / 128) * (E / 128);
+  }
   // split K while the grid is small: each split keeps >= 2 stages of 64 values
   int ks = 1;
   // (at most 16 splits: the top-k of a small batch loads 16 at once;

@@ -155,6 +155,15 @@ ROUTE_PATHS = [
     (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel("),
     # one expert tile and no K split (ragged last tile), with codes
     (moe_synth.Spec("e48_codes_ragged", 1000, 128, 48, 6, 64, zipf_s=1.1), True, "route_gemm_kernel("),
+    # large batches: 128 x 128 tiles split in K (ragged last token tile, codes
+    # folded by two threads per row); E not a multiple of 128 keeps 64 x 64
+    # (a full grid without a split; at E = 80 the second expert tile mostly
+    # past E)
+    (moe_synth.Spec("big_e256_codes", 4096 + 37, 512, 256, 8, 64), True,
+     "tokens/wg=128,experts/wg=128,ksplit=4)"),
+    (moe_synth.Spec("big_e64_codes", 16384 + 5, 1024, 64, 6, 64, zipf_s=1.1), True,
+     "tokens/wg=64,experts/wg=64,ksplit=1)"),
+    (moe_synth.Spec("big_e80", 8300, 256, 80, 4, 64), False, "tokens/wg=64,experts/wg=64,ksplit=1)"),
 ]
 
 
