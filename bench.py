@@ -255,7 +255,7 @@ def cpu_baseline(cfg: int, sample_n: int, spec=None) -> dict:
 def main() -> int:
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the MoE path has no multi-GPU code); got --gpus {args.gpus}",
               file=sys.stderr)
         return 2
     import torch
