@@ -19,6 +19,7 @@ Prints exactly one JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -360,6 +361,23 @@ def main() -> int:
     torch.cuda.synchronize()
     copy_GBps = 5 * 2 * flush.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del flush, dst
+    # measured MFMA rate: a dense loop of MFMA 32x32x16 bf16 from registers
+    # (one workgroup of 4 waves per CU), best of three launches
+    probe = torch.empty(256 * 256, device="cuda")
+    pst = moe.binding._stream(probe.device)
+    mfma_iters, mfma_best = 20000, float("inf")
+    for _ in range(4):
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        rc = moe.lib.moe_probe_mfma_rate(256, mfma_iters, ctypes.c_void_p(probe.data_ptr()), pst)
+        m1.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError("moe_probe_mfma_rate: " + moe.lib.moe_last_error().decode())
+        mfma_best = min(mfma_best, m0.elapsed_time(m1))
+    mfma_TFLOPs = 256 * mfma_iters * 4 * 16 * 32768 / (mfma_best * 1e-3) / 1e12
+    del probe
+    log(f"measured: copy {copy_GBps:.0f} GB/s, dense MFMA bf16 loop {mfma_TFLOPs:.0f} TFLOP/s")
     lib_ref = library_gemm_reference(torch, spec, d, N, D) if not args.no_library_ref else None
 
     # algorithmic work (bytes / flops the method must move or do)
@@ -409,6 +427,7 @@ def main() -> int:
         "layer_ms_p10_p50_p90": [float(np.percentile(per_step, 10)), float(np.median(per_step)),
                                  float(np.percentile(per_step, 90))],
         "measured_copy_GBps": copy_GBps,
+        "measured_mfma_bf16_TFLOPs": mfma_TFLOPs,
         "library_bmm_same_shapes": lib_ref,
         "kept_rows_N": N, "active_experts_D": D, "capacity": C,
         "layer_gpu_ms": gpu_ms,

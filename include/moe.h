@@ -347,6 +347,16 @@ const char* moe_last_error(void);
 const char* moe_last_dispatch(void);
 const char* moe_version(void);
 
+/* moe_probe_mfma_rate: a diagnostic outside the MoE path, for stating a
+ * measured MFMA peak beside the published one.  Enqueues one kernel of
+ * `blocks` workgroups of 4 waves; every wave runs iters x 16 MFMA 32x32x16
+ * bf16 instructions from registers only (no memory traffic, no LDS), then
+ * each thread writes one float to out[blocks * 256] (device, caller-owned).
+ * Work: blocks * iters * 4 * 16 * 32768 flops; time it with events on the
+ * stream.  Errors: MOE_ERR_INVALID_ARG for blocks or iters < 1 or out NULL.
+ */
+moe_status moe_probe_mfma_rate(int32_t blocks, int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "align.hip", "ffn.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "align.hip", "ffn.hip", "combine.hip", "probe.hip", "moe_api.cpp"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

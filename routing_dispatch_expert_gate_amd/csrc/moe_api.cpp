@@ -193,6 +193,14 @@ const char* moe_last_error(void) { return g_err.c_str(); }
 const char* moe_last_dispatch(void) { return g_dispatch.c_str(); }
 const char* moe_version(void) { return "moe-gfx950 0.1.0"; }
 
+moe_status moe_probe_mfma_rate(int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1) return fail(MOE_ERR_INVALID_ARG, "blocks (%d) and iters (%d) must be >= 1", blocks, iters);
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  hipError_t e = moe::launch_mfma_rate(blocks, iters, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_probe_mfma_rate launch");
+  return ok("mfma_rate_kernel");
+}
+
 int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor) {
   if (!(factor > 0.0) || E < 1 || T < 0 || k < 1) return 0;
   const int64_t load = T * (int64_t)k;

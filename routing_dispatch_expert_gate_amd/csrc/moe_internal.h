@@ -230,6 +230,9 @@ hipError_t launch_route_grouped(const RoutePlan& p, const void* x, const void* w
                                 int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
                                 hipStream_t s);
 
+// probe.hip: a dense MFMA loop (diagnostic, outside the MoE path)
+hipError_t launch_mfma_rate(int blocks, int iters, float* out, hipStream_t s);
+
 // align.hip
 struct AlignPlan {
   int slots_per_block;

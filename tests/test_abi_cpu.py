@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_header_symbols_exported(moe):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(moe.lib, n), n
         assert n in moe.SIGNATURES, n
@@ -252,3 +252,12 @@ def test_layer_options_validation(moe):
     assert ex(shared=ctypes.c_void_p(272)) == INVALID  # overlaps out without being out
     assert ex(shared=P) == WORKSPACE                 # shared may be out itself
     assert ex(T=0, ng=4, tg=2) == OK
+
+
+def test_mfma_probe_validation(moe):
+    # argument errors return before any launch (no GPU needed)
+    L = moe.lib
+    assert L.moe_probe_mfma_rate(0, 10, ctypes.c_void_p(256), None) == INVALID
+    assert L.moe_probe_mfma_rate(4, 0, ctypes.c_void_p(256), None) == INVALID
+    assert L.moe_probe_mfma_rate(4, 10, None, None) == INVALID
+    assert "NULL" in L.moe_last_error().decode()
