@@ -335,6 +335,65 @@ def test_w8a8_close_to_dequantised_fp64_layer():
     assert 1e-4 < rel < 2e-2, rel
 
 
+def _w8a8_hand_case():
+    """One token, H = 4, I = 2, one expert, k = 1 (weight 1).
+
+    x = (127, -3, 2.5, 0.5): absmax 127, so the per-token scale is exactly 1
+    and the codes are the half-even roundings (127, -3, 2, 0).
+    W1 codes (0,0,16,0), (0,0,2,0) with scales 1, 1:        g = (32, 4)
+    W3 codes (2,-1,0,0), (0,0,-8,0) with scales 1/32, 1:    u = (257/32, -16)
+    h = silu(g) * u = (257 / (1 + e^-32), -64 / (1 + e^-4))
+      in fp32: (257, -62.849...);  in bf16: (256, -62.75)
+      (257 is the tie between 256 and 258: even mantissa 256; bf16 steps by
+      1/4 between 32 and 64, and -62.849 is nearest -62.75)
+    row scale s_h = 256 / 127 (fp32 division), codes round(h / s_h) =
+      (127, round(-31.13)) = (127, -31)
+    W2 codes (1,0), (0,1), (2,-3), (-1,1) with scales (1, 1/2, 1/4, 1):
+      acc2 = (127, -31, 347, -158), y = acc2 * s_h * s2."""
+    x = np.array([[127.0, -3.0, 2.5, 0.5]], dtype=np.float32)
+    wg = np.zeros((1, 4), dtype=np.float32)
+    w13 = np.array([[[0, 0, 16, 0], [0, 0, 2, 0], [2, -1, 0, 0], [0, 0, -8, 0]]], dtype=np.int8)
+    s13 = np.array([[1.0, 1.0, 1.0 / 32.0, 1.0]], dtype=np.float32)
+    w2 = np.array([[[1, 0], [0, 1], [2, -3], [-1, 1]]], dtype=np.int8)
+    s2 = np.array([[1.0, 0.5, 0.25, 1.0]], dtype=np.float32)
+    return x, wg, w13, s13, w2, s2
+
+
+def test_w8a8_hand_worked():
+    """The W8A8 FFN step by step ([LightOP] section 4.1: per-token int8
+    quantisation of each GEMM's input, integer accumulation, dequantisation
+    by the row scale times the channel scale; h held in bf16 between the
+    GEMMs, reading R7).  A variant that skips the re-quantisation of h,
+    quantises h per column, or leaves out its bf16 rounding lands off the
+    hand-worked output by far more than the 1e-12 used here."""
+    x, wg, w13, s13, w2, s2 = _w8a8_hand_case()
+    res = oracle.layer(x, "f32", wg, "f32", None, w13, w2, "i8", 1, 0.0, s13, s2)
+    np.testing.assert_array_equal(res["xq"], [[127, -3, 2, 0]])
+    assert res["xs"][0] == np.float32(1.0)
+    # h: the fp32 values, then the bf16 ones, by hand (see _w8a8_hand_case)
+    g = np.array([32.0, 4.0])
+    u = np.array([257.0 / 32.0, -16.0])
+    h32 = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    assert h32[0] == np.float32(257.0) and -62.86 < h32[1] < -62.84
+    hb = np.array([256.0, -62.75])
+    s_h = float(np.float32(256.0) / np.float32(127.0))
+    hq = np.array([127.0, -31.0])
+    assert abs(hb[1] / s_h - (-31.13)) < 1e-3
+    acc2 = np.array([[1, 0], [0, 1], [2, -3], [-1, 1]], dtype=np.float64) @ hq
+    np.testing.assert_array_equal(acc2, [127.0, -31.0, 347.0, -158.0])
+    want = acc2 * s_h * s2[0].astype(np.float64)
+    np.testing.assert_allclose(res["out"][0], want, rtol=1e-12, atol=0)
+
+    # the slips this pin must catch: each lands far outside 1e-12
+    w2f = np.array([[1, 0], [0, 1], [2, -3], [-1, 1]], dtype=np.float64) * s2[0].astype(np.float64)[:, None]
+    no_requant = w2f @ hb                                    # h straight into the second GEMM
+    per_column = w2f @ hb                                    # one scale per column: codes +-127 give back h
+    s_h32 = float(np.float32(257.0) / np.float32(127.0))     # h left in fp32
+    no_bf16 = w2f @ (np.rint(h32.astype(np.float64) / s_h32) * s_h32)
+    for slip in (no_requant, per_column, no_bf16):
+        assert np.max(np.abs(slip - want) / np.abs(want)) > 1e-3
+
+
 # ----------------------------------------------------------------- the pages' figures
 def test_pages_figures():
     g = json.load(open(GOLDEN))
