@@ -113,7 +113,12 @@ moe_status moe_route_grouped(const void* x, int32_t x_dtype, const void* wg, int
  * Per-expert capacity C = ceil(factor * T * k / E) ([Router] section on
  * communication/computation overlap, capacity limit, with the load counted as
  * the T*k assignments).  factor <= 0 means no limit and returns 0.
- * factor = 1.25 is evaluated exactly as ceil(5*T*k / (4*E)).  Host only.
+ * The factor is taken as the fraction p/q nearest to it with q <= 2^20 (its
+ * continued-fraction best approximation), so a decimal factor such as 1.1 or
+ * 1.25 counts as the decimal (11/10, 5/4) and not as the double just above
+ * or below it; C is then ceil(p*T*k / (q*E)) in integers.  Factors outside
+ * [2^-20, 2^30] return -1 (not a capacity: check before passing it on, since
+ * moe_align treats any capacity <= 0 as no limit).  Host only.
  */
 int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor);
 

@@ -185,6 +185,79 @@ LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
   return c;
 }
 
+// ------------------------------------------------------------- capacity --
+// A capacity factor such as 1.1 has no exact double: the stored value lies a
+// little above or below the decimal, and ceil(factor * load / E) can then
+// land one off when the decimal quotient is an integer.  The factor is
+// therefore taken as the fraction p/q nearest to it with q <= 2^20 (the
+// continued-fraction best approximation, ties to the convergent), which
+// recovers every decimal of up to six places, and the ceiling is taken in
+// integers.
+typedef unsigned __int128 u128;
+constexpr double kCapFactorMin = 0x1p-20, kCapFactorMax = 0x1p30;
+constexpr uint64_t kCapDenMax = 1u << 20;
+
+// a * b as a 192-bit value (hi, lo) for a < 2^128, b < 2^64
+struct U192 {
+  uint64_t hi;
+  u128 lo;
+};
+U192 mul_u128_u64(u128 a, uint64_t b) {
+  const u128 lo = (u128)(uint64_t)a * b;
+  const u128 mid = (u128)(uint64_t)(a >> 64) * b + (lo >> 64);
+  return U192{(uint64_t)(mid >> 64), (mid << 64) | (u128)(uint64_t)lo};
+}
+bool le192(const U192& a, const U192& b) { return a.hi != b.hi ? a.hi < b.hi : a.lo <= b.lo; }
+
+// The fraction nearest to f (in [2^-20, 2^30]) with denominator <= dmax.
+void nearest_fraction(double f, uint64_t dmax, uint64_t* p_out, uint64_t* q_out) {
+  // f = N / D exactly, in lowest terms (D a power of two)
+  int ex = 0;
+  const double mant = std::frexp(f, &ex);
+  uint64_t m = (uint64_t)std::ldexp(mant, 53);
+  int e = ex - 53;
+  while ((m & 1) == 0 && e < 0) {
+    m >>= 1;
+    ++e;
+  }
+  const u128 N = e >= 0 ? (u128)m << e : (u128)m;
+  const u128 D = e >= 0 ? (u128)1 : (u128)1 << (-e);
+  if (D <= dmax) {
+    *p_out = (uint64_t)N;
+    *q_out = (uint64_t)D;
+    return;
+  }
+  // convergents p1/q1 of N/D while their denominator stays <= dmax
+  u128 p0 = 0, q0 = 1, p1 = 1, q1 = 0, n = N, d = D;
+  for (;;) {
+    const u128 a = n / d;
+    const u128 q2 = q0 + a * q1;
+    if (q2 > dmax) break;
+    const u128 p2 = p0 + a * p1;
+    p0 = p1;
+    q0 = q1;
+    p1 = p2;
+    q1 = q2;
+    const u128 r = n - a * d;
+    n = d;
+    d = r;
+  }
+  // the best semiconvergent below the bound, against the last convergent
+  const u128 kk = (dmax - q0) / q1;
+  const u128 pb = p0 + kk * p1, qb = q0 + kk * q1;
+  // |p1/q1 - N/D| <= |pb/qb - N/D|  <=>  |p1 D - N q1| qb <= |pb D - N qb| q1
+  auto absdiff = [](u128 a, u128 b) { return a > b ? a - b : b - a; };
+  const U192 lhs = mul_u128_u64(absdiff(p1 * D, N * q1), (uint64_t)qb);
+  const U192 rhs = mul_u128_u64(absdiff(pb * D, N * qb), (uint64_t)q1);
+  if (le192(lhs, rhs)) {
+    *p_out = (uint64_t)p1;
+    *q_out = (uint64_t)q1;
+  } else {
+    *p_out = (uint64_t)pb;
+    *q_out = (uint64_t)qb;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,16 +276,12 @@ moe_status moe_probe_mfma_rate(int32_t blocks, int32_t iters, float* out, void* 
 
 int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor) {
   if (!(factor > 0.0) || E < 1 || T < 0 || k < 1) return 0;
-  const int64_t load = T * (int64_t)k;
-  const double f4 = factor * 4.0;
-  if (f4 == (double)(int64_t)f4) {   // quarter steps (1.25 included): exact integer ceil
-    const int64_t num = (int64_t)f4 * load, den = 4 * (int64_t)E;
-    return (num + den - 1) / den;
-  }
-  const long double q = (long double)factor * (long double)load / (long double)E;
-  int64_t c = (int64_t)q;
-  if ((long double)c < q) ++c;
-  return c;
+  if (!(factor >= kCapFactorMin && factor <= kCapFactorMax)) return -1;
+  uint64_t p, q;
+  nearest_fraction(factor, kCapDenMax, &p, &q);
+  // ceil(p * T * k / (q * E)) in integers: p < 2^51, T * k < 2^31
+  const u128 num = (u128)p * (u128)(T * (int64_t)k), den = (u128)q * (u128)E;
+  return (int64_t)((num + den - 1) / den);
 }
 
 size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k) {

@@ -46,6 +46,12 @@ def test_capacity_and_sizes(moe):
     assert L.moe_capacity(10, 3, 4, 1.25) == 10
     assert L.moe_capacity(64, 2, 8, 0.0) == 0
     assert L.moe_capacity(7, 1, 3, 1.1) == 3          # ceil(2.566..)
+    # 1.1 * 80 * 2 / 16 is 11 for the decimal, a little above 11 for the double
+    assert L.moe_capacity(80, 2, 16, 1.1) == 11
+    assert L.moe_capacity(100, 1, 10, 1.1) == 11
+    assert L.moe_capacity(10, 1, 1, 0.3) == 3        # 0.3 * 10: the double is just below
+    assert L.moe_capacity(64, 2, 8, 1e-7) == -1      # outside [2^-20, 2^30]
+    assert L.moe_capacity(64, 2, 8, 2.0 ** 31) == -1
     assert L.moe_align_max_tiles(4096, 2, 8, 128) == 64 + 8
     assert L.moe_align_max_tiles(16, 8, 256, 128) == 1 + 128
     assert L.moe_ffn_block_m(4096, 4096, 14336, 8, 2, BF16) in (16, 32, 64, 128, 256)
@@ -261,3 +267,24 @@ def test_mfma_probe_validation(moe):
     assert L.moe_probe_mfma_rate(4, 0, ctypes.c_void_p(256), None) == INVALID
     assert L.moe_probe_mfma_rate(4, 10, None, None) == INVALID
     assert "NULL" in L.moe_last_error().decode()
+
+
+def test_capacity_equals_oracle_over_a_grid(moe):
+    """moe_capacity takes the factor as the same bounded-denominator fraction
+    as the oracle (reading R1), over decimal and random factors and loads
+    whose quotient is or is not an integer."""
+    import numpy as np
+
+    import oracle
+    L = moe.lib
+    rng = np.random.default_rng(3)
+    factors = [0.1, 0.2, 0.3, 0.7, 0.9, 1.0, 1.05, 1.1, 1.15, 1.2, 1.25, 1.3, 1.35, 1.5, 1.7, 1.9, 2.0, 2.2,
+               2.5, 3.3, 4.4, 1 / 3, 2 / 3, 1 / 7, 0.001, 0.000123, 123.456, 1000.5, 2.0 ** -20, 2.0 ** 30]
+    factors += [round(float(f), int(d)) for f, d in zip(rng.uniform(0.01, 20, 60), rng.integers(1, 7, 60))]
+    factors += rng.uniform(0.01, 50, 40).tolist()
+    loads = [(1, 1, 1), (7, 1, 3), (10, 3, 4), (80, 2, 16), (100, 1, 10), (333, 2, 8), (4096, 8, 256),
+             (16384, 6, 64), (1000, 5, 7), (2 ** 20 + 3, 8, 256), (50, 8, 10), (12345, 4, 100)]
+    for f in factors:
+        for T, k, E in loads:
+            want = oracle.capacity(T, k, E, f)
+            assert L.moe_capacity(T, k, E, f) == want, (T, k, E, f, want)
