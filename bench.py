@@ -57,8 +57,8 @@ def parse() -> argparse.Namespace:
                          "int4 codes and per-channel scales, packed on the device; i4a8: the same weights "
                          "with per-token int8 activations, W4A8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-library-ref", action="store_true",
-                    help="skip the hipBLASLt (torch.bmm) reference on the same GEMM shapes")
+    ap.add_argument("--library-ref", action="store_true",
+                    help="also time hipBLASLt (torch.bmm) on the same GEMM shapes, for context (off by default)")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (to calibrate HBM byte counters) and exit")
@@ -224,33 +224,71 @@ def library_gemm_reference(torch, spec, d, N: int, D: int):
     return res
 
 
-def cpu_baseline(cfg: int, sample_n: int, spec=None) -> dict:
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int | None:
+    try:
+        import threadpoolctl
+        blas = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        return max(blas) if blas else None
+    except Exception:
+        return None
+
+
+def routing_vs_oracle(ids_gpu: np.ndarray, r: dict) -> dict:
+    """The near-tie accounting of the top-k contract: rows whose oracle
+    k-th/(k+1)-th probability gap is below 1e-4 (the band), GPU ids that
+    differ from the oracle's inside and outside the band, and rows outside it
+    whose ids differ only in the order of selected experts with oracle
+    probabilities within 1e-6 (the order of near-equal keys)."""
+    ids_o = r["ids"]
+    band = r["gap_p"] < 1e-4
+    diff = ~(ids_gpu == ids_o).all(axis=1)
+    swaps, other = 0, 0
+    for t in np.nonzero(diff & ~band)[0]:
+        pg = r["p"][t, ids_gpu[t]]
+        if set(ids_gpu[t].tolist()) == set(ids_o[t].tolist()) and np.all(np.diff(pg) <= 1e-6):
+            swaps += 1
+        else:
+            other += 1
+    return {"tokens": int(len(ids_o)), "band_size": int(band.sum()), "band_logit_gap": int((r["gap_logit"] < 1e-4).sum()),
+            "mismatched_in_band": int((diff & band).sum()), "order_swaps_outside_band": swaps,
+            "mismatched_outside_band": other}
+
+
+def cpu_baseline(cfg: int, sample_n: int, spec=None, ids_gpu=None) -> dict:
+    """The CPU oracle on a bounded token sample of the workload, in whole
+    passes until about 10 s have run; with the GPU's top-k ids, also the
+    near-tie accounting against the oracle's routing of every token."""
     import moe_synth
     import oracle
     inp = moe_synth.config_inputs(cfg) if spec is None else moe_synth.make_inputs(spec, 1000 * cfg)
     T = inp.spec.T
     S = min(sample_n, T)
     sample = np.sort(np.random.default_rng(7).choice(T, size=S, replace=False))
-    threads = os.cpu_count() or 1
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        blas = [i["num_threads"] for i in info if i.get("user_api") == "blas"]
-        if blas:
-            threads = max(blas)
-    except Exception:
-        pass
-    # whole passes over the sample until about 10 s of CPU time have run
+    blas = _blas_threads()
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.layer_from_inputs(inp, sample_tokens=sample)
+        res = oracle.layer_from_inputs(inp, sample_tokens=sample)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= 10.0:
             break
-    return {"value": passes * S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{passes} pass(es) over {S} of {T} tokens of {inp.spec.name} (routing and align over all "
-                      f"{T} tokens, expert FFN and combine for the sample; fp64 NumPy/OpenBLAS), {dt:.1f} s"}
+    out = {"value": passes * S / dt, "unit": "tokens/s", "cores": int(blas or os.cpu_count() or 1), "kind": "oracle",
+           "sample": f"{passes} pass(es) over {S} of {T} tokens of {inp.spec.name} (routing and align over all "
+                     f"{T} tokens, expert FFN and combine for the sample; fp64 NumPy/OpenBLAS), {dt:.1f} s",
+           "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(), "blas_threads": blas}
+    if ids_gpu is not None:
+        out["routing_vs_oracle"] = routing_vs_oracle(ids_gpu, res["route"])
+    return out
 
 
 def main() -> int:
@@ -294,7 +332,8 @@ def main() -> int:
     counts = torch.empty(E, dtype=torch.int32, device="cuda")
     offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
     out = torch.empty((T, H), dtype=d["x"].dtype, device="cuda")
-    aux = {"counts": counts, "offsets": offsets}
+    ids_buf = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    aux = {"counts": counts, "offsets": offsets, "topk_ids": ids_buf}
 
     def step(with_aux=False):
         layer(d["x"], d["wg"], d["w13"], d["w2"], C, d["bias"], d["s13"], d["s2"], out=out,
@@ -303,6 +342,7 @@ def main() -> int:
     step(True)
     torch.cuda.synchronize()
     dispatch = moe.last_dispatch()
+    ids_gpu = ids_buf.cpu().numpy()
     off = offsets.cpu().numpy()
     kept = np.diff(off)
     N, D = int(off[-1]), int((kept > 0).sum())
@@ -362,23 +402,27 @@ def main() -> int:
     copy_GBps = 5 * 2 * flush.numel() / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del flush, dst
     # measured MFMA rate: a dense loop of MFMA 32x32x16 bf16 from registers
-    # (one workgroup of 4 waves per CU), best of three launches
+    # (one workgroup of 4 waves per CU), best of three launches; the probe is
+    # a bench-only library outside the MoE ABI
+    probe_lib = ctypes.CDLL(os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "libmoe_probe.so"))
+    probe_lib.moe_probe_mfma_rate.restype = ctypes.c_int
+    probe_lib.moe_probe_mfma_rate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     probe = torch.empty(256 * 256, device="cuda")
     pst = moe.binding._stream(probe.device)
     mfma_iters, mfma_best = 20000, float("inf")
     for _ in range(4):
         m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         m0.record()
-        rc = moe.lib.moe_probe_mfma_rate(256, mfma_iters, ctypes.c_void_p(probe.data_ptr()), pst)
+        rc = probe_lib.moe_probe_mfma_rate(256, mfma_iters, ctypes.c_void_p(probe.data_ptr()), pst)
         m1.record()
         torch.cuda.synchronize()
         if rc != 0:
-            raise RuntimeError("moe_probe_mfma_rate: " + moe.lib.moe_last_error().decode())
+            raise RuntimeError(f"moe_probe_mfma_rate returned {rc}")
         mfma_best = min(mfma_best, m0.elapsed_time(m1))
     mfma_TFLOPs = 256 * mfma_iters * 4 * 16 * 32768 / (mfma_best * 1e-3) / 1e12
     del probe
     log(f"measured: copy {copy_GBps:.0f} GB/s, dense MFMA bf16 loop {mfma_TFLOPs:.0f} TFLOP/s")
-    lib_ref = library_gemm_reference(torch, spec, d, N, D) if not args.no_library_ref else None
+    lib_ref = library_gemm_reference(torch, spec, d, N, D) if args.library_ref else None
 
     # algorithmic work (bytes / flops the method must move or do)
     bx, bg, bw = BYTES[spec.x_dtype], BYTES[spec.wg_dtype], BYTES[spec.w_dtype]
@@ -438,7 +482,7 @@ def main() -> int:
     if not args.no_cpu_baseline:
         n = args.cpu_sample or CPU_SAMPLE[cfg]
         log(f"timing the CPU oracle on {n} tokens")
-        cpu = cpu_baseline(cfg, n, spec)
+        cpu = cpu_baseline(cfg, n, spec, ids_gpu)
 
     rec = {
         "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,

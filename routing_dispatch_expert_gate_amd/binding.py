@@ -67,7 +67,6 @@ SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_last_dispatch": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
-    "moe_probe_mfma_rate": (_i32, [_i32, _i32, _vp, _vp]),
 }
 
 

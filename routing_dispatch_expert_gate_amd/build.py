@@ -19,9 +19,12 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
+# bench-only diagnostics (a dense MFMA loop), outside the library's ABI
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "align.hip", "ffn.hip", "combine.hip", "probe.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "align.hip", "ffn.hip", "combine.hip", "moe_api.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -49,7 +52,8 @@ def _run(cmd: list[str]) -> None:
 
 
 def build(jobs: int | None = None) -> str:
-    """Compile every source and link ``libmoe.so``; returns its path."""
+    """Compile every source and link ``libmoe.so`` (and the bench-only
+    ``libmoe_probe.so``); returns the path of ``libmoe.so``."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -59,12 +63,14 @@ def build(jobs: int | None = None) -> str:
         _run([hipcc, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
-    n = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    srcs = SOURCES + PROBE_SOURCES
+    n = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(n) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+        objs = dict(zip(srcs, ex.map(compile_one, srcs)))
+    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *(objs[s] for s in names)])
+        os.replace(tmp, lib)
     return LIB
 
 

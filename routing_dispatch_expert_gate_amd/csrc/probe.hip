@@ -1,10 +1,12 @@
-// Diagnostic: the MFMA rate this device sustains, for stating a measured
-// peak beside the published one.  Each wave keeps a 128 x 128 block of
-// accumulators (16 fragments of MFMA 32x32x16 bf16) and runs the MFMAs from
+// Diagnostic outside the MoE path: the MFMA rate this device sustains, for
+// stating a measured peak beside the published one.  Built into its own
+// library (libmoe_probe.so), not into libmoe.so, and declared in probe.h.
+// Each wave keeps a 128 x 128 block of accumulators (16 fragments of MFMA 32x32x16 bf16) and runs the MFMAs from
 // registers only: no memory traffic, no LDS, no barriers.  The operands are
 // small integers, so every sum is exact; the result is written so the loop
 // is not removed.
 #include "moe_internal.h"
+#include "probe.h"
 
 namespace moe {
 namespace {
@@ -44,9 +46,10 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
 
 }  // namespace
 
-hipError_t launch_mfma_rate(int blocks, int iters, float* out, hipStream_t s) {
-  mfma_rate_kernel<<<blocks, 256, 0, s>>>(out, iters);
-  return hipGetLastError();
-}
-
 }  // namespace moe
+
+extern "C" int moe_probe_mfma_rate(int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out) return -1;
+  moe::mfma_rate_kernel<<<blocks, 256, 0, (hipStream_t)stream>>>(out, iters);
+  return (int)hipGetLastError();
+}
