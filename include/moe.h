@@ -342,6 +342,28 @@ moe_status moe_layer_ex(const void* x, int32_t x_dtype, const void* wg, int32_t 
                         const moe_layer_aux* aux, const moe_layer_options* options, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------ allocation-free layer --
+ * For callers that cannot allocate device memory or hand the library a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  moe_layer_noalloc is moe_layer with the workspace
+ * taken from a scratch array the library itself holds on each GPU it runs on
+ * (MOE_NOALLOC_SCRATCH_BYTES, for the life of the process); the caller still
+ * passes x, the weights, out and, if it wants them, the aux buffers.  It
+ * calls no allocating routine.  Shapes whose moe_layer_workspace_size
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES (16 MiB: decode-sized batches, e.g. up
+ * to 128 tokens at H = 4096, E = 256, k = 8, I = 1024) return
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  Arguments, outputs and
+ * the other errors are moe_layer's; every output equals moe_layer's.
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (two host threads, or two streams
+ * not ordered by the caller) race.  Calls on one stream are ordered. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+moe_status moe_layer_noalloc(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                             const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                             const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                             const moe_layer_aux* aux, void* stream);
+
 /* ------------------------------------------------------- diagnostics -----
  * moe_last_error: message of this thread's last failed call ("" if none).
  * moe_last_dispatch: kernel variants this thread's last successful call

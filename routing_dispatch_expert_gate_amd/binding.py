@@ -64,6 +64,8 @@ SIGNATURES = {
                         _i32, _i64, _vp, _i32, _vp, _vp, _sz, _vp]),
     "moe_layer_ex": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
                            _i32, _i64, _vp, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "moe_layer_noalloc": (_st, [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32,
+                                _i32, _i64, _vp, _i32, _vp, _vp]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_last_dispatch": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -594,16 +595,54 @@ size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int3
 
 }  // extern "C"
 
+// ------------------------------------------------ allocation-free layer ---
+// moe_layer_noalloc carves its workspace from this file-scope device array
+// instead of a caller buffer.  Each GPU the library runs on holds its own
+// copy (MOE_NOALLOC_SCRATCH_BYTES) until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in noalloc_ptr.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-// The fused layer behind moe_layer and moe_layer_ex (opt NULL: plain top-k,
-// no shared term, no bias).
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[kMaxDevices];
+
+// The device address of the current device's scratch array.
+moe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_layer_noalloc: device %d beyond the %d it keeps scratch for", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(noalloc_mu);
+  if (!noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_layer_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p || !al(p, 256)) return fail(MOE_ERR_HIP, "moe_layer_noalloc: scratch address not 256-byte aligned");
+    noalloc_ptr[dev] = p;
+  }
+  *out = noalloc_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// The fused layer behind moe_layer, moe_layer_ex and moe_layer_noalloc
+// (opt NULL: plain top-k, no shared term, no bias; noalloc: the workspace is
+// the current device's scratch array).
 moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
                       const float* bias, const void* w13, const void* w2, int32_t w_dtype,
                       const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
                       int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
                       const moe_layer_aux* aux, const moe_layer_options* opt, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, bool noalloc = false) {
   const moe_layer_options no_opt{0, 0, nullptr, 1.0f, nullptr};
   const moe_layer_options& o = opt ? *opt : no_opt;
   const bool grouped = o.n_group != 0;
@@ -668,6 +707,15 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
   }
   if (o.out_bias) MOE_ALIGNED(o.out_bias, 16);
   const LayerCarve c = carve_layer(T, H, I, E, k, x_dtype, wg_dtype, w_dtype);
+  if (noalloc) {
+    if (c.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "moe_layer_noalloc: this shape needs %zu bytes of scratch, above the %zu it holds "
+                  "(call moe_layer with a workspace)",
+                  c.total, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    MOE_TRY(noalloc_scratch(&workspace));
+    workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  }
   MOE_TRY(check_ws(workspace, workspace_bytes, c.total));
 
   uint8_t* base = (uint8_t*)workspace;
@@ -756,6 +804,17 @@ moe_status moe_layer_ex(const void* x, int32_t x_dtype, const void* wg, int32_t 
                         size_t workspace_bytes, void* stream) {
   return layer_impl(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, s13, s2, T, H, I, E, k, capacity, out,
                     out_dtype, aux, options, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_layer_noalloc(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
+                             const float* bias, const void* w13, const void* w2, int32_t w_dtype,
+                             const float* s13, const float* s2, int64_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k, int64_t capacity, void* out, int32_t out_dtype,
+                             const moe_layer_aux* aux, void* stream) {
+  const moe_status st = layer_impl(x, x_dtype, wg, wg_dtype, bias, w13, w2, w_dtype, s13, s2, T, H, I, E, k,
+                                   capacity, out, out_dtype, aux, nullptr, nullptr, 0, stream, true);
+  if (st == MOE_OK && T > 0) g_dispatch += " (no-alloc scratch)";
+  return st;
 }
 
 }  // extern "C"
