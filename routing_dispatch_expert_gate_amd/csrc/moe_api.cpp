@@ -82,13 +82,13 @@ moe_status check_ws(void* ws, size_t have, size_t need) {
 
 moe_status route_checks(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, int64_t T,
                         int32_t H, int32_t E, int32_t k, int32_t* ids, float* w, int8_t* xq,
-                        float* xs, moe::RoutePlan* plan) {
+                        float* xs, moe::RoutePlan* plan, bool fused_ok = true) {
   MOE_TRY(check_dims(T, H, E, k));
   if (!is_act(x_dtype)) return fail(MOE_ERR_UNSUPPORTED, "x dtype must be MOE_F32 or MOE_BF16");
   if (!is_act(wg_dtype)) return fail(MOE_ERR_UNSUPPORTED, "wg dtype must be MOE_F32 or MOE_BF16");
   if ((xq == nullptr) != (xs == nullptr))
     return fail(MOE_ERR_INVALID_ARG, "xq and xs must both be given or both be NULL");
-  *plan = moe::plan_route(T, H, E, k, x_dtype, wg_dtype);
+  *plan = moe::plan_route(T, H, E, k, x_dtype, wg_dtype, fused_ok);
   if (plan->kind < 0)
     return fail(MOE_ERR_UNSUPPORTED,
                 "route: E=%d with x/wg dtypes %d/%d and H=%d is not implemented (E<=8 with H<=8192 or "
@@ -109,6 +109,8 @@ std::string route_name(const moe::RoutePlan& p) {
   char b[160];
   if (p.kind == 0)
     snprintf(b, sizeof b, "route_fma_kernel(tokens/wg=%d,waves=%d)", p.bt, p.nw);
+  else if (p.kind == 3)
+    snprintf(b, sizeof b, "route_fused_kernel(tokens/wg=%d,parts=%d)", p.bt, p.ks);
   else
     snprintf(b, sizeof b, "route_gemm_kernel(tokens/wg=%d,experts/wg=%d,ksplit=%d)+route_topk_kernel", p.bt,
              p.be, p.ks);
@@ -151,11 +153,15 @@ struct LayerCarve {
   moe::FfnPlan fp;
 };
 
+// grouped: the group-limited router (never the fused kind).  The scratch
+// covers the two-kernel router either way, so one workspace size serves
+// moe_layer and moe_layer_ex with any options.
 LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t x_dtype,
-                       int32_t wg_dtype, int32_t w_dtype) {
+                       int32_t wg_dtype, int32_t w_dtype, bool grouped = false) {
   LayerCarve c{};
   const int64_t n = T * k;
-  c.rp = moe::plan_route(T, H, E, k, x_dtype, wg_dtype);
+  c.rp = moe::plan_route(T, H, E, k, x_dtype, wg_dtype, !grouped);
+  const moe::RoutePlan rp2 = moe::plan_route(T, H, E, k, x_dtype, wg_dtype, false);
   c.ap = moe::plan_align(T, k, E);
   c.fp = moe::plan_ffn(T, H, I, E, k, w_dtype);
   size_t off = 0;
@@ -178,7 +184,7 @@ LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
   c.xq = take(a8 ? (size_t)T * H : 0);
   c.xs = take(a8 ? (size_t)T * 4 : 0);
   c.y = take(n * (size_t)H * (w_dtype == MOE_F32 ? 4 : 2));
-  size_t scratch = c.rp.ws_bytes;
+  size_t scratch = c.rp.ws_bytes > rp2.ws_bytes ? c.rp.ws_bytes : rp2.ws_bytes;
   if (c.ap.ws_bytes > scratch) scratch = c.ap.ws_bytes;
   if (c.fp.ws_bytes > scratch) scratch = c.fp.ws_bytes;
   c.scratch = take(scratch);
@@ -278,7 +284,9 @@ int64_t moe_capacity(int64_t T, int32_t k, int32_t E, double factor) {
 }
 
 size_t moe_route_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k) {
-  return moe::plan_route(T, H, E, k, MOE_BF16, MOE_BF16).ws_bytes;
+  // the two-kernel plan's (the fused kind needs none): the same size serves
+  // moe_route_grouped
+  return moe::plan_route(T, H, E, k, MOE_BF16, MOE_BF16, false).ws_bytes;
 }
 
 moe_status moe_route(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype,
@@ -309,7 +317,7 @@ moe_status moe_route_grouped(const void* x, int32_t x_dtype, const void* wg, int
     return fail(MOE_ERR_INVALID_ARG, "k (%d) exceeds the %d experts of the kept groups", k,
                 topk_group * (E / n_group));
   moe::RoutePlan plan;
-  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, topk_ids, topk_w, xq, xs, &plan));
+  MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, topk_ids, topk_w, xq, xs, &plan, false));
   if (plan.kind != 2)
     return fail(MOE_ERR_UNSUPPORTED,
                 "group-limited routing needs 16 < E <= 256, E %% 16 == 0, bf16 x and bf16 wg (got E=%d)", E);
@@ -671,7 +679,7 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
   int32_t* const si = stand_in;
   moe::RoutePlan rp;
   MOE_TRY(route_checks(x, x_dtype, wg, wg_dtype, T, H, E, k, si, (float*)si,
-                       act == MOE_I8 ? (int8_t*)si : nullptr, act == MOE_I8 ? (float*)si : nullptr, &rp));
+                       act == MOE_I8 ? (int8_t*)si : nullptr, act == MOE_I8 ? (float*)si : nullptr, &rp, !grouped));
   if (grouped) {
     const int32_t ng = o.n_group, tg = o.topk_group;
     if (ng < 1 || ng > 64 || E % ng != 0)
@@ -706,7 +714,7 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
     }
   }
   if (o.out_bias) MOE_ALIGNED(o.out_bias, 16);
-  const LayerCarve c = carve_layer(T, H, I, E, k, x_dtype, wg_dtype, w_dtype);
+  const LayerCarve c = carve_layer(T, H, I, E, k, x_dtype, wg_dtype, w_dtype, grouped);
   if (noalloc) {
     if (c.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
       return fail(MOE_ERR_UNSUPPORTED,

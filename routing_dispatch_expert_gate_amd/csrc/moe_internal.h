@@ -203,14 +203,16 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // ------------------------------------------------------------- launchers
 // route.hip
 struct RoutePlan {
-  int kind;      // 0 = fused FMA (E <= 16), 2 = MFMA logits + top-k (E > 16)
+  int kind;      // 0 = fused FMA (E <= 16), 2 = MFMA logits + top-k (E > 16),
+                 // 3 = fused MFMA logits + top-k (E <= 64, large batches)
   int bt;        // tokens per workgroup
-  int ks;        // K splits (kind 2)
+  int ks;        // K splits (kind 2) or parts of H (kind 3)
   int nw;        // waves per workgroup (kind 0)
   size_t ws_bytes;
   int be;        // experts per workgroup (kind 2)
 };
-RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype);
+// fused_ok = false: never kind 3 (the group-limited router runs on kind 2)
+RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, bool fused_ok = true);
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                         const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
                         float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s);

@@ -75,6 +75,33 @@ __device__ void wave_topk_select_store(float v[4], int k, float m, float s, int6
   }
 }
 
+// The same selection for E <= 64, one logit per lane (lane = expert, -inf
+// past E): k argmax rounds, the first of which gives the token's maximum.
+__device__ void wave_topk64_store(float v, int E, int k, int64_t t, int32_t* __restrict__ ids,
+                                  float* __restrict__ w, float* __restrict__ prob) {
+  const int lane = threadIdx.x & 63;
+  const float m = wave_max(v);
+  const float s = prob ? wave_sum(lane < E ? expf(v - m) : 0.f) : 0.f;
+  int my_id = 0;
+  float my_l = -INFINITY;
+  for (int i = 0; i < k; ++i) {
+    const float bv = i == 0 ? m : wave_max(v);
+    const int bi = __ffsll((unsigned long long)__ballot(v == bv)) - 1;   // lowest expert holding it
+    if (lane == i) {
+      my_id = bi;
+      my_l = bv;
+    }
+    if (lane == bi) v = -INFINITY;
+  }
+  const float ex = lane < k ? expf(my_l - m) : 0.f;
+  const float se = wave_sum(ex);
+  if (lane < k) {
+    ids[t * k + lane] = my_id;
+    w[t * k + lane] = ex / se;
+    if (prob) prob[t * k + lane] = ex / s;
+  }
+}
+
 __device__ __forceinline__ float wave_logit_max(const float v[4]) {
   return wave_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
 }
@@ -180,13 +207,48 @@ __device__ void wave_topk_rank_store(const float* L, int E, int k, int64_t t, in
 }
 
 // ------------------------------------------------------- per-token quant --
-// codes of 8 values with scale s (rs = 1/s)
-__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float rs) {
-  uint32_t b[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) b[i >> 2] |= (uint32_t)(quant_code(v[i], s, rs) & 0xFF) << (8 * (i & 3));
-  return make_uint2(b[0], b[1]);
+// Codes of 4 or 8 values with scale s (rs = 1/s), as quant_code, for a row
+// whose reciprocal scale is finite (rok; s is the row's max |x| / 127, so
+// every |x * rs| <= 127 (1 + 2^-23) and rounds into [-127, 127]): x * rs
+// rounds to the integer of the correctly rounded quotient unless it lies
+// within 2^-14 of a half-integer; a group holding such a value (or a row
+// without rok) takes the division for the whole group, clamped as the rule
+// writes it (about one group in a thousand), so the common path has no
+// branch, clamp or division per value.
+__device__ __forceinline__ uint32_t pack_codes4(const float (&q)[4]) {
+  const int32_t a = (int32_t)q[0], b = (int32_t)q[1], c = (int32_t)q[2], d = (int32_t)q[3];
+  // v_perm_b32: selector bytes 0-3 pick the second operand's bytes, 4-7 the
+  // first's, 0x0c gives zero
+  return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
 }
+template <int N>
+__device__ __forceinline__ void quant_group(const float (&v)[N], float s, float rs, bool rok, float (&q)[N]) {
+  bool risky = !rok;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float y = v[i] * rs;
+    q[i] = rintf(y);
+    // bitwise, not short-circuit: no branch per value
+    risky = risky | !(fabsf(fabsf(y - q[i]) - 0.5f) >= 0x1p-14f);
+  }
+  if (risky) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = fminf(fmaxf(rintf(v[i] / s), -128.f), 127.f);
+  }
+}
+__device__ __forceinline__ uint32_t quant4(const float (&v)[4], float s, float rs, bool rok) {
+  float q[4];
+  quant_group<4>(v, s, rs, rok, q);
+  return pack_codes4(q);
+}
+__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float rs, bool rok) {
+  float q[8];
+  quant_group<8>(v, s, rs, rok, q);
+  const float lo[4] = {q[0], q[1], q[2], q[3]}, hi[4] = {q[4], q[5], q[6], q[7]};
+  return make_uint2(pack_codes4(lo), pack_codes4(hi));
+}
+// whether a row's reciprocal scale is finite (a denormal scale's is not)
+__device__ __forceinline__ bool rs_ok(float rs) { return rs <= 3.4028234e38f; }
 
 __device__ __forceinline__ float row_scale(float absmax) {
   return absmax == 0.f ? 1.f : absmax / 127.f;
@@ -418,7 +480,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
         if (hv) {
           float v[8];
           r[u].get(v);
-          *reinterpret_cast<uint2*>(xq + (t0 + tt) * H + h0) = quant8(v, s, 1.f / s);
+          *reinterpret_cast<uint2*>(xq + (t0 + tt) * H + h0) = quant8(v, s, 1.f / s, rs_ok(1.f / s));
         }
         if (threadIdx.x == 0) xs[t0 + tt] = s;
       }
@@ -681,6 +743,7 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
     }
     const float s = row_scale(am);
     const float rs = 1.f / s;
+    const bool rok = rs_ok(rs);
     const uint16_t* xrow = x + t * H;
     int8_t* qrow = xq + t * H;
 #pragma unroll
@@ -694,7 +757,7 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
           c[2 * i] = __uint_as_float(q4[i] << 16);
           c[2 * i + 1] = __uint_as_float(q4[i] & 0xFFFF0000u);
         }
-        *reinterpret_cast<uint2*>(qrow + h) = quant8(c, s, rs);
+        *reinterpret_cast<uint2*>(qrow + h) = quant8(c, s, rs, rok);
       }
     }
     // the rest of a longer row: 4 chunks of 8 values per lane in flight
@@ -705,7 +768,7 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
         if (h0 + u * 512 < H) load8(xrow + h0 + u * 512, c[u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (h0 + u * 512 < H) *reinterpret_cast<uint2*>(qrow + h0 + u * 512) = quant8(c[u], s, rs);
+        if (h0 + u * 512 < H) *reinterpret_cast<uint2*>(qrow + h0 + u * 512) = quant8(c[u], s, rs, rok);
     }
     if (lane == 0) xs[t] = s;
   }
@@ -729,6 +792,227 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   topk_token<QUANT, GROUPED, LAT ? 8 : 0, LAT ? 16 : 8>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob,
                                                          xq, xs, n_group, topk_group, lrow[wv],
                                                          grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+}
+
+// ------------------------------------------------------------ kind 3 -----
+// E <= 64, bf16: gate, softmax and top-k (and, with quantisation, the int8
+// codes) in one kernel, with the logits on chip and x read from memory once.
+// A workgroup of 16 waves takes BM = 256 / KQ tokens and every expert over
+// all of H.  Wave (tb, q) owns tokens [16 tb, 16 tb + 16) of the block and
+// the q-th of KQ contiguous parts of H.  It loads its whole x slice straight
+// into registers, all loads issued at once, laid out as the A operand of MFMA
+// 16x16x32 bf16 (row = lane % 16, eight K values at 8 (lane / 16) of each
+// 32-value substep); the same registers give the int8 codes, made a few
+// substeps per stage inside the K loop once the row's max |x| has been
+// exchanged through LDS at the first stage.  Wg streams through LDS: a stage
+// holds RB / 2 K values of every part for all 64 expert rows (rows past E
+// copy row 0), S stages deep, copied straight into LDS by every wave.  Each
+// wave accumulates its 16 tokens x 64 experts (four 16 x 16 fragments) over
+// its part; the KQ parts are then summed through LDS in part order, the
+// bias added, and the top-k taken by argmax rounds, one wave per token.  No
+// atomics: deterministic.
+constexpr int kFE = 64;   // experts per fused tile
+
+// f(IntC<I>) for I = B, B+1, ..., E-1: a loop whose index is a compile-time
+// constant in every iteration (register arrays indexed by it stay registers)
+template <int V>
+struct IC {
+  static constexpr int value = V;
+};
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// the part count for H (x slice of at most 512 values per wave, whole
+// 32-value substeps, whole stages), or 0 if the fused kernel does not apply
+inline int fused_parts(int H) {
+  for (int kq = 2; kq <= 8; kq *= 2) {
+    const int part = H / kq;
+    if (H % kq == 0 && (part == 64 || part == 128 || part == 256 || part == 512)) return kq;
+  }
+  return 0;
+}
+
+template <bool QUANT, int KQ, int NSUB>
+__global__ __launch_bounds__(1024) void route_fused_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T,
+    int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob,
+    int8_t* __restrict__ xq, float* __restrict__ xs) {
+  constexpr int BM = 256 / KQ;                     // tokens per workgroup
+  constexpr int RB = KQ >= 8 ? 64 : 128;           // stage row bytes
+  constexpr int SPS = RB / 64;                     // substeps per stage
+  constexpr int NST = NSUB / SPS;                  // stages per K loop
+  constexpr int BROWS = kFE * KQ;                  // stage rows: (part, expert)
+  constexpr int STAGE = BROWS * RB;
+  constexpr int SMAX = 128 * 1024 / STAGE;
+  // short loops issue every stage before the first wait
+  constexpr int S = NST + 1 < SMAX ? (NST + 1 < 2 ? 2 : NST + 1) : SMAX;
+  constexpr int L = STAGE / 1024 / 16;             // 1 KiB copies per wave per stage
+  constexpr int CPR = RB / 16, RPB = 1024 / RB;
+  static_assert(L >= 1 && L * 16 * 1024 == STAGE, "copies split evenly over the 16 waves");
+  static_assert(NST * SPS == NSUB && S >= 2, "stages");
+  // One LDS allocation (with a second LDS object the compiler can no longer
+  // tell the stage reads from the in-flight copies and drains every copy
+  // before each stage): the stages, which the partial logits [KQ][BM][64]
+  // fp32 (whose first plane becomes the logits) reuse after the K loop, then
+  // the per-part row maxima of |x| [KQ][BM].
+  constexpr int PL_BYTES = BM * kFE * 4 * KQ;
+  constexpr int AMX_OFF = S * STAGE > PL_BYTES ? S * STAGE : PL_BYTES;
+  constexpr int SMEM = AMX_OFF + (QUANT ? KQ * BM * 4 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
+  float* const amx = reinterpret_cast<float*>(smem + AMX_OFF);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = wv / KQ, q = wv - tb * KQ;
+  const int64_t t0 = (int64_t)blockIdx.x * BM;
+  const int part = H / KQ;
+  const int lr = lane & 15, lk = lane >> 4;
+
+  // x slice: token row t0 + 16 tb + lr, values [q part + 32 s + 8 lk, +8)
+  const int64_t trow = t0 + tb * 16 + lr;
+  const uint16_t* xrow = x + (trow < T ? trow : T - 1) * (int64_t)H + q * part + 8 * lk;
+  u32x4 a[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) a[s] = *reinterpret_cast<const u32x4*>(xrow + 32 * s);
+
+  // Wg copies: this wave's 1 KiB blocks wv * L + j of each stage; lane i
+  // copies stage row RPB * blk + i / CPR (row = part * 64 + expert) into LDS
+  // chunk i % CPR, which holds logical chunk (i % CPR) ^ sw(row)
+  // (byte offsets into Wg, which is at most 256 x 4096 bf16 = 2 MiB)
+  uint32_t src[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    const int row = (wv * L + j) * RPB + lane / CPR;
+    const int qq = row / kFE, e = row - qq * kFE;
+    const int c = (lane % CPR) ^ swr<RB>(row);
+    src[j] = (uint32_t)((e < E ? e : 0) * H * 2 + qq * part * 2 + c * 16);
+  }
+  const uint8_t* const wgb = reinterpret_cast<const uint8_t*>(wg);
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void*)(wgb + src[j] + kt * RB), (lds_void*)(st + (wv * L + j) * 1024),
+                                       16, 0, 0);
+  };
+  // B fragment of expert block eb at logical chunk c of this wave's part
+  int boff[4][SPS];
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int ss = 0; ss < SPS; ++ss) {
+      const int row = q * kFE + eb * 16 + lr;
+      boff[eb][ss] = row * RB + (((4 * ss + lk) ^ swr<RB>(row)) << 4);
+    }
+
+  // int8 codes (QUANT): the lane's row max |x| over this wave's part is
+  // published at the first stage (the x loads are done by then) and read at
+  // the second; the codes of the row's values in the lane's registers are
+  // then made and stored a few substeps per stage, overlapping the K loop
+  // (after it when the loop has one stage)
+  const bool row_ok = trow < T;
+  float qs = 1.f, qrs = 1.f;
+  bool qrok = true;
+  constexpr int QPS = NST > 1 ? (NSUB + NST - 2) / (NST - 1) : NSUB;   // substeps coded per stage
+  auto publish_absmax = [&]() {
+    uint32_t m = 0;
+#pragma unroll
+    for (int ss = 0; ss < NSUB; ++ss)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(a[ss][j] & 0x7FFFu, (a[ss][j] >> 16) & 0x7FFFu));
+    float mf = __uint_as_float(m << 16);
+    mf = fmaxf(mf, lane_xor16(mf));
+    mf = fmaxf(mf, lane_xor32(mf));
+    if (lk == 0) amx[q * BM + tb * 16 + lr] = mf;
+  };
+  auto take_scale = [&]() {
+    float am = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq) am = fmaxf(am, amx[qq * BM + tb * 16 + lr]);
+    qs = row_scale(am);
+    qrs = 1.f / qs;
+    qrok = rs_ok(qrs);
+    if (row_ok && q == 0 && lk == 0) xs[trow] = qs;
+  };
+  int8_t* const qrow = QUANT ? xq + trow * (int64_t)H + q * part + 8 * lk : nullptr;
+  auto store_codes = [&](auto s0c, auto s1c) {
+    constexpr int S0 = decltype(s0c)::value;
+    constexpr int S1 = decltype(s1c)::value < NSUB ? decltype(s1c)::value : NSUB;
+    if (!row_ok) return;
+    static_for<S0, S1>([&](auto ssc) {
+      constexpr int ss = decltype(ssc)::value;
+      uint32_t wd[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float c[4] = {__uint_as_float(a[ss][2 * h] << 16), __uint_as_float(a[ss][2 * h] & 0xFFFF0000u),
+                            __uint_as_float(a[ss][2 * h + 1] << 16),
+                            __uint_as_float(a[ss][2 * h + 1] & 0xFFFF0000u)};
+        wd[h] = quant4(c, qs, qrs, qrok);
+      }
+      *reinterpret_cast<uint2*>(qrow + 32 * ss) = make_uint2(wd[0], wd[1]);
+    });
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < NST) issue(p);
+  static_for<0, NST>([&](auto ktc) {
+    constexpr int kt = decltype(ktc)::value;
+    constexpr int after = NST - 1 - kt < S - 2 ? NST - 1 - kt : S - 2;
+    wait_vmcnt<L * after>();   // the x loads, issued first, are done too
+    if constexpr (QUANT && kt == 0) publish_absmax();
+    lds_barrier();
+    if constexpr (kt + S - 1 < NST) issue(kt + S - 1);
+    if constexpr (QUANT && kt == 1) take_scale();
+    if constexpr (QUANT && kt >= 1) store_codes(IC<(kt - 1) * QPS>{}, IC<kt * QPS>{});
+    const uint8_t* st = smem + (kt % S) * STAGE;
+#pragma unroll
+    for (int ss = 0; ss < SPS; ++ss) {
+      u32x4 b[4];
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) b[eb] = *reinterpret_cast<const u32x4*>(st + boff[eb][ss]);
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb)
+        acc[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[kt * SPS + ss]),
+                                                          __builtin_bit_cast(bf16x8, b[eb]), acc[eb], 0, 0, 0);
+    }
+  });
+  lds_barrier();   // every wave is done with the stages
+  if constexpr (QUANT) {
+    if constexpr (NST == 1) {
+      take_scale();
+      store_codes(IC<0>{}, IC<NSUB>{});
+    }
+  }
+
+  // partial logits [part][token][expert] in the freed stage memory: lane
+  // holds expert 16 eb + lr, tokens 16 tb + 4 lk + i
+  float* pl = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pl[(q * BM + tb * 16 + 4 * lk + i) * kFE + eb * 16 + lr] = acc[eb][i];
+  __syncthreads();
+  // logits = the parts summed in order, plus the bias, in place over the
+  // first part's plane (each thread reads and writes its own entries)
+  for (int i = tid; i < BM * kFE; i += 1024) {
+    const int e = i % kFE;
+    float v = 0.f;
+#pragma unroll
+    for (int qq = 0; qq < KQ; ++qq) v += pl[qq * BM * kFE + i];
+    pl[i] = e < E ? v + (bias ? bias[e] : 0.f) : -INFINITY;
+  }
+  __syncthreads();
+  const int ntok = (int)(T - t0 < BM ? T - t0 : BM);
+  for (int t = wv; t < ntok; t += 16) wave_topk64_store(pl[t * kFE + lane], E, k, t0 + t, ids, w, prob);
 }
 
 // Route and align fused for small batches (T <= kFusedTopkT): one workgroup
@@ -862,7 +1146,7 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
 
 }  // namespace
 
-RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) {
+RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, bool fused_ok) {
   (void)k;
   RoutePlan p{-1, 0, 1, 0, 0};
   if (E <= 16) {
@@ -875,6 +1159,16 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
     return p;
   }
   if (x_dtype != kBF16 || wg_dtype != kBF16 || E % 16 != 0 || E > kMaxE) return p;
+  // E <= 64: the fused kernel (logits on chip, x read once) when its grid
+  // has at least 64 workgroups; smaller batches split K over more of them
+  const int kq = E <= kFE ? fused_parts(H) : 0;
+  if (fused_ok && kq > 0 && (T + 256 / kq - 1) / (256 / kq) >= 64) {
+    p.kind = 3;
+    p.bt = 256 / kq;
+    p.be = kFE;
+    p.ks = kq;
+    return p;
+  }
   p.bt = kRT;
   p.be = kRE;
   p.kind = 2;
@@ -897,9 +1191,37 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype) 
 }
 
 namespace {
+template <int KQ, int NSUB>
+hipError_t launch_fused_n(const RoutePlan& p, const void* x, const void* wg, const float* bias, int64_t T, int H,
+                          int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, hipStream_t s) {
+  const dim3 grid((unsigned)((T + p.bt - 1) / p.bt));
+  if (xq)
+    route_fused_kernel<true, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H, E,
+                                                             k, ids, w, prob, xq, xs);
+  else
+    route_fused_kernel<false, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H,
+                                                              E, k, ids, w, prob, xq, xs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const RoutePlan& p, const void* x, const void* wg, const float* bias, int64_t T, int H,
+                        int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, hipStream_t s) {
+  const int nsub = H / p.ks / 32;
+  if (p.ks == 2) {
+    if (nsub == 2) return launch_fused_n<2, 2>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    if (nsub == 4) return launch_fused_n<2, 4>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    if (nsub == 8) return launch_fused_n<2, 8>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    if (nsub == 16) return launch_fused_n<2, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+  }
+  if (p.ks == 4 && nsub == 16) return launch_fused_n<4, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+  if (p.ks == 8 && nsub == 16) return launch_fused_n<8, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t route_any(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                      const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                      int8_t* xq, float* xs, void* ws, const AlignArgs* al, hipStream_t s) {
+  if (p.kind == 3) return launch_fused(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
   if (p.kind == 0) {
     if (E <= 8 && p.nw > 8)
       return launch_fma_dt<8, true>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
@@ -922,7 +1244,7 @@ bool route_align_fusable(const RoutePlan& p, int64_t T, int k) {
   // kind 0: one workgroup routes every token; kind 2: one workgroup takes
   // every token's top-k.  Either then aligns the T*k slots itself.
   if (p.kind == 0) return T <= kFmaTB && T * k <= (int64_t)p.nw * 64 * kBlockIds;
-  return T <= kFusedTopkT;
+  return p.kind == 2 && T <= kFusedTopkT;
 }
 
 hipError_t launch_route_align_fused(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,

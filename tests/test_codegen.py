@@ -91,3 +91,31 @@ def test_small_kernels_use_no_scratch(src, tmp_path):
         if m:
             assert int(m.group(1)) == 0, f"{cur} uses scratch"
     assert seen > 0
+
+
+def test_fused_router_loop_never_drains_all_copies(tmp_path):
+    """The fused E <= 64 router streams Wg through LDS stages behind its x
+    loads: inside the K loop each stage waits for its own copies only (the
+    single LDS allocation keeps the compiler from draining them)."""
+    out = tmp_path / "route.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-fhip-fp32-correctly-rounded-divide-sqrt", "-x", "hip",
+           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}", "-S", os.path.join(CSRC, "route.hip"),
+           "--cuda-device-only", "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    text = out.read_text()
+    names = re.findall(r"^(_ZN3moe12_GLOBAL__N_118route_fused_kernel\w+):", text, re.M)
+    assert len(names) == 12, names
+    for name in names:
+        a = text.index(name + ":")
+        b = text.index(".Lfunc_end", a)
+        body = text[a:b]
+        # the loop is unrolled: every wait from the first barrier to the last
+        # MFMA, except the final stage's, leaves later copies in flight (before
+        # the first barrier the codes variants publish the row maxima to LDS,
+        # and the compiler drains the prefetched stages once for that write)
+        first = body.index("s_barrier")
+        last = body.rindex("v_mfma")
+        waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", body[first:last])
+        assert all(int(w) > 0 for w in waits[:-1]), (name, waits)

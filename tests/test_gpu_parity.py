@@ -111,22 +111,29 @@ def test_route_matches_oracle(cfg):
         np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
 
 
-def test_route_zero_rows_and_quant_edge_values():
+@pytest.mark.parametrize("T,E,k,H", [(40, 8, 2, 256), (40, 16, 4, 128), (40, 64, 6, 2048), (40, 256, 8, 512),
+                                     (8300, 64, 6, 512), (16400, 64, 6, 2048)])
+def test_route_zero_rows_and_quant_edge_values(T, E, k, H):
+    """A zero row routes to experts 0..k-1 with weight 1/k and gets scale 1;
+    exact half quotients round half-even; the last two shapes take the
+    fused E <= 64 kernel, with the edge rows in the first and last blocks."""
     moe = _moe()
-    for E, k, H in ((8, 2, 256), (16, 4, 128), (64, 6, 2048), (256, 8, 512)):
-        spec = moe_synth.Spec("z", 40, H, E, k, 64)
+    for base in ((0,) if T < 1000 else (0, T - 40)):
+        spec = moe_synth.Spec("z", T, H, E, k, 64)
         i = moe_synth.make_inputs(spec, 7, with_experts=False)
         x = moe_synth.bf16_bits_as_f32(i.x)
-        x[3] = 0.0
-        x[5, :] = 0.0
-        x[5, 7] = -2.5                         # scale 2.5/127, code -127
-        x[6, :4] = [127.0, -63.5, 0.5, 1.5]    # exact .5 quotients round half-even
+        x[base + 3] = 0.0
+        x[base + 5, :] = 0.0
+        x[base + 5, 7] = -2.5                         # scale 2.5/127, code -127
+        x[base + 6, :4] = [127.0, -63.5, 0.5, 1.5]    # exact .5 quotients round half-even
         xb = moe_synth.f32_to_bf16_bits(x)
         r = moe.route(to_dev(xb), to_dev(i.wg), k, want_p=True, quant=True)
         torch.cuda.synchronize()
+        print(moe.last_dispatch())
+        assert ("route_fused_kernel" in moe.last_dispatch()) == (T > 1000)
         ids = r["ids"].cpu().numpy()
-        np.testing.assert_array_equal(ids[3], np.arange(k))
-        np.testing.assert_allclose(r["w"].cpu().numpy()[3], 1.0 / k, atol=1e-7)
+        np.testing.assert_array_equal(ids[base + 3], np.arange(k))
+        np.testing.assert_allclose(r["w"].cpu().numpy()[base + 3], 1.0 / k, atol=1e-7)
         xq_o, xs_o = oracle.quant_per_token_int8(moe_synth.bf16_bits_as_f32(xb))
         np.testing.assert_array_equal(r["xq"].cpu().numpy(), xq_o)
         np.testing.assert_array_equal(r["xs"].cpu().numpy(), xs_o)
@@ -146,9 +153,21 @@ ROUTE_PATHS = [
     (moe_synth.Spec("fma_tb4_e16", 2049, 1024, 12, 3, 64), True, "tokens/wg=4,"),
     (moe_synth.Spec("fma_tb16_e8", 4099, 512, 8, 2, 64, wg_dtype="f32"), False, "tokens/wg=16,"),
     (moe_synth.Spec("fma_tb16_many", 16411, 256, 8, 2, 64), True, "tokens/wg=16,"),
+    # E <= 64, large batches: the fused kernel (logits on chip, x read once),
+    # two parts of H (H <= 1024: 2, 4, 8 or 16 substeps per wave), four
+    # (H = 2048) and eight (H = 4096), ragged last token block, bias, codes
     (moe_synth.Spec("e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
-     "route_gemm_kernel("),
-    (moe_synth.Spec("e32_many_tokens", 128 * 64 + 1, 128, 32, 3, 64), False, "ksplit=1)"),
+     "route_fused_kernel(tokens/wg=128,parts=2)"),
+    (moe_synth.Spec("e32_many_tokens", 128 * 64 + 1, 128, 32, 3, 64), False,
+     "route_fused_kernel(tokens/wg=128,parts=2)"),
+    (moe_synth.Spec("fused_e32_h512", 8200, 512, 32, 3, 64), False, "route_fused_kernel(tokens/wg=128,parts=2)"),
+    (moe_synth.Spec("fused_e64_h2048_codes", 16384 + 77, 2048, 64, 6, 64, zipf_s=1.1), True,
+     "route_fused_kernel(tokens/wg=64,parts=4)"),
+    (moe_synth.Spec("fused_e48_h4096_codes", 2085, 4096, 48, 4, 64), True,
+     "route_fused_kernel(tokens/wg=32,parts=8)"),
+    (moe_synth.Spec("fused_e64_h4096", 2048, 4096, 64, 8, 64), False, "route_fused_kernel(tokens/wg=32,parts=8)"),
+    # below 64 workgroups the batch keeps the K split
+    (moe_synth.Spec("e64_h2048_splitk", 4000, 2048, 64, 6, 64), True, "route_gemm_kernel("),
     (moe_synth.Spec("logits_e64_splitk", 16, 4096, 64, 6, 64), True, "route_gemm_kernel("),
     (moe_synth.Spec("logits_e128", 300, 1024, 128, 4, 64), False, "route_gemm_kernel("),
     (moe_synth.Spec("logits_e256_T1", 1, 4096, 256, 8, 64), True, "route_gemm_kernel("),
@@ -161,7 +180,7 @@ ROUTE_PATHS = [
     (moe_synth.Spec("big_e256_codes", 4096 + 37, 512, 256, 8, 64), True,
      "tokens/wg=128,experts/wg=128,ksplit=4)"),
     (moe_synth.Spec("big_e64_codes", 16384 + 5, 1024, 64, 6, 64, zipf_s=1.1), True,
-     "tokens/wg=64,experts/wg=64,ksplit=1)"),
+     "route_fused_kernel(tokens/wg=128,parts=2)"),
     (moe_synth.Spec("big_e80", 8300, 256, 80, 4, 64), False, "tokens/wg=64,experts/wg=64,ksplit=1)"),
 ]
 
@@ -175,7 +194,7 @@ def test_route_paths(spec, quant, path):
     print(moe.last_dispatch())
     d = moe.last_dispatch()
     assert path in d
-    if "splitk" in spec.name or spec.name == "logits_e128":
+    if spec.name in ("logits_e64_splitk", "logits_e128", "e64_h2048_splitk"):
         assert "ksplit=1)" not in d            # K really split
     ro = oracle.route(oracle.to_f64(i.x, spec.x_dtype), oracle.to_f64(i.wg, spec.wg_dtype), spec.k, i.bias)
     same = check_ids(r["ids"].cpu().numpy(), ro)
@@ -197,6 +216,8 @@ GROUPED = [
     (moe_synth.Spec("g_e64_G8_TG1", 257, 1024, 64, 6, 64), 8, 1, False),
     (moe_synth.Spec("g_e32_G32_TG5_T1", 1, 256, 32, 4, 64), 32, 5, True),
     (moe_synth.Spec("g_e256_G8_TG4_splitk", 64, 4096, 256, 8, 64), 8, 4, False),
+    # a batch the plain router takes fused: the grouped one keeps two kernels
+    (moe_synth.Spec("g_e64_G8_TG3_bigT", 8300, 256, 64, 6, 64, zipf_s=1.1), 8, 3, True),
 ]
 
 
@@ -727,6 +748,10 @@ LAYER_EX = [
     (moe_synth.Spec("lx_e64_plain_w4a8", 96, 256, 64, 4, 128, w_dtype="i4a8"), 0, 0, True, 2.0, True, False),
     (moe_synth.Spec("lx_e256_G8_TG4_T1", 1, 512, 256, 8, 128), 8, 4, False, 1.0, True, False),
     (moe_synth.Spec("lx_e256_G8_TG4_w4a16", 64, 512, 256, 8, 128, w_dtype="i4"), 8, 4, True, -1.0, True, True),
+    # large batch at E = 64: the grouped router keeps two kernels (and its
+    # workspace) where the plain one would be fused
+    (moe_synth.Spec("lx_e64_G8_TG3_bigT_i8", 8300, 256, 64, 6, 128, w_dtype="i8", capacity_factor=1.25),
+     8, 3, True, 0.5, True, False),
 ]
 
 
