@@ -78,9 +78,13 @@ class Staged:
     """The layer as its separate launches with preallocated buffers, for
     per-kernel timing with events between launches."""
 
-    def __init__(self, moe, torch, spec, d, C):
+    def __init__(self, moe, torch, spec, d, C, from_route=False):
         import ctypes
         self.moe, self.torch, self.spec, self.d, self.C = moe, torch, spec, d, C
+        # the layer's align step takes the route step's per-workgroup counts:
+        # time route + align as moe_route_align runs them (the layer's
+        # launches) and report align as that minus the route alone
+        self.from_route = from_route
         L = moe.lib
         T, H, E, k, I = spec.T, spec.H, spec.E, spec.k, spec.I
         n = T * k
@@ -108,7 +112,8 @@ class Staged:
         self.n_route = int(L.moe_route_workspace_size(T, H, E, k))
         self.n_align = int(L.moe_align_workspace_size(T, k, E))
         self.n_ffn = int(L.moe_ffn_workspace_size(T, H, I, E, k, self.wd))
-        mx = max(self.n_route, self.n_align, self.n_ffn, 1)
+        self.n_ra = int(L.moe_route_align_workspace_size(T, H, E, k))
+        mx = max(self.n_route, self.n_align, self.n_ffn, self.n_ra, 1)
         self.ws = torch.empty(mx, dtype=torch.uint8, device=dev)
         self.P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
         self.DT = moe.binding._DT
@@ -132,6 +137,12 @@ class Staged:
                             P(self.sorted_slot), P(self.pos), P(self.tiles), P(self.num_tiles),
                             P(self.num_dropped), ws, self.n_align, st))
 
+        def route_align():
+            chk(L.moe_route_align(P(d["x"]), DT[d["x"].dtype], P(d["wg"]), DT[d["wg"].dtype], P(d["bias"]), T, H, E,
+                                  k, self.C, self.bm, P(self.ids), P(self.w), None, P(self.xq), P(self.xs),
+                                  P(self.counts), P(self.offsets), P(self.sorted_slot), P(self.pos), P(self.tiles),
+                                  P(self.num_tiles), P(self.num_dropped), ws, self.n_ra, st))
+
         def up():
             chk(L.moe_ffn_up(P(act), DT[act.dtype], P(self.xs), P(d["w13"]), self.wd, P(d["s13"]),
                              P(self.sorted_slot), P(self.tiles), P(self.num_tiles), self.bm, T, H, I, E, k, ws,
@@ -146,16 +157,14 @@ class Staged:
             chk(L.moe_combine(P(self.y), DT[self.y.dtype], P(self.pos), None, T, k, H, P(self.out),
                               DT[self.out.dtype], st))
 
+        if self.from_route:
+            return [("route", route), ("route_align", route_align), ("ffn_up", up), ("ffn_down", down),
+                    ("combine", combine)]
         return [("route", route), ("align", align), ("ffn_up", up), ("ffn_down", down), ("combine", combine)]
 
-    def run(self, events=None):
-        ev = events or [None] * 6
-        if ev[0] is not None:
-            ev[0].record()
-        for i, (_, fn) in enumerate(self.stages()):
+    def run(self):
+        for _, fn in self.stages():
             fn()
-            if ev[i + 1] is not None:
-                ev[i + 1].record()
 
     def time_each(self, reps: int) -> dict:
         """Average GPU time of each step: `reps` launches of it captured in one
@@ -368,12 +377,14 @@ def main() -> int:
 
     # per-kernel durations: each step (entry point) launched back to back
     # `steps` times between two events on the library's stream
-    st = Staged(moe, torch, spec, d, C)
-    names = ["route", "align", "ffn_up", "ffn_down", "combine"]
+    st = Staged(moe, torch, spec, d, C, from_route="align(from route counts" in dispatch)
+    names = [n for n, _ in st.stages()]
     for _ in range(max(2, args.warmup)):
         st.run()
     torch.cuda.synchronize()
     stage_ms = st.time_each(args.steps)
+    if st.from_route:
+        stage_ms["align"] = stage_ms.pop("route_align") - stage_ms["route"]
     log("stages (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in stage_ms.items()))
 
     # isolated cold: a 1 GiB write before each staged pass evicts L2 and the
@@ -381,14 +392,30 @@ def main() -> int:
     # queues the pass's launches while the write runs, so events between them
     # time the GPU)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    acc = np.zeros(5)
-    for i in range(args.steps):
-        flush.fill_(i & 0xFF)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        st.run(evs)
-        torch.cuda.synchronize()
-        acc += [evs[i].elapsed_time(evs[i + 1]) for i in range(5)]
-    cold_ms = dict(zip(names, (acc / args.steps).tolist()))
+
+    def cold_pass(fns):
+        acc = np.zeros(len(fns))
+        for i in range(args.steps):
+            flush.fill_(i & 0xFF)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            evs[0].record()
+            for j, fn in enumerate(fns):
+                fn()
+                evs[j + 1].record()
+            torch.cuda.synchronize()
+            acc += [evs[j].elapsed_time(evs[j + 1]) for j in range(len(fns))]
+        return (acc / args.steps).tolist()
+
+    stage_fns = dict(st.stages())
+    if st.from_route:
+        # route alone, then (after another write) route + align as the layer
+        # runs them and the rest: the align share is the difference
+        route_cold = cold_pass([stage_fns["route"]])[0]
+        rest = cold_pass([stage_fns[n] for n in ("route_align", "ffn_up", "ffn_down", "combine")])
+        cold_ms = {"route": route_cold, "align": rest[0] - route_cold, "ffn_up": rest[1], "ffn_down": rest[2],
+                   "combine": rest[3]}
+    else:
+        cold_ms = dict(zip(names, cold_pass([stage_fns[n] for n in names])))
     log("stages cold (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in cold_ms.items()))
     # measured streaming rate: a 1 GiB device copy (read + write)
     dst = torch.empty_like(flush)

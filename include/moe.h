@@ -161,13 +161,18 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E,
  * the top-k workgroup for E > 16 and T <= 64: decode-sized batches), which
  * then aligns the T*k slots it has just routed (the MoE FlashAttention page's
  * first fusion, routing fused with grouping by expert, [FA-MoE] "融合一").
- * Larger batches run the two steps back to back.  Arguments, outputs and
- * errors are those of moe_route and moe_align (capacity, block_m and the
- * align outputs as in moe_align); every output equals what the two calls
- * give.  moe_last_dispatch() says whether the launch was fused.  The
- * workspace (moe_route_align_workspace_size bytes) serves both steps.
- * The fused launch saves the host one launch; on the GPU it is no faster
- * (one workgroup takes every token's top-k), so moe_layer does not use it. */
+ * Larger batches run two launches: where the route kernel takes every
+ * expert of its tokens (E <= 64), each of its workgroups also publishes its
+ * per-expert selection counts and a single align launch takes them
+ * (per-expert bases and offsets from integer sums of the counts, then the
+ * stable ranking), instead of histogramming the ids again; otherwise the
+ * route step is followed by moe_align.  Arguments, outputs and errors are
+ * those of moe_route and moe_align (capacity, block_m and the align outputs
+ * as in moe_align); every output equals what the two calls give.
+ * moe_last_dispatch() names the path taken.  The workspace
+ * (moe_route_align_workspace_size bytes) serves both steps.  The one-launch
+ * form saves the host one launch; on the GPU it is no faster (one workgroup
+ * takes every token's top-k), so moe_layer uses the two-launch forms. */
 size_t moe_route_align_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k);
 moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, const float* bias,
                            int64_t T, int32_t H, int32_t E, int32_t k, int64_t capacity, int32_t block_m,

@@ -114,34 +114,58 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
     *reinterpret_cast<int4*>(tiles + 4 * q) = make_int4(-1, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int spb, const int32_t* __restrict__ bhist,
-    const int32_t* __restrict__ offsets, int64_t cap, int32_t* __restrict__ sorted_slot,
-    int32_t* __restrict__ pos) {
-  __shared__ int32_t wh[4 * kMaxE];
+// The ranking pass of one block over slots [s0, s1) (256 threads): four
+// waves take contiguous quarters, count them per wave (LDS atomics), turn
+// the counts into per-wave bases after the block's own base(e) (the slots of
+// expert e before s0), and then rank their slots 64 at a time in slot order:
+// the lanes holding the same expert are found with one ballot per bit of the
+// expert id and ranked by popcount of the lower lanes.  off(e) is expert e's
+// first sorted row, N the kept total; the block also fills its share of the
+// unused tail [N, n) of sorted_slot.  wh: 4 * kMaxE ints of LDS, zeroed.
+// This wave's quarter of a block's slots [s0, s1), and its ids: eight loads
+// in flight per lane, kept for the ranking pass when the quarter fits (the
+// usual 1024-slot blocks: four per lane).  Issued before a block's other
+// loads, so their latencies overlap.
+constexpr int kKeepIds = 8;
+struct WaveIds {
+  int64_t w0, w1;
+  bool kept_regs;
+  int idv[kKeepIds];
+};
+__device__ __forceinline__ WaveIds load_wave_ids(const int32_t* __restrict__ ids, int64_t s0, int64_t s1) {
+  WaveIds q;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t sub = (((s1 - s0) + 3) / 4 + 63) / 64 * 64;
+  q.w0 = s0 + wv * sub < s1 ? s0 + wv * sub : s1;
+  q.w1 = q.w0 + sub < s1 ? q.w0 + sub : s1;
+  q.kept_regs = q.w1 - q.w0 <= 64 * kKeepIds;
+#pragma unroll
+  for (int u = 0; u < kKeepIds; ++u) {
+    const int64_t s = q.w0 + 64 * u + lane;
+    q.idv[u] = s < q.w1 ? ids[s] : -1;
+  }
+  return q;
+}
+
+template <typename Base, typename Off>
+__device__ void scatter_block(const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int64_t s0, int64_t s1,
+                              WaveIds& q, Base base, Off off, int64_t N, int64_t cap,
+                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ pos, int32_t* wh) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  for (int i = tid; i < 4 * kMaxE; i += kAlignThreads) wh[i] = 0;
-  __syncthreads();
-
-  const int64_t s0 = (int64_t)blockIdx.x * spb;
-  const int64_t s1 = s0 + spb < n ? s0 + spb : n;
-  const int64_t sub = (((s1 - s0) + 3) / 4 + 63) / 64 * 64;
-  const int64_t w0 = s0 + wv * sub < s1 ? s0 + wv * sub : s1;
-  const int64_t w1 = w0 + sub < s1 ? w0 + sub : s1;
+  const int64_t w0 = q.w0, w1 = q.w1;
   int32_t* my = wh + wv * kMaxE;
-
-  // this wave's ids, eight loads in flight per lane; kept for the ranking
-  // pass when the quarter fits (the usual 1024-slot blocks: four per lane)
-  constexpr int KEEP = 8;
-  int idv[KEEP];
-  const bool kept_regs = w1 - w0 <= 64 * KEEP;
+  constexpr int KEEP = kKeepIds;
+  int* const idv = q.idv;
+  const bool kept_regs = q.kept_regs;
   for (int64_t c = w0; c < w1; c += 64 * KEEP) {
+    if (c != w0) {   // a quarter longer than the registers hold: later chunks
 #pragma unroll
-    for (int u = 0; u < KEEP; ++u) {
-      const int64_t s = c + 64 * u + lane;
-      idv[u] = s < w1 ? ids[s] : -1;
+      for (int u = 0; u < KEEP; ++u) {
+        const int64_t s = c + 64 * u + lane;
+        idv[u] = s < w1 ? ids[s] : -1;
+      }
     }
 #pragma unroll
     for (int u = 0; u < KEEP; ++u)
@@ -149,17 +173,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   }
   __syncthreads();
   for (int e = tid; e < E; e += kAlignThreads) {
-    // this block's base for expert e: slots of e in all earlier blocks
-    int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int nbefore = blockIdx.x;
-    int b = 0;
-    for (; b + 8 <= nbefore; b += 8)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) part[u] += bhist[(size_t)(b + u) * E + e];
-    for (; b < nbefore; ++b) part[0] += bhist[(size_t)b * E + e];
-    int run = 0;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) run += part[u];
+    int run = base(e);
     for (int q = 0; q < 4; ++q) {
       const int v = wh[q * kMaxE + e];
       wh[q * kMaxE + e] = run;
@@ -169,12 +183,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
   __syncthreads();
 
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = w0; base < w1; base += 64) {
-    const int64_t s = base + lane;
+  for (int64_t b0 = w0; b0 < w1; b0 += 64) {
+    const int64_t s = b0 + lane;
     const bool in_range = s < w1;
     int e = -1;
     if (kept_regs) {
-      const int u = (int)((base - w0) >> 6);   // uniform, < KEEP
+      const int u = (int)((b0 - w0) >> 6);   // uniform, < KEEP
 #pragma unroll
       for (int v = 0; v < KEEP; ++v)
         if (v == u) e = idv[v];
@@ -194,16 +208,140 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     if (valid && (same & lt) == 0) my[e] += __popcll(same);
     if (in_range) {
       const bool kept = valid && (cap <= 0 || rank < cap);
-      const int p = kept ? offsets[e] + rank : -1;
+      const int p = kept ? off(e) + rank : -1;
       pos[s] = p;
       if (kept) sorted_slot[p] = (int32_t)s;
     }
   }
 
   // sentinel fill of the unused tail [N, n) of sorted_slot, split over blocks
-  const int64_t N = offsets[E];
   const int64_t f1 = N + s1 < n ? N + s1 : n;
   for (int64_t i = N + s0 + tid; i < f1; i += kAlignThreads) sorted_slot[i] = -1;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int ebits, int spb, const int32_t* __restrict__ bhist,
+    const int32_t* __restrict__ offsets, int64_t cap, int32_t* __restrict__ sorted_slot,
+    int32_t* __restrict__ pos) {
+  __shared__ int32_t wh[4 * kMaxE];
+  for (int i = threadIdx.x; i < 4 * kMaxE; i += kAlignThreads) wh[i] = 0;
+  __syncthreads();
+  const int64_t s0 = (int64_t)blockIdx.x * spb;
+  const int64_t s1 = s0 + spb < n ? s0 + spb : n;
+  WaveIds q = load_wave_ids(ids, s0, s1);
+  // this block's base for expert e: slots of e in all earlier blocks
+  // (independent loads: the sum is exact in any order)
+  auto base = [&](int e) {
+    int part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int nbefore = blockIdx.x;
+    int b = 0;
+    for (; b + 8 <= nbefore; b += 8)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part[u] += bhist[(size_t)(b + u) * E + e];
+    for (; b < nbefore; ++b) part[0] += bhist[(size_t)b * E + e];
+    int run = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) run += part[u];
+    return run;
+  };
+  scatter_block(ids, n, E, ebits, s0, s1, q, base, [&](int e) { return offsets[e]; }, (int64_t)offsets[E], cap,
+                sorted_slot, pos, wh);
+}
+
+// The whole align step in one launch from the route step's published counts
+// (whist[g][E]: the selections of route workgroup g, which covers tokens
+// [g tg, (g + 1) tg), slots [g spg, (g + 1) spg) with spg = tg k).  Block b
+// takes the slots of route workgroups [b G, (b + 1) G).  Every block sums the
+// counts of the route workgroups before its own (its per-expert base) and of
+// all of them (the per-expert totals), applies the capacity and scans the
+// kept counts into offsets; block 0 also writes counts, offsets, the tile
+// list and num_dropped.  Integer sums are exact in any order, so every
+// output is deterministic, and equal to the three-launch path's.
+// (E <= 64)
+__global__ __launch_bounds__(kAlignThreads) void align_route_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int ebits, const int32_t* __restrict__ whist, int64_t ng,
+    int G, int spg, int64_t cap, int bm, int64_t max_tiles, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ pos,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles, int32_t* __restrict__ num_dropped) {
+  __shared__ int32_t wh[4 * kMaxE];
+  __shared__ int32_t pb[kAlignThreads], pt[kAlignThreads];   // per-thread partial base / total
+  __shared__ int32_t bb[kMaxE], off_s[kMaxE + 1], tb_s[kMaxE], tot_s[2];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 4 * kMaxE; i += kAlignThreads) wh[i] = 0;
+  const int64_t g0 = (int64_t)blockIdx.x * G;
+  const int64_t s0 = g0 * spg;
+  const int64_t s1 = s0 + (int64_t)G * spg < n ? s0 + (int64_t)G * spg : n;
+  WaveIds q = load_wave_ids(ids, s0, s1);   // in flight while the counts are summed
+  // thread (r, e), r < R = 256 / E: route workgroups g = r, r + R, ...
+  const int R = kAlignThreads / E;
+  int sb = 0, st = 0;
+  if (tid < R * E) {
+    const int e = tid % E, r = tid / E;
+    int64_t g = r;
+    for (; g + 3 * R < ng; g += 4 * R) {
+      const int a0 = whist[g * E + e], a1 = whist[(g + R) * E + e], a2 = whist[(g + 2 * R) * E + e],
+                a3 = whist[(g + 3 * R) * E + e];
+      st += (a0 + a1) + (a2 + a3);
+      sb += (g < g0 ? a0 : 0) + (g + R < g0 ? a1 : 0) + (g + 2 * R < g0 ? a2 : 0) + (g + 3 * R < g0 ? a3 : 0);
+    }
+    for (; g < ng; g += R) {
+      const int a = whist[g * E + e];
+      st += a;
+      sb += g < g0 ? a : 0;
+    }
+  }
+  pb[tid] = sb;
+  pt[tid] = st;
+  __syncthreads();
+  // wave 0 (E <= 64: lane e): totals, capacity, and the scans over experts
+  // of kept rows and row tiles (DPP wave scans); block 0 writes them out
+  if (tid < 64) {
+    int total = 0, b = 0;
+    if (tid < E)
+      for (int r = 0; r < R; ++r) {
+        b += pb[r * E + tid];
+        total += pt[r * E + tid];
+      }
+    const int kept = tid < E ? (cap > 0 && total > cap ? (int)cap : total) : 0;
+    const int ntile = (kept + bm - 1) / bm;
+    const int ik = wave_incl_scan(kept), it = wave_incl_scan(ntile);
+    const int off = ik - kept;
+    if (tid < E) {
+      bb[tid] = b;
+      off_s[tid] = off;
+      tb_s[tid] = it - ntile;
+    }
+    if (tid == 63) {
+      off_s[E] = ik;
+      tot_s[0] = ik;
+      tot_s[1] = it;
+    }
+    if (blockIdx.x == 0 && tid < E) {
+      counts[tid] = total;
+      offsets[tid] = off;
+    }
+  }
+  __syncthreads();
+  const int n_kept = tot_s[0], n_tiles = tot_s[1];
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      offsets[E] = n_kept;
+      *num_dropped = (int32_t)(n - n_kept);
+      *num_tiles = n_tiles;
+    }
+    if (tid < E) {
+      const int kept = (tid + 1 < E ? off_s[tid + 1] : n_kept) - off_s[tid];
+      const int ntile = (kept + bm - 1) / bm;
+      for (int i = 0; i < ntile; ++i) {
+        const int rows = kept - i * bm < bm ? kept - i * bm : bm;
+        *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tb_s[tid] + i)) = make_int4(tid, off_s[tid] + i * bm, rows, 0);
+      }
+    }
+    for (int64_t i = n_tiles + tid; i < max_tiles; i += kAlignThreads)
+      *reinterpret_cast<int4*>(tiles + 4 * i) = make_int4(-1, 0, 0, 0);
+  }
+  scatter_block(ids, n, E, ebits, s0, s1, q, [&](int e) { return bb[e]; }, [&](int e) { return off_s[e]; },
+                (int64_t)n_kept, cap, sorted_slot, pos, wh);
 }
 
 // ------------------------------------------------- one-workgroup variant --
@@ -272,6 +410,24 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
   if (err != hipSuccess) return err;
   align_scatter_kernel<<<p.nblocks, kAlignThreads, 0, s>>>(ids, n, E, ebits, p.slots_per_block, bhist,
                                                           offsets, cap, sorted_slot, pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_from_route(const int32_t* ids, const int32_t* whist, int64_t ng, int tg, int64_t T, int k,
+                                   int E, int64_t cap, int block_m, int64_t max_tiles, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_slot, int32_t* pos, int32_t* tiles,
+                                   int32_t* num_tiles, int32_t* num_dropped, hipStream_t s) {
+  const int64_t n = T * k;
+  int ebits = 0;
+  while ((1 << ebits) < E) ++ebits;
+  // about 1024 slots per block, whole route workgroups each
+  const int spg = tg * k;
+  int G = 1024 / spg;
+  if (G < 1) G = 1;
+  const int64_t nb = (ng + G - 1) / G;
+  align_route_kernel<<<(unsigned)nb, kAlignThreads, 0, s>>>(ids, n, E, ebits, whist, ng, G, spg, cap, block_m,
+                                                            max_tiles, counts, offsets, sorted_slot, pos, tiles,
+                                                            num_tiles, num_dropped);
   return hipGetLastError();
 }
 

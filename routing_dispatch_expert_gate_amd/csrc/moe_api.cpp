@@ -186,6 +186,10 @@ LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
   c.y = take(n * (size_t)H * (w_dtype == MOE_F32 ? 4 : 2));
   size_t scratch = c.rp.ws_bytes > rp2.ws_bytes ? c.rp.ws_bytes : rp2.ws_bytes;
   if (c.ap.ws_bytes > scratch) scratch = c.ap.ws_bytes;
+  // the route step's per-workgroup counts, read by the align step (route
+  // kinds that publish them use no other route or align workspace)
+  const size_t whist = (size_t)moe::route_hist_groups(c.rp, T, k) * (size_t)E * 4;
+  if (whist > scratch) scratch = whist;
   if (c.fp.ws_bytes > scratch) scratch = c.fp.ws_bytes;
   c.scratch = take(scratch);
   c.total = off;
@@ -372,9 +376,17 @@ moe_status moe_align(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, i
 }
 
 size_t moe_route_align_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k) {
-  // the two steps run one after the other and share the workspace
+  // the two steps run one after the other and share the workspace; route
+  // kinds that publish per-workgroup counts put them there for the align
   const size_t r = moe_route_workspace_size(T, H, E, k), a = moe_align_workspace_size(T, k, E);
-  return r > a ? r : a;
+  size_t need = r > a ? r : a;
+  for (int xd = MOE_F32; xd <= MOE_BF16; ++xd)
+    for (int wd = MOE_F32; wd <= MOE_BF16; ++wd) {
+      const moe::RoutePlan p = moe::plan_route(T, H, E, k, xd, wd);
+      const size_t h = (size_t)moe::route_hist_groups(p, T, k) * (size_t)(E > 0 ? E : 0) * 4;
+      if (p.kind >= 0 && h > need) need = h;
+    }
+  return need;
 }
 
 moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32_t wg_dtype, const float* bias,
@@ -409,6 +421,18 @@ moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32
     moe::RoutePlan named = plan;
     if (named.kind == 0) named.bt = (int)T;   // one workgroup takes every token
     return ok(route_name(named) + "+align (one launch)");
+  }
+  if (moe::route_publishes_hist(plan, T, k)) {
+    // the route step publishes each workgroup's counts; one align launch
+    // takes them (the layer's path for these route kinds)
+    int32_t* whist = (int32_t*)workspace;
+    e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p, xq, xs,
+                          workspace, s, whist);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_align route launch");
+    e = moe::launch_align_from_route(topk_ids, whist, moe::route_hist_groups(plan, T, k), plan.bt, T, k, E, cap, block_m,
+                                     mt, counts, offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_route_align align launch");
+    return ok(route_name(plan) + " | align(from route counts, one launch)");
   }
   e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p, xq, xs,
                         workspace, s);
@@ -761,14 +785,23 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
                                       sorted_slot, pos, tiles, num_tiles, num_dropped, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route+align launch");
   } else {
+    // route kinds that publish per-workgroup counts (E <= 64) let one align
+    // launch take them instead of histogramming the ids again
+    const bool from_route = !grouped && moe::route_publishes_hist(c.rp, T, k);
+    int32_t* whist = from_route ? (int32_t*)scratch : nullptr;
     if (grouped)
       e = moe::launch_route_grouped(c.rp, x, wg, bias, T, H, E, k, o.n_group, o.topk_group, ids, w, p, xq, xs,
                                     scratch, s);
     else
-      e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s);
+      e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s, whist);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
-    e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts,
-                          offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, scratch, s);
+    if (from_route)
+      e = moe::launch_align_from_route(ids, whist, moe::route_hist_groups(c.rp, T, k), c.rp.bt, T, k, E,
+                                       capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts, offsets,
+                                       sorted_slot, pos, tiles, num_tiles, num_dropped, s);
+    else
+      e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts,
+                            offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, scratch, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
   }
   e = moe::launch_ffn_up(c.fp, act == MOE_I8 ? (const void*)xq : x, xs, w13, w_dtype, s13,
@@ -783,9 +816,12 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
   else
     e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
-  return ok(route_name(c.rp) + (grouped ? "<grouped>" : "") + " | " + (fused ? std::string("align(fused into route)")
-                                : c.ap.nblocks == 0 ? std::string("align(one block)")
-                                                    : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
+  const bool from_route_d = !grouped && moe::route_publishes_hist(c.rp, T, k);
+  return ok(route_name(c.rp) + (grouped ? "<grouped>" : "") + " | " +
+            (fused ? std::string("align(fused into route)")
+             : from_route_d ? std::string("align(from route counts, one launch)")
+             : c.ap.nblocks == 0 ? std::string("align(one block)")
+                                 : "align(blocks=" + std::to_string(c.ap.nblocks) + ")") + " | " +
             c.fp.up_name + "+" + c.fp.down_name + "(block_m=" + std::to_string(c.fp.block_m) +
             ") | combine_kernel<pre-weighted" + (merge ? ",shared+bias>" : ">"));
 }

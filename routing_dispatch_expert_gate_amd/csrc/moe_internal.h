@@ -213,9 +213,18 @@ struct RoutePlan {
 };
 // fused_ok = false: never kind 3 (the group-limited router runs on kind 2)
 RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, bool fused_ok = true);
+// whist (may be NULL): where route kinds 0 and 3 publish each workgroup's
+// per-expert selection counts, [route_hist_groups(p, T)][E] int32, for
+// launch_align_from_route; other kinds ignore it
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                         const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
-                        float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s);
+                        float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s, int32_t* whist = nullptr);
+// whether the route step publishes per-workgroup counts for this batch (route
+// kinds 0 and 3, at least kAlignFromRouteSlots slots)
+constexpr int64_t kAlignFromRouteSlots = 4096;
+bool route_publishes_hist(const RoutePlan& p, int64_t T, int k);
+// route workgroups (each over tokens [g bt, (g + 1) bt)) that publish counts
+int64_t route_hist_groups(const RoutePlan& p, int64_t T, int k);
 // route and align in one launch where one workgroup can take every token
 // (route_align_fusable): the align outputs as in launch_align
 bool route_align_fusable(const RoutePlan& p, int64_t T, int k);
@@ -243,6 +252,13 @@ hipError_t launch_align(const AlignPlan& p, const int32_t* ids, int64_t T, int k
                         int block_m, int64_t max_tiles, int32_t* counts, int32_t* offsets,
                         int32_t* sorted_slot, int32_t* pos, int32_t* tiles, int32_t* num_tiles,
                         int32_t* num_dropped, void* ws, hipStream_t s);
+// The same outputs from the route step's published counts: whist[g][E] for
+// the ng route workgroups of tg tokens each (g over tokens [g tg, ...)); one
+// launch, no workspace.
+hipError_t launch_align_from_route(const int32_t* ids, const int32_t* whist, int64_t ng, int tg, int64_t T, int k,
+                                   int E, int64_t cap, int block_m, int64_t max_tiles, int32_t* counts,
+                                   int32_t* offsets, int32_t* sorted_slot, int32_t* pos, int32_t* tiles,
+                                   int32_t* num_tiles, int32_t* num_dropped, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const void* y, int y_dtype, const int32_t* pos, const float* w, int64_t T,

@@ -78,7 +78,7 @@ __device__ void wave_topk_select_store(float v[4], int k, float m, float s, int6
 // The same selection for E <= 64, one logit per lane (lane = expert, -inf
 // past E): k argmax rounds, the first of which gives the token's maximum.
 __device__ void wave_topk64_store(float v, int E, int k, int64_t t, int32_t* __restrict__ ids,
-                                  float* __restrict__ w, float* __restrict__ prob) {
+                                  float* __restrict__ w, float* __restrict__ prob, int* hist = nullptr) {
   const int lane = threadIdx.x & 63;
   const float m = wave_max(v);
   const float s = prob ? wave_sum(lane < E ? expf(v - m) : 0.f) : 0.f;
@@ -99,6 +99,7 @@ __device__ void wave_topk64_store(float v, int E, int k, int64_t t, int32_t* __r
     ids[t * k + lane] = my_id;
     w[t * k + lane] = ex / se;
     if (prob) prob[t * k + lane] = ex / s;
+    if (hist) atomicAdd(&hist[my_id], 1);   // counts only: their order is irrelevant
   }
 }
 
@@ -179,7 +180,7 @@ __device__ void wave_grouped_topk_store(float v[4], float* L, float* gs, int E, 
 // order, and the k lanes of rank < k write selection rank.  The same order
 // and arithmetic as wave_topk_store, without its serial argmax rounds.
 __device__ void wave_topk_rank_store(const float* L, int E, int k, int64_t t, int32_t* __restrict__ ids,
-                                     float* __restrict__ w, float* __restrict__ prob) {
+                                     float* __restrict__ w, float* __restrict__ prob, int* hist = nullptr) {
   const int lane = threadIdx.x & 63;
   const float v = lane < E ? L[lane] : -INFINITY;
   int rank = 0;
@@ -203,6 +204,7 @@ __device__ void wave_topk_rank_store(const float* L, int E, int k, int64_t t, in
     ids[t * k + rank] = lane;
     w[t * k + rank] = ex / se;
     if (prob) prob[t * k + rank] = ex / s;
+    if (hist) atomicAdd(&hist[lane], 1);   // counts only: their order is irrelevant
   }
 }
 
@@ -369,7 +371,8 @@ template <int EP, bool WIDE, typename XT, typename WT, bool QUANT, bool ALIGN, i
 __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     const XT* __restrict__ x, const WT* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w,
-    float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs, const AlignArgs al) {
+    float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs, const AlignArgs al,
+    int32_t* __restrict__ whist) {
   // rows per load batch (all sixteen at once costs occupancy: measured
   // slower at large T)
   constexpr int PF0 = (sizeof(XT) == 4 ? 4 : 8) / (WIDE ? 2 : 1), PF = PF0 < TB ? PF0 : TB;
@@ -382,6 +385,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
   __shared__ float part[16][TB][EP];
   __shared__ float amax_s[16][TB];
   __shared__ __attribute__((aligned(16))) float lg[TB][16];
+  __shared__ int hist[16];   // this workgroup's selections per expert (whist)
   const int nw = blockDim.x >> 6;
   const int wv = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -447,6 +451,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
   __syncthreads();
 
   // logits (plus bias) of the block's tokens, rows padded with -inf
+  if (threadIdx.x < 16) hist[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < TB * 16; i += blockDim.x) {
     const int tt = i >> 4, e = i & 15;
     float s = -INFINITY;
@@ -458,7 +463,13 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
     lg[tt][e] = s;
   }
   __syncthreads();
-  for (int tt = wv; tt < ntok; tt += nw) wave_topk_rank_store(&lg[tt][0], E, k, t0 + tt, ids, w, prob);
+  for (int tt = wv; tt < ntok; tt += nw)
+    wave_topk_rank_store(&lg[tt][0], E, k, t0 + tt, ids, w, prob, whist ? hist : nullptr);
+  if (whist) {
+    // publish the workgroup's per-expert selection counts for the align step
+    __syncthreads();
+    if (threadIdx.x < E) whist[(int64_t)blockIdx.x * E + threadIdx.x] = hist[threadIdx.x];
+  }
 
   if (QUANT) {
     for (int tb = 0; tb < ntok; tb += PF) {
@@ -513,27 +524,30 @@ constexpr int kRT = 64;                        // tokens per tile (small batches
 constexpr int kRE = 64;                        // experts per tile (small batches)
 constexpr int kRRow = 128;                     // bytes of K per stage row
 constexpr int kRLds = 128 * 1024;              // bytes of stages
+constexpr int kRouteGemmWaves128 = 8;          // waves of a 128 x 128 tile (4, 8 or 16; 8 measured best)
 
 // workspace: partial logits [ks][T][E] fp32, then per-split row absmax [ks][T]
 size_t route_part_bytes(int64_t T, int E, int ks) {
   return ((size_t)ks * (size_t)T * (size_t)E * sizeof(float) + 255) & ~(size_t)255;
 }
 
-template <bool QUANT, int RT, int RE>
-__global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ wg, int64_t T,
-                                                        int H, int E, int kchunk,
-                                                        float* __restrict__ part,
-                                                        float* __restrict__ amax_part) {
+template <bool QUANT, int RT, int RE, int WM = 2, int WN = 2>
+__global__ __launch_bounds__(WM* WN * 64) void route_gemm_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ wg, int64_t T,
+                                                                int H, int E, int kchunk,
+                                                                float* __restrict__ part,
+                                                                float* __restrict__ amax_part) {
+  constexpr int NW = WM * WN, NT = NW * 64;
   constexpr int STAGE = (RT + RE) * kRRow;
   constexpr int RS = kRLds / STAGE;              // stages
-  constexpr int RL = STAGE / 1024 / 4;           // 1 KiB copies per wave per stage
-  constexpr int FR = RT / 64, FE = RE / 64;      // fragments per wave
-  static_assert(RL * 4 * 1024 == STAGE && RS >= 3, "stages");
+  constexpr int RL = STAGE / 1024 / NW;          // 1 KiB copies per wave per stage
+  constexpr int FR = RT / WM / 32, FE = RE / WN / 32;   // fragments per wave
+  static_assert(RL * NW * 1024 == STAGE && RS >= 3, "stages");
+  static_assert(FR >= 1 && FE >= 1, "wave tile");
   __shared__ __attribute__((aligned(16))) uint8_t smem[RS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv / WN, wn = wv - (wv / WN) * WN;
   const int64_t t0 = (int64_t)blockIdx.x * RT;
   const int e0 = blockIdx.y * RE;
   const int64_t rowbytes = (int64_t)H * 2;
@@ -576,7 +590,8 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
   }
   // quantisation: TPR threads fold |x| of each stage token row, CPT 16-byte
   // chunks each
-  constexpr int TPR = 256 / RT, CPT = 8 / TPR;
+  constexpr int TPR = NT / RT, CPT = 8 / TPR;
+  static_assert(TPR >= 2 && TPR <= 8 && CPT * TPR == 8, "absmax fold threads per row");
   const int qrow = tid / TPR;
   int qoff[CPT];
 #pragma unroll
@@ -603,10 +618,10 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int i = 0; i < FR; ++i)
-        af[s][i] = *reinterpret_cast<const u32x4*>(As + (wm * (RT / 2) + 32 * i) * kRRow + lo[s]);
+        af[s][i] = *reinterpret_cast<const u32x4*>(As + (wm * (RT / WM) + 32 * i) * kRRow + lo[s]);
 #pragma unroll
       for (int j = 0; j < FE; ++j)
-        bf[s][j] = *reinterpret_cast<const u32x4*>(Bs + (wn * (RE / 2) + 32 * j) * kRRow + lo[s]);
+        bf[s][j] = *reinterpret_cast<const u32x4*>(Bs + (wn * (RE / WN) + 32 * j) * kRRow + lo[s]);
     }
     if constexpr (QUANT) {
 #pragma unroll
@@ -632,20 +647,22 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const uint16_t* __restr
 
 #pragma unroll
   for (int j = 0; j < FE; ++j) {
-    const int e = e0 + wn * (RE / 2) + 32 * j + (lane & 31);
+    const int e = e0 + wn * (RE / WN) + 32 * j + (lane & 31);
 #pragma unroll
     for (int i = 0; i < FR; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t t = t0 + wm * (RT / 2) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int64_t t = t0 + wm * (RT / WM) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (t < T && e < E) part[((int64_t)blockIdx.z * T + t) * E + e] = acc[i][j][v];
       }
   }
   if constexpr (QUANT) {
     // the TPR threads of a row are adjacent lanes
     amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-    if constexpr (TPR == 4)
+    if constexpr (TPR >= 4)
       amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+    if constexpr (TPR == 8)   // quads now uniform: row_half_mirror pairs the two quads of each 8 lanes
+      amax = max(amax, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)amax, 0x141, 0xF, 0xF, false));
     if (blockIdx.y == 0 && tid % TPR == 0 && t0 + qrow < T)
       amax_part[(int64_t)blockIdx.z * T + t0 + qrow] = __uint_as_float(amax << 16);
   }
@@ -841,7 +858,7 @@ template <bool QUANT, int KQ, int NSUB>
 __global__ __launch_bounds__(1024) void route_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob,
-    int8_t* __restrict__ xq, float* __restrict__ xs) {
+    int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ whist) {
   constexpr int BM = 256 / KQ;                     // tokens per workgroup
   constexpr int RB = KQ >= 8 ? 64 : 128;           // stage row bytes
   constexpr int SPS = RB / 64;                     // substeps per stage
@@ -862,9 +879,14 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(
   // the per-part row maxima of |x| [KQ][BM].
   constexpr int PL_BYTES = BM * kFE * 4 * KQ;
   constexpr int AMX_OFF = S * STAGE > PL_BYTES ? S * STAGE : PL_BYTES;
-  constexpr int SMEM = AMX_OFF + (QUANT ? KQ * BM * 4 : 0);
+  constexpr int HIST_OFF = AMX_OFF + (QUANT ? KQ * BM * 4 : 0);
+  constexpr int SMEM = HIST_OFF + kFE * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   float* const amx = reinterpret_cast<float*>(smem + AMX_OFF);
+  // this workgroup's selections per expert (whist), zeroed before any copy
+  // into LDS is in flight
+  int* const hist = reinterpret_cast<int*>(smem + HIST_OFF);
+  if (threadIdx.x < kFE) hist[threadIdx.x] = 0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1012,7 +1034,13 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(
   }
   __syncthreads();
   const int ntok = (int)(T - t0 < BM ? T - t0 : BM);
-  for (int t = wv; t < ntok; t += 16) wave_topk64_store(pl[t * kFE + lane], E, k, t0 + t, ids, w, prob);
+  for (int t = wv; t < ntok; t += 16)
+    wave_topk64_store(pl[t * kFE + lane], E, k, t0 + t, ids, w, prob, whist ? hist : nullptr);
+  if (whist) {
+    // publish the workgroup's per-expert selection counts for the align step
+    __syncthreads();
+    if (threadIdx.x < E) whist[(int64_t)blockIdx.x * E + threadIdx.x] = hist[threadIdx.x];
+  }
 }
 
 // Route and align fused for small batches (T <= kFusedTopkT): one workgroup
@@ -1043,7 +1071,7 @@ __global__ __launch_bounds__(1024) void route_topk_align_kernel(
 template <int EP, bool WIDE, typename XT, typename WT>
 hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                       int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
-                      int8_t* xq, float* xs, const AlignArgs* al, hipStream_t s) {
+                      int8_t* xq, float* xs, const AlignArgs* al, int32_t* whist, hipStream_t s) {
   const int tb = al ? kFmaTB : p.bt;
   const dim3 grid((unsigned)((T + tb - 1) / tb));
   const dim3 block(64 * p.nw);
@@ -1051,7 +1079,7 @@ hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const f
 #define MOE_FMA(Q, A, TB, NVM)                                                                         \
   route_fma_kernel<EP, WIDE, XT, WT, Q, A, TB, NVM><<<grid, block, 0, s>>>((const XT*)x, (const WT*)wg, bias, \
                                                                            T, H, E, k, ids, w, prob, xq, xs,   \
-                                                                           al ? *al : none)
+                                                                           al ? *al : none, whist)
   if (al) {
     if (xq)
       MOE_FMA(true, true, kFmaTB, 64);
@@ -1085,14 +1113,14 @@ hipError_t launch_fma(const RoutePlan& p, const void* x, const void* wg, const f
 template <int EP, bool WIDE>
 hipError_t launch_fma_dt(const RoutePlan& p, const void* x, int xd, const void* wg, int wd,
                          const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
-                         float* prob, int8_t* xq, float* xs, const AlignArgs* al, hipStream_t s) {
+                         float* prob, int8_t* xq, float* xs, const AlignArgs* al, int32_t* whist, hipStream_t s) {
   if (xd == kF32 && wd == kF32)
-    return launch_fma<EP, WIDE, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+    return launch_fma<EP, WIDE, float, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, whist, s);
   if (xd == kF32 && wd == kBF16)
-    return launch_fma<EP, WIDE, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+    return launch_fma<EP, WIDE, float, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, whist, s);
   if (xd == kBF16 && wd == kF32)
-    return launch_fma<EP, WIDE, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
-  return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+    return launch_fma<EP, WIDE, uint16_t, float>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, whist, s);
+  return launch_fma<EP, WIDE, uint16_t, uint16_t>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, al, whist, s);
 }
 
 template <bool GROUPED>
@@ -1105,15 +1133,21 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
   float* part = (float*)ws;
   float* amax_part = (float*)((uint8_t*)ws + route_part_bytes(T, E, p.ks));
   const dim3 grid((unsigned)((T + p.bt - 1) / p.bt), (unsigned)((E + p.be - 1) / p.be), (unsigned)p.ks);
-#define MOE_RG(RT, RE)                                                                                        \
-  if (xq)                                                                                                   \
-    route_gemm_kernel<true, RT, RE><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part); \
-  else                                                                                                      \
-    route_gemm_kernel<false, RT, RE><<<grid, 256, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, amax_part);
-  if (p.bt == 128) {
-    MOE_RG(128, 128)
+#define MOE_RG(RT, RE, WM, WN)                                                                                 \
+  if (xq)                                                                                                      \
+    route_gemm_kernel<true, RT, RE, WM, WN><<<grid, WM * WN * 64, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part,  \
+                                                                           amax_part);                          \
+  else                                                                                                         \
+    route_gemm_kernel<false, RT, RE, WM, WN><<<grid, WM * WN * 64, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, \
+                                                                            amax_part);
+  if (p.bt == 128 && p.nw == 16) {
+    MOE_RG(128, 128, 4, 4)
+  } else if (p.bt == 128 && p.nw == 8) {
+    MOE_RG(128, 128, 2, 4)
+  } else if (p.bt == 128) {
+    MOE_RG(128, 128, 2, 2)
   } else {
-    MOE_RG(64, 64)
+    MOE_RG(64, 64, 2, 2)
   }
 #undef MOE_RG
   hipError_t err = hipGetLastError();
@@ -1180,6 +1214,7 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, 
     p.be = 128;
     blocks = ((T + 127) / 128) * (E / 128);
   }
+  p.nw = kRouteGemmWaves128;
   // split K while the grid is small: each split keeps >= 2 stages of 64 values
   int ks = 1;
   // (at most 16 splits: the top-k of a small batch loads 16 at once;
@@ -1193,41 +1228,46 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, 
 namespace {
 template <int KQ, int NSUB>
 hipError_t launch_fused_n(const RoutePlan& p, const void* x, const void* wg, const float* bias, int64_t T, int H,
-                          int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, hipStream_t s) {
+                          int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, int32_t* whist,
+                          hipStream_t s) {
   const dim3 grid((unsigned)((T + p.bt - 1) / p.bt));
   if (xq)
     route_fused_kernel<true, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H, E,
-                                                             k, ids, w, prob, xq, xs);
+                                                             k, ids, w, prob, xq, xs, whist);
   else
     route_fused_kernel<false, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H,
-                                                              E, k, ids, w, prob, xq, xs);
+                                                              E, k, ids, w, prob, xq, xs, whist);
   return hipGetLastError();
 }
 
 hipError_t launch_fused(const RoutePlan& p, const void* x, const void* wg, const float* bias, int64_t T, int H,
-                        int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, hipStream_t s) {
+                        int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, int32_t* whist,
+                        hipStream_t s) {
   const int nsub = H / p.ks / 32;
+#define MOE_FUSED(KQ, NS) return launch_fused_n<KQ, NS>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, whist, s)
   if (p.ks == 2) {
-    if (nsub == 2) return launch_fused_n<2, 2>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-    if (nsub == 4) return launch_fused_n<2, 4>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-    if (nsub == 8) return launch_fused_n<2, 8>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-    if (nsub == 16) return launch_fused_n<2, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+    if (nsub == 2) MOE_FUSED(2, 2);
+    if (nsub == 4) MOE_FUSED(2, 4);
+    if (nsub == 8) MOE_FUSED(2, 8);
+    if (nsub == 16) MOE_FUSED(2, 16);
   }
-  if (p.ks == 4 && nsub == 16) return launch_fused_n<4, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
-  if (p.ks == 8 && nsub == 16) return launch_fused_n<8, 16>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+  if (p.ks == 4 && nsub == 16) MOE_FUSED(4, 16);
+  if (p.ks == 8 && nsub == 16) MOE_FUSED(8, 16);
+#undef MOE_FUSED
   return hipErrorInvalidValue;
 }
 
 hipError_t route_any(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                      const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
-                     int8_t* xq, float* xs, void* ws, const AlignArgs* al, hipStream_t s) {
-  if (p.kind == 3) return launch_fused(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, s);
+                     int8_t* xq, float* xs, void* ws, const AlignArgs* al, hipStream_t s, int32_t* whist = nullptr) {
+  if (p.kind == 3) return launch_fused(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, whist, s);
   if (p.kind == 0) {
-    if (E <= 8 && p.nw > 8)
-      return launch_fma_dt<8, true>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
-    if (E <= 8)
-      return launch_fma_dt<8, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
-    return launch_fma_dt<16, false>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, s);
+#define MOE_FMA_DT(EP, WIDE) \
+  return launch_fma_dt<EP, WIDE>(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, al, whist, s)
+    if (E <= 8 && p.nw > 8) MOE_FMA_DT(8, true);
+    if (E <= 8) MOE_FMA_DT(8, false);
+    MOE_FMA_DT(16, false);
+#undef MOE_FMA_DT
   }
   return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, al, s);
 }
@@ -1236,8 +1276,20 @@ hipError_t route_any(const RoutePlan& p, const void* x, int x_dtype, const void*
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg,
                         int wg_dtype, const float* bias, int64_t T, int H, int E, int k,
                         int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, void* ws,
-                        hipStream_t s) {
-  return route_any(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, ws, nullptr, s);
+                        hipStream_t s, int32_t* whist) {
+  return route_any(p, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, prob, xq, xs, ws, nullptr, s,
+                   route_publishes_hist(p, T, k) ? whist : nullptr);
+}
+
+// (small batches keep the one-workgroup align, whose single wave is faster
+// than a workgroup summing the counts: 4.0 vs 5.3 us at 128 slots)
+bool route_publishes_hist(const RoutePlan& p, int64_t T, int k) {
+  return (p.kind == 0 || p.kind == 3) && T * k >= kAlignFromRouteSlots;
+}
+
+int64_t route_hist_groups(const RoutePlan& p, int64_t T, int k) {
+  if (!route_publishes_hist(p, T, k) || T <= 0) return 0;
+  return (T + p.bt - 1) / p.bt;
 }
 
 bool route_align_fusable(const RoutePlan& p, int64_t T, int k) {

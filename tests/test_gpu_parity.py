@@ -295,6 +295,10 @@ ROUTE_ALIGN = [
     (moe_synth.Spec("ra_e16_T10_cap", 10, 256, 16, 4, 64, x_dtype="f32", wg_dtype="f32"), 2, 32, True, True),
     (moe_synth.Spec("ra_e64_T300", 300, 512, 64, 6, 64), 30, 128, False, False),
     (moe_synth.Spec("ra_e8_T100", 100, 512, 8, 2, 64), 0, 256, True, False),
+    # large batches at E <= 64: the route kernel publishes per-workgroup
+    # counts and one align launch takes them (fused E <= 64 router, FMA router)
+    (moe_synth.Spec("ra_e64_T8300_cap", 8300, 256, 64, 6, 64, zipf_s=1.1), 700, 128, True, False),
+    (moe_synth.Spec("ra_e16_T20011_cap", 20011, 128, 16, 4, 64, zipf_s=1.1), 4000, 256, False, False),
 ]
 
 
@@ -501,6 +505,12 @@ SMALL = [
     moe_synth.Spec("i4a8_mid_H384_cap1", 300, 384, 8, 2, 256, w_dtype="i4a8", capacity_factor=1.0, zipf_s=1.1),
     moe_synth.Spec("i4a8_decode_E64", 16, 512, 64, 6, 256, w_dtype="i4a8"),
     moe_synth.Spec("i4a8_decode_H384", 8, 384, 32, 4, 128, w_dtype="i4a8"),
+    # large batches whose route step publishes per-workgroup counts (E <= 64)
+    # and whose align step is one launch over them, with capacity drops
+    moe_synth.Spec("align_from_route_e64_cap", 8300, 256, 64, 6, 128, capacity_factor=1.0, zipf_s=1.1),
+    moe_synth.Spec("align_from_route_e32_i8_cap", 9001, 128, 32, 3, 128, w_dtype="i8", capacity_factor=1.25,
+                   zipf_s=1.1),
+    moe_synth.Spec("align_from_route_e16_fma_cap", 20011, 128, 16, 4, 64, capacity_factor=1.25, zipf_s=1.1),
 ]
 
 
@@ -623,6 +633,7 @@ def _layer_case(c, sample, check_aux=True):
         "counts": torch.empty(s.E, dtype=torch.int32, device="cuda"),
         "offsets": torch.empty(s.E + 1, dtype=torch.int32, device="cuda"),
         "pos": torch.empty((T, k), dtype=torch.int32, device="cuda"),
+        "sorted_slot": torch.empty(T * k, dtype=torch.int32, device="cuda"),
         "num_dropped": torch.empty(1, dtype=torch.int32, device="cuda"),
     }
     out = moe.layer(c.x, c.wg, c.w13, c.w2, k, capacity=c.C or 0, bias=c.bias, s13=c.s13, s2=c.s2, aux=aux,
@@ -637,6 +648,7 @@ def _layer_case(c, sample, check_aux=True):
         np.testing.assert_array_equal(aux["counts"].cpu().numpy(), c.align["counts"])
         np.testing.assert_array_equal(aux["offsets"].cpu().numpy(), c.align["offsets"])
         np.testing.assert_array_equal(pos_g, c.align["pos"])
+        np.testing.assert_array_equal(aux["sorted_slot"].cpu().numpy(), c.align["sorted_slot"])
         assert int(aux["num_dropped"].item()) == c.align["num_dropped"]
     assert agree.mean() > 0.99
     ref = oracle.layer_from_inputs(c.inp, sample_tokens=sample)
