@@ -166,7 +166,9 @@ struct GemmArgs {
   const float* hs;             // down, W8A8: per-row scale of h
   const float* topk_w;         // down: route weight per slot (NULL: 1)
   void* out;                   // up: h [rows, I] bf16; down: y [rows, H] bf16
-  uint32_t* rowmax;            // up, W8A8: max |h| of each row (bit pattern of a non-negative float)
+  float* rowmax;               // up, W8A8: [n_blocks][max rows] each up workgroup's max |h| of
+                               // its rows over its columns (of the bf16-rounded values)
+  int rowmax_stride;           // rows of rowmax per N block
                                // (W4A16: wscale as for W8A8, w packed two codes per byte)
   void* partial;               // down, last-round split: raw partial tiles [conc][BM * BN]
   int H, I, k;
@@ -631,7 +633,12 @@ void gg_kernel(const GemmArgs a) {
       }
     }
   } else if constexpr (UP) {
+    // h is stored in bf16; the row maximum is that of the stored values,
+    // taken here on the fp32 values and rounded once: rounding to nearest is
+    // monotone and symmetric, so max |RN(h_i)| = RN(max |h_i|)
     uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
+    static_assert((1 + WN) * BM * 4 <= S * STAGE, "row scales and per-wave row maxima fit the stages");
+    float* pm = row_scale + BM;   // [WN][BM] per-wave row maxima (freed stage memory)
     float sg[NF / 2], su[NF / 2];
 #pragma unroll
     for (int f = 0; f < NF / 2; ++f) {
@@ -639,37 +646,58 @@ void gg_kernel(const GemmArgs a) {
       sg[f] = a.wscale[(int64_t)e * 2 * a.I + col];
       su[f] = a.wscale[(int64_t)e * 2 * a.I + a.I + col];
     }
+    const bool even = (lane & 1) == 0;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
       float mv[16];   // per accumulator row v: max |h| over this lane's columns
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-        const bool valid = row < rows;
-        const float xsr = row_scale[row];
-        float m = 0.f;
+      for (int v = 0; v < 16; ++v) mv[v] = 0.f;
 #pragma unroll
-        for (int f = 0; f < NF / 2; ++f) {
-          const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+      for (int f = 0; f < NF / 2; ++f) {
+        const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
+        float hv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float xsr = row_scale[wm * WROWS + fm * 32 + acc_row(v, lane)];
           const float gv = (float)acc[fm][f][v] * xsr * sg[f];
           const float uv = (float)acc[fm][NF / 2 + f][v] * xsr * su[f];
-          // h is stored in bf16; the row maximum is that of the stored values
-          const uint32_t hb = f32_to_bf16_bits(silu_f32(gv) * uv);
-          if (valid) h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)hb;
-          m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
+          hv[v] = silu_f32(gv) * uv;
+          mv[v] = fmaxf(mv[v], fabsf(hv[v]));
         }
-        mv[v] = m;
+        // rows v and v + 1 (v even) are consecutive rows, and lanes l and
+        // l ^ 1 consecutive columns: the even lane stores its row v with
+        // its neighbour's column beside it, the odd lane its row v + 1, one
+        // 32-bit store of two bf16 each
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float give = even ? hv[v + 1] : hv[v];
+          const float got = dpp_f32<0xB1>(give);   // lane ^ 1
+          const int row = wm * WROWS + fm * 32 + acc_row(even ? v : v + 1, lane);
+          if (row < rows) {
+            const uint32_t pair = even ? pack_bf16x2(hv[v], got) : pack_bf16x2(got, hv[v + 1]);
+            *reinterpret_cast<uint32_t*>(h + (int64_t)(r0 + row) * a.I + (col & ~1)) = pair;
+          }
+        }
       }
       // the 16 rows' maxima over the 32 columns of each half-wave at once:
       // lane l ends with row v = l % 16 over its 16-lane row, the other
-      // 16-lane row of the half is folded in, and one atomic instruction
-      // (16 lanes per half) publishes them
+      // 16-lane row of the half is folded in; lanes 0-15 and 32-47 hold the
+      // fragment's 32 rows
       const int v = lane & 15;
       const float r16 = rows_max16x16(mv, lane);
       const float m = fmaxf(r16, lane_xor16(r16));
       const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-      if ((lane & 16) == 0 && row < rows) atomicMax(a.rowmax + r0 + row, __float_as_uint(m));
+      if ((lane & 16) == 0) pm[wn * BM + row] = __uint_as_float(f32_to_bf16_bits(m) << 16);
+    }
+    // the workgroup's row maxima over its columns: one plain store per row
+    // (the quantisation step takes the maximum over the N blocks)
+    lds_barrier();
+    if (tid < rows) {
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < WN; ++q) m = fmaxf(m, pm[q * BM + tid]);
+      a.rowmax[(int64_t)nb * a.rowmax_stride + r0 + tid] = m;
     }
   } else {
     uint16_t* y = reinterpret_cast<uint16_t*>(a.out);
@@ -752,8 +780,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const GemmArgs a) {
 // clamped to [-128, 127]; fp32 IEEE arithmetic.  The tile list covers rows
 // [0, N) in order, so N is the end of the last tile; waves past it exit.
 __global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict__ h,
-                                                      const uint32_t* __restrict__ rowmax,
-                                                      const int32_t* __restrict__ tiles,
+                                                      const float* __restrict__ rowmax, int nparts,
+                                                      int64_t stride, const int32_t* __restrict__ tiles,
                                                       const int32_t* __restrict__ num_tiles, int I,
                                                       int8_t* __restrict__ hq, float* __restrict__ hs) {
   const int nt = *num_tiles;
@@ -762,7 +790,10 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= (int64_t)last.y + last.z) return;
   const int lane = threadIdx.x & 63;
-  const float am = __uint_as_float(rowmax[r]);
+  // the row's max |h|: the up workgroups' partial maxima, one per N block
+  float am = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += 64)
+    am = fmaxf(am, wave_max(p0 + lane < nparts ? rowmax[(int64_t)(p0 + lane) * stride + r] : 0.f));
   const float s = am == 0.f ? 1.f : am / 127.f;
   const float rs = 1.f / s;
   for (int c = lane * 8; c < I; c += 512) {
@@ -774,11 +805,6 @@ __global__ __launch_bounds__(256) void quant_h_kernel(const uint16_t* __restrict
     *reinterpret_cast<uint2*>(hq + r * I + c) = make_uint2(b[0], b[1]);
   }
   if (lane == 0) hs[r] = s;
-}
-
-__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* __restrict__ p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
 }
 
 // ------------------------------------------------------------ fp32 path --
@@ -844,7 +870,7 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct FfnBufs {
   void* h;
-  uint32_t* rowmax;
+  float* rowmax;   // W8A8: [parts][n] partial row maxima of |h|, one row block per up N block
   int8_t* hq;
   float* hs;
   void* partial;   // down, last-round split
@@ -854,23 +880,6 @@ struct FfnBufs {
 // at most kTailParts partial 256 x 256 tiles of 4 bytes
 constexpr int kTailParts = 256;
 constexpr size_t kTailBytes = (size_t)kTailParts * 256 * 256 * 4;
-
-FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int down_var) {
-  uint8_t* wsb = (uint8_t*)ws;
-  FfnBufs b{wsb, nullptr, nullptr, nullptr, nullptr};
-  const bool a8 = w_dtype == kI8 || w_dtype == kI4A8;   // int8 activations: bf16 h, then hq
-  size_t off = align256((size_t)n * I * (w_dtype == kF32 ? 4 : 2));
-  if (a8) {
-    b.rowmax = (uint32_t*)(wsb + off);
-    off += align256((size_t)n * 4);
-    b.hq = (int8_t*)(wsb + off);
-    off += align256((size_t)n * I);
-    b.hs = (float*)(wsb + off);
-    off += align256((size_t)n * 4);
-  }
-  if ((w_dtype == kBF16 || w_dtype == kI8) && down_var == 0) b.partial = wsb + off;
-  return b;
-}
 
 // workgroups resident at once for the one-per-CU prefill tile: the device's
 // compute units, capped at kTailParts (queried once per device)
@@ -923,6 +932,29 @@ constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {128, 256, 1, 4, 
                                   {128, 128, 1, 2, 3, 128, 8}, {64, 128, 1, 2, 3, 128, 8},
                                   {256, 64, 2, 2, 3, 128, 8},  {128, 64, 1, 2, 3, 128, 8},
                                   {64, 64, 1, 2, 3, 128, 8}};
+
+// the up GEMM's N blocks (each writes one partial row maximum per row of h)
+int up_parts(int I, int w_dtype, int up_var) {
+  const int bn = (w_dtype == kI4 || w_dtype == kI4A8 ? kUpVarW4 : kUpVar)[up_var].bn;
+  return I / (bn / 2);
+}
+
+FfnBufs carve_ffn(void* ws, int64_t n, int I, int w_dtype, int up_var, int down_var) {
+  uint8_t* wsb = (uint8_t*)ws;
+  FfnBufs b{wsb, nullptr, nullptr, nullptr, nullptr};
+  const bool a8 = w_dtype == kI8 || w_dtype == kI4A8;   // int8 activations: bf16 h, then hq
+  size_t off = align256((size_t)n * I * (w_dtype == kF32 ? 4 : 2));
+  if (a8) {
+    b.rowmax = (float*)(wsb + off);
+    off += align256((size_t)n * 4 * up_parts(I, w_dtype, up_var));
+    b.hq = (int8_t*)(wsb + off);
+    off += align256((size_t)n * I);
+    b.hs = (float*)(wsb + off);
+    off += align256((size_t)n * 4);
+  }
+  if ((w_dtype == kBF16 || w_dtype == kI8) && down_var == 0) b.partial = wsb + off;
+  return b;
+}
 
 #define MOE_GG_CASE(IDX, BM, BN, WM, WN, S, R, G) \
   case IDX:                                       \
@@ -1003,8 +1035,6 @@ hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const v
                      const float* s13, const int32_t* sorted_slot, const int32_t* tiles,
                      const int32_t* num_tiles, int64_t T, int H, int I, int k, const FfnBufs& b,
                      hipStream_t s) {
-  const int64_t n = T * k;
-  if (I8) zero_u32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(b.rowmax, n);
   GemmArgs a{};
   a.act = (const uint8_t*)act;
   a.w = (const uint8_t*)w13;
@@ -1015,6 +1045,7 @@ hipError_t launch_up(const FfnPlan& p, const void* act, const float* xs, const v
   a.wscale = s13;
   a.out = b.h;
   a.rowmax = b.rowmax;
+  a.rowmax_stride = (int)(T * k);
   a.H = H;
   a.I = I;
   a.k = k;
@@ -1029,8 +1060,9 @@ hipError_t launch_down(const FfnPlan& p, const void* w2, const float* s2, const 
                        const int32_t* tiles, const int32_t* num_tiles, const float* topk_w, int64_t rows,
                        int H, int I, void* y, const FfnBufs& b, hipStream_t s) {
   if (I8)
-    quant_h_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>((const uint16_t*)b.h, b.rowmax, tiles,
-                                                              num_tiles, I, b.hq, b.hs);
+    quant_h_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(
+        (const uint16_t*)b.h, b.rowmax, up_parts(I, W4 ? kI4A8 : kI8, p.up_var), rows, tiles, num_tiles, I,
+        b.hq, b.hs);
   GemmArgs a{};
   a.act = I8 ? (const uint8_t*)b.hq : (const uint8_t*)b.h;
   a.w = (const uint8_t*)w2;
@@ -1107,8 +1139,8 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     if (w_dtype == kI4)
       p.ws_bytes = align256((size_t)n * I * 2);
     else
-      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4) + align256((size_t)n * I) +
-                   align256((size_t)n * 4);
+      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4 * up_parts(I, w_dtype, p.up_var)) +
+                   align256((size_t)n * I) + align256((size_t)n * 4);
   } else {
     // shape class from the mean rows per expert: decode-sized (weight
     // streaming, short tiles), mid (one 256-row tile per expert, waves split
@@ -1129,8 +1161,8 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     if (w_dtype == kBF16)
       p.ws_bytes = align256((size_t)n * I * 2);
     else
-      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4) + align256((size_t)n * I) +
-                   align256((size_t)n * 4);
+      p.ws_bytes = align256((size_t)n * I * 2) + align256((size_t)n * 4 * up_parts(I, w_dtype, p.up_var)) +
+                   align256((size_t)n * I) + align256((size_t)n * 4);
     if (p.down_var == 0) p.ws_bytes += kTailBytes;
   }
   p.max_tiles = align_max_tiles(T, k, E, p.block_m);
@@ -1141,7 +1173,7 @@ hipError_t launch_ffn_up(const FfnPlan& p, const void* x, const float* xs, const
                          int w_dtype, const float* s13, const int32_t* sorted_slot,
                          const int32_t* tiles, const int32_t* num_tiles, int64_t T, int H, int I,
                          int k, void* ws, hipStream_t s) {
-  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.down_var);
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.up_var, p.down_var);
   if (w_dtype == kF32) {
     const unsigned mt = (unsigned)p.max_tiles;
     ffn_f32_kernel<true><<<mt * (I / 32), 256, 0, s>>>((const float*)x, (const float*)w13, sorted_slot,
@@ -1162,7 +1194,7 @@ hipError_t launch_ffn_down(const FfnPlan& p, const void* w2, int w_dtype, const 
                            const int32_t* sorted_slot, const int32_t* tiles,
                            const int32_t* num_tiles, const float* topk_w, int64_t T, int H, int I,
                            int k, void* y, void* ws, hipStream_t s) {
-  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.down_var);
+  const FfnBufs b = carve_ffn(ws, T * k, I, w_dtype, p.up_var, p.down_var);
   if (w_dtype == kF32) {
     const unsigned mt = (unsigned)p.max_tiles;
     ffn_f32_kernel<false><<<mt * (H / 32), 256, 0, s>>>((const float*)b.h, (const float*)w2,
