@@ -604,100 +604,98 @@ void gg_kernel(const GemmArgs a) {
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) fv[fm] = fm < fmv;
 
-  if constexpr (UP && !I8) {
-    uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
-    float sg[NF / 2], su[NF / 2];
+  if constexpr (UP) {
+    // SwiGLU, h = silu(g) * u with g = ag * cg, u = au * cu (ag, au the
+    // accumulators; cg, cu the dequantisation: the token's scale times the
+    // channel's for W8A8, the channel's for int4 weights, else 1), as
+    //   h = (ag * au) * (cg * cu) / (1 + 2^(ag * cg * -log2 e)),
+    // one product, one exponential and one (hardware) reciprocal per value.
+    // h is stored in bf16.  W8A8 also takes each row's max |h| for the
+    // quantisation of h: on the fp32 values, rounded once (rounding to
+    // nearest is monotone and symmetric, so max |RN(h_i)| = RN(max |h_i|)).
+    constexpr float kNegLog2e = -1.44269504088896341f;
+    uint8_t* const hbase = reinterpret_cast<uint8_t*>(a.out) + (int64_t)r0 * a.I * 2;
+    float* pm = row_scale + BM;   // [WN][BM] per-wave row maxima (freed stage memory)
+    float kg[NF / 2], kgu[NF / 2];
 #pragma unroll
     for (int f = 0; f < NF / 2; ++f) {
       const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
-      sg[f] = W4 ? a.wscale[(int64_t)e * 2 * a.I + col] : 1.f;
-      su[f] = W4 ? a.wscale[(int64_t)e * 2 * a.I + a.I + col] : 1.f;
+      const bool scaled = I8 || W4;
+      const float sg = scaled ? a.wscale[(int64_t)e * 2 * a.I + col] : 1.f;
+      const float su = scaled ? a.wscale[(int64_t)e * 2 * a.I + a.I + col] : 1.f;
+      kg[f] = sg * kNegLog2e;
+      kgu[f] = sg * su;
     }
+    // Rows v and v + 1 (v even) of a fragment are consecutive rows, and
+    // lanes l and l ^ 1 consecutive columns: each lane packs its two rows'
+    // bf16 values, swaps the pack with its neighbour, and a byte permute
+    // forms one row's two columns, row v on the even lane, row v + 1 on the
+    // odd one: one 32-bit store per two values.
+    const bool odd = (lane & 1) != 0;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
+      float xr[16], mv[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-        if (row >= rows) continue;
-#pragma unroll
-        for (int f = 0; f < NF / 2; ++f) {
-          const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
-          float gv = (float)acc[fm][f][v], uv = (float)acc[fm][NF / 2 + f][v];
-          if constexpr (W4) {
-            gv *= sg[f];
-            uv *= su[f];
-          }
-          h[(int64_t)(r0 + row) * a.I + col] = (uint16_t)f32_to_bf16_bits(silu_f32(gv) * uv);
-        }
+        xr[v] = I8 ? row_scale[wm * WROWS + fm * 32 + acc_row(v, lane)] : 1.f;
+        mv[v] = 0.f;
       }
-    }
-  } else if constexpr (UP) {
-    // h is stored in bf16; the row maximum is that of the stored values,
-    // taken here on the fp32 values and rounded once: rounding to nearest is
-    // monotone and symmetric, so max |RN(h_i)| = RN(max |h_i|)
-    uint16_t* h = reinterpret_cast<uint16_t*>(a.out);
-    static_assert((1 + WN) * BM * 4 <= S * STAGE, "row scales and per-wave row maxima fit the stages");
-    float* pm = row_scale + BM;   // [WN][BM] per-wave row maxima (freed stage memory)
-    float sg[NF / 2], su[NF / 2];
-#pragma unroll
-    for (int f = 0; f < NF / 2; ++f) {
-      const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
-      sg[f] = a.wscale[(int64_t)e * 2 * a.I + col];
-      su[f] = a.wscale[(int64_t)e * 2 * a.I + a.I + col];
-    }
-    const bool even = (lane & 1) == 0;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      if (!fv[fm]) continue;
-      float mv[16];   // per accumulator row v: max |h| over this lane's columns
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mv[v] = 0.f;
+      // this lane's store row for v = 0 (even lanes) or 1 (odd lanes)
+      const int rl = wm * WROWS + fm * 32 + 4 * (lane >> 5) + (odd ? 1 : 0);
 #pragma unroll
       for (int f = 0; f < NF / 2; ++f) {
-        const int col = nb * HB + wn * HW + f * 32 + (lane & 31);
-        float hv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float xsr = row_scale[wm * WROWS + fm * 32 + acc_row(v, lane)];
-          const float gv = (float)acc[fm][f][v] * xsr * sg[f];
-          const float uv = (float)acc[fm][NF / 2 + f][v] * xsr * su[f];
-          hv[v] = silu_f32(gv) * uv;
-          mv[v] = fmaxf(mv[v], fabsf(hv[v]));
-        }
-        // rows v and v + 1 (v even) are consecutive rows, and lanes l and
-        // l ^ 1 consecutive columns: the even lane stores its row v with
-        // its neighbour's column beside it, the odd lane its row v + 1, one
-        // 32-bit store of two bf16 each
+        const int colp = (nb * HB + wn * HW + f * 32 + (lane & 31)) & ~1;
+        // element offset of this lane's store for v = 0; row v adds a
+        // wave-uniform multiple of I
+        uint32_t obase = (uint32_t)(rl * a.I + colp);
+        // (kept opaque so the compiler does not fold the row offsets back
+        // into one 32-bit multiply per store)
+        asm volatile("" : "+v"(obase));
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
-          const float give = even ? hv[v + 1] : hv[v];
-          const float got = dpp_f32<0xB1>(give);   // lane ^ 1
-          const int row = wm * WROWS + fm * 32 + acc_row(even ? v : v + 1, lane);
-          if (row < rows) {
-            const uint32_t pair = even ? pack_bf16x2(hv[v], got) : pack_bf16x2(got, hv[v + 1]);
-            *reinterpret_cast<uint32_t*>(h + (int64_t)(r0 + row) * a.I + (col & ~1)) = pair;
+          float hh[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const float ag = (float)acc[fm][f][v + j], au = (float)acc[fm][NF / 2 + f][v + j];
+            const float t = I8 ? ag * (xr[v + j] * kg[f]) : ag * kg[f];
+            const float q = I8 ? (ag * au) * (xr[v + j] * xr[v + j] * kgu[f])
+                               : ((W4 ? ag * au * kgu[f] : ag * au));
+            hh[j] = q * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(t));
+            if constexpr (I8) mv[v + j] = fmaxf(mv[v + j], fabsf(hh[j]));
           }
+          const uint32_t mine = pack_bf16x2(hh[0], hh[1]);
+          const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp((int)mine, (int)mine, 0xB1, 0xF, 0xF, false);
+          const uint32_t pair = __builtin_amdgcn_perm(other, mine, sel);
+          const int dv = 8 * (v >> 2) + (v & 3);   // unrolled: a constant
+          if (rl + dv < rows)
+            *reinterpret_cast<uint32_t*>(hbase + (obase + (uint32_t)(dv * a.I)) * 2u) = pair;
         }
       }
-      // the 16 rows' maxima over the 32 columns of each half-wave at once:
-      // lane l ends with row v = l % 16 over its 16-lane row, the other
-      // 16-lane row of the half is folded in; lanes 0-15 and 32-47 hold the
-      // fragment's 32 rows
-      const int v = lane & 15;
-      const float r16 = rows_max16x16(mv, lane);
-      const float m = fmaxf(r16, lane_xor16(r16));
-      const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-      if ((lane & 16) == 0) pm[wn * BM + row] = __uint_as_float(f32_to_bf16_bits(m) << 16);
+      if constexpr (I8) {
+        // the 16 rows' maxima over the 32 columns of each half-wave at once:
+        // lane l ends with row v = l % 16 over its 16-lane row, the other
+        // 16-lane row of the half is folded in; lanes 0-15 and 32-47 hold the
+        // fragment's 32 rows
+        const int v = lane & 15;
+        const float r16 = rows_max16x16(mv, lane);
+        const float m = fmaxf(r16, lane_xor16(r16));
+        const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
+        if ((lane & 16) == 0) pm[wn * BM + row] = __uint_as_float(f32_to_bf16_bits(m) << 16);
+      }
     }
-    // the workgroup's row maxima over its columns: one plain store per row
-    // (the quantisation step takes the maximum over the N blocks)
-    lds_barrier();
-    if (tid < rows) {
-      float m = 0.f;
+    if constexpr (I8) {
+      static_assert((1 + WN) * BM * 4 <= S * STAGE, "row scales and per-wave row maxima fit the stages");
+      // the workgroup's row maxima over its columns: one plain store per row
+      // (the quantisation step takes the maximum over the N blocks)
+      lds_barrier();
+      if (tid < rows) {
+        float m = 0.f;
 #pragma unroll
-      for (int q = 0; q < WN; ++q) m = fmaxf(m, pm[q * BM + tid]);
-      a.rowmax[(int64_t)nb * a.rowmax_stride + r0 + tid] = m;
+        for (int q = 0; q < WN; ++q) m = fmaxf(m, pm[q * BM + tid]);
+        a.rowmax[(int64_t)nb * a.rowmax_stride + r0 + tid] = m;
+      }
     }
   } else {
     uint16_t* y = reinterpret_cast<uint16_t*>(a.out);
