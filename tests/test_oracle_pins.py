@@ -198,6 +198,25 @@ def test_capacity_closed_forms():
     assert oracle.capacity(16384, 6, 64, 1.25) == 1920
     assert oracle.capacity(10, 3, 4, 1.25) == 10          # 9.375 rounds up
     assert oracle.capacity(64, 2, 8, 0.0) is None
+    # factors written in decimal: the decimal value decides, not its binary float
+    # (the double nearest 1.1 lies above it, so a float product would round to 12)
+    assert oracle.capacity(80, 2, 16, 1.1) == 11
+    assert oracle.capacity(100, 1, 10, 1.1) == 11
+    assert oracle.capacity(7, 1, 3, 1.1) == 3           # ceil(2.566...)
+
+
+def test_capacity_is_the_decimal_ceiling():
+    """C = ceil(f * T * k / E) with f the decimal the caller wrote, computed in
+    exact rationals from the decimal string (not from the oracle's float)."""
+    from fractions import Fraction
+    factors = ["0.1", "0.3", "0.7", "1.0", "1.05", "1.1", "1.15", "1.2", "1.25", "1.3", "1.35", "1.5", "1.7",
+               "1.9", "2.2", "2.5", "3.3", "1.333", "0.001"]
+    loads = [(80, 2, 16), (100, 1, 10), (4096, 8, 256), (16384, 6, 64), (7, 1, 3), (1000, 3, 7), (30, 1, 9),
+             (65536, 8, 256), (12, 5, 11)]
+    for f in factors:
+        for T, k, E in loads:
+            want = math.ceil(Fraction(f) * Fraction(T * k, E))
+            assert oracle.capacity(T, k, E, float(f)) == want, (f, T, k, E)
 
 
 def test_tiles_cover_rows():
