@@ -4,14 +4,15 @@
 
 A step is one whole-layer call (moe_layer) over one batch of seeded synthetic
 inputs already resident in HBM.  The default workload is the Mixtral-8x7B
-shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  After the K
-timed steps, K launches of each step of the layer (through its own entry
-point) are captured in a HIP graph and replayed between two HIP events on the
-replaying stream, to get each kernel's average duration without the host's
-per-call cost (which exceeds the small kernels' own times); the
-dominant kernel's roofline is computed from those durations and its
-algorithmic flops/bytes.  A cold pass (after a 1 GiB write) gives each step's
-time with its inputs in HBM.  The CPU oracle is timed on a bounded token
+shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  Each timed
+layer call records six events of the caller's around its five steps
+(moe_layer_aux.stage_events), which time every step inside the timed region;
+the dominant kernel's roofline is computed from its average there and its
+algorithmic flops/bytes.  After the K timed steps, K launches of each step
+(through its own entry point) are captured in a HIP graph and replayed
+between two HIP events, for each kernel's time launched back to back, and a
+cold pass (after a 1 GiB write) gives each step's time with its inputs in
+HBM.  The CPU oracle is timed on a bounded token
 sample of the same workload on the host cores (a baseline, not the target).
 
 Prints exactly one JSON line.
@@ -344,9 +345,9 @@ def main() -> int:
     ids_buf = torch.empty((T, k), dtype=torch.int32, device="cuda")
     aux = {"counts": counts, "offsets": offsets, "topk_ids": ids_buf}
 
-    def step(with_aux=False):
+    def step(with_aux=False, events=None):
         layer(d["x"], d["wg"], d["w13"], d["w2"], C, d["bias"], d["s13"], d["s2"], out=out,
-              aux=aux if with_aux else None)
+              aux=aux if with_aux else ({"stage_events": events} if events else None))
 
     step(True)
     torch.cuda.synchronize()
@@ -357,14 +358,22 @@ def main() -> int:
     N, D = int(off[-1]), int((kept > 0).sum())
     log(f"dispatch: {dispatch}; N={N} D={D}")
 
+    # each timed layer call records six events of its own around its five
+    # steps (moe_layer_aux.stage_events), so every step is timed inside the
+    # timed region, in the layer's order and on the layer's stream
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for es in ev_sets:
+        for e in es:
+            e.record()                      # torch creates its events lazily, at the first record
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in es] for es in ev_sets]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(args.steps):
-        step()
+        step(events=handles[i])
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -374,6 +383,10 @@ def main() -> int:
     log(f"layer: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on the stream "
         f"(p10 {np.percentile(per_step, 10):.3f}, median {np.median(per_step):.3f}, "
         f"p90 {np.percentile(per_step, 90):.3f})")
+    step_names = ("route", "align", "ffn_up", "ffn_down", "combine")
+    in_layer = {n: float(np.mean([es[j].elapsed_time(es[j + 1]) for es in ev_sets]))
+                for j, n in enumerate(step_names)}
+    log("steps inside the timed layer calls (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in in_layer.items()))
 
     # per-kernel durations: each step (entry point) launched back to back
     # `steps` times between two events on the library's stream
@@ -465,7 +478,8 @@ def main() -> int:
     align_bytes = 12 * T * k
     combine_bytes = N * H * by + T * H * bo + 4 * T * k
     dt = spec.w_dtype
-    up_s = stage_ms["ffn_up"] * 1e-3
+    # the dominant kernel's time: its average inside the timed layer calls
+    up_s = in_layer["ffn_up"] * 1e-3
     ai = up_flops / up_bytes
     if ai >= RIDGE[dt]:
         roof = {"bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": PEAK_TFLOPS[dt],
@@ -475,7 +489,9 @@ def main() -> int:
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["kernel"] = "up GEMM: " + (dispatch.split("|")[2].strip().split("+")[0]
                                      if dispatch.count("|") >= 3 else "gg_kernel")
-    roof["per_launch"] = {"flops": up_flops, "bytes": up_bytes, "ms": stage_ms["ffn_up"]}
+    roof["per_launch"] = {"flops": up_flops, "bytes": up_bytes, "ms": in_layer["ffn_up"],
+                          "timed": "average over the timed layer calls, between the layer's own events",
+                          "ms_back_to_back": stage_ms["ffn_up"]}
     roof["traffic"] = traffic_for(spec.name, os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "csrc",
                                                           "ffn.hip"))
     gemm_s = (stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e-3
@@ -491,6 +507,7 @@ def main() -> int:
                                 "GBps": rac_bytes / rac_s / 1e9,
                                 "frac_of_hbm": rac_bytes / rac_s / 1e9 / PEAK_HBM_GBPS},
         "stages_ms": stage_ms,
+        "stages_ms_in_layer": in_layer,
         "stages_ms_cold": cold_ms,
         "route_align_combine_cold": {"ms": sum(cold_ms[n] for n in ("route", "align", "combine")),
                                      "frac_of_hbm": rac_bytes / (sum(cold_ms[n] for n in ("route", "align", "combine"))

@@ -290,6 +290,12 @@ moe_status moe_combine_shared(const void* y_sorted, int32_t y_dtype, const int32
  * buffers the layer writes its intermediates to instead of the workspace:
  * topk_ids/topk_w/topk_p [T,k], counts [E], offsets [E+1], sorted_slot and
  * pos [T*k], num_dropped [1], xq [T,H] int8 and xs [T] (W8A8 only).
+ * aux->stage_events (each entry may be NULL) are hipEvent_t handles the
+ * caller created; the layer records them on its stream before the route
+ * step and after each of its five steps (route, align, up GEMM, down GEMM
+ * with the W8A8 quantisation of h, combine), so the caller can time every
+ * step inside a layer call.  They are checked (hipEventQuery) before the
+ * first launch; the layer only records them.
  * The layer returns the MoE branch only: the caller adds the residual, which
  * is where dropped assignments go.
  */
@@ -304,6 +310,7 @@ typedef struct moe_layer_aux {
   int32_t* num_dropped;
   int8_t* xq;
   float* xs;
+  void* stage_events[6];
 } moe_layer_aux;
 
 size_t moe_layer_workspace_size(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,

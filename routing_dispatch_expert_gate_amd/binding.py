@@ -74,7 +74,7 @@ SIGNATURES = {
 
 class MoeLayerAux(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("topk_ids", "topk_w", "topk_p", "counts", "offsets", "sorted_slot",
-                                   "pos", "num_dropped", "xq", "xs")]
+                                   "pos", "num_dropped", "xq", "xs")] + [("stage_events", _vp * 6)]
 
 
 class MoeLayerOptions(ctypes.Structure):
@@ -341,14 +341,21 @@ class Layer:
     def __call__(self, x, wg, w13, w2, capacity=0, bias=None, s13=None, s2=None, out=None, aux=None,
                  options: dict | None = None):
         """``options`` (a dict of moe_layer_options members: n_group,
-        topk_group, shared, shared_factor, out_bias) selects moe_layer_ex."""
+        topk_group, shared, shared_factor, out_bias) selects moe_layer_ex.
+        ``aux`` maps moe_layer_aux member names to device tensors, and
+        ``stage_events`` to six hipEvent_t handles (ints, or None)."""
         T, H, I, E, k = self.shape
         if out is None:
             out = torch.empty((T, H), dtype=x.dtype, device=x.device)
         aux_s = None
         if aux is not None:
             aux_s = MoeLayerAux(**{n: (aux[n].data_ptr() if aux.get(n) is not None else None)
-                                   for n, _ in MoeLayerAux._fields_})
+                                   for n, _ in MoeLayerAux._fields_ if n != "stage_events"})
+            ev = aux.get("stage_events")
+            if ev is not None:
+                if len(ev) != 6:
+                    raise ValueError("stage_events takes six hipEvent_t handles (ints or None)")
+                aux_s.stage_events = (_vp * 6)(*ev)
         args = [_p(x), _DT[x.dtype], _p(wg), _DT[wg.dtype], _p(bias), _p(w13), _p(w2), _DT[self.w_dtype],
                 _p(s13), _p(s2), T, H, I, E, k, int(capacity), _p(out), _DT[out.dtype],
                 ctypes.byref(aux_s) if aux_s is not None else None]

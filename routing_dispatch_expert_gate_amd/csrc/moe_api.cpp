@@ -749,6 +749,14 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
     workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
   }
   MOE_TRY(check_ws(workspace, workspace_bytes, c.total));
+  if (aux) {
+    for (int i = 0; i < 6; ++i) {
+      if (!aux->stage_events[i]) continue;
+      const hipError_t q = hipEventQuery((hipEvent_t)aux->stage_events[i]);
+      if (q != hipSuccess && q != hipErrorNotReady)
+        return fail(MOE_ERR_INVALID_ARG, "moe_layer stage_events[%d]: %s", i, hipGetErrorString(q));
+    }
+  }
 
   uint8_t* base = (uint8_t*)workspace;
   auto pick = [&](auto* user, size_t off) {
@@ -772,18 +780,24 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
   void* y = base + c.y;
   void* scratch = base + c.scratch;
   hipStream_t s = (hipStream_t)stream;
+  // the caller's timing events around the steps (already checked)
+  auto mark = [&](int i) -> hipError_t {
+    return a.stage_events[i] ? hipEventRecord((hipEvent_t)a.stage_events[i], s) : hipSuccess;
+  };
 
   // the fused route + align (moe_route_align) saves a launch but puts every
   // token's top-k on one workgroup: measured ~2 us slower on the GPU at
   // decode than route_topk's four workgroups plus the align launch, so the
   // layer, which runs GPU-bound, keeps the two launches
   const bool fused = false;
-  hipError_t e;
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer stage event");
   if (fused) {
     e = moe::launch_route_align_fused(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch,
                                       capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts, offsets,
                                       sorted_slot, pos, tiles, num_tiles, num_dropped, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route+align launch");
+    if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   } else {
     // route kinds that publish per-workgroup counts (E <= 64) let one align
     // launch take them instead of histogramming the ids again
@@ -795,6 +809,7 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
     else
       e = moe::launch_route(c.rp, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, ids, w, p, xq, xs, scratch, s, whist);
     if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
+    if ((e = mark(1)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
     if (from_route)
       e = moe::launch_align_from_route(ids, whist, moe::route_hist_groups(c.rp, T, k), c.rp.bt, T, k, E,
                                        capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts, offsets,
@@ -803,19 +818,23 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
       e = moe::launch_align(c.ap, ids, T, k, E, capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts,
                             offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, scratch, s);
     if (e != hipSuccess) return hip_fail(e, "moe_layer align launch");
+    if ((e = mark(2)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   }
   e = moe::launch_ffn_up(c.fp, act == MOE_I8 ? (const void*)xq : x, xs, w13, w_dtype, s13,
                          sorted_slot, tiles, num_tiles, T, H, I, k, scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn up launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   e = moe::launch_ffn_down(c.fp, w2, w_dtype, s2, sorted_slot, tiles, num_tiles, w, T, H, I, k, y,
                            scratch, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer ffn down launch");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   if (merge)
     e = moe::launch_combine_shared(y, ydt, pos, nullptr, T, k, H, o.shared, o.shared_factor, o.out_bias, out,
                                    out_dtype, s);
   else
     e = moe::launch_combine(y, ydt, pos, nullptr, T, k, H, out, out_dtype, s);
   if (e != hipSuccess) return hip_fail(e, "moe_layer combine launch");
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   const bool from_route_d = !grouped && moe::route_publishes_hist(c.rp, T, k);
   return ok(route_name(c.rp) + (grouped ? "<grouped>" : "") + " | " +
             (fused ? std::string("align(fused into route)")

@@ -737,6 +737,36 @@ def test_layer_replays_from_a_hip_graph(spec):
     assert torch.equal(scratch, ref_other)
 
 
+@pytest.mark.parametrize("spec", [GRAPH_CASES[0], GRAPH_CASES[1],
+                                  moe_synth.Spec("events_from_route_E8", 2048, 256, 8, 2, 256)],
+                         ids=["bf16_E64_cap", "w8a8_E16", "from_route_E8"])
+def test_layer_stage_events_time_each_step(spec):
+    """moe_layer_aux.stage_events: the layer records the caller's six events
+    around its five steps; the output is the same as without them, and the
+    five intervals are non-negative and add up to the whole call."""
+    moe = _moe()
+    c = Case(spec, 77)
+    L = moe.Layer(spec.T, spec.H, spec.I, spec.E, spec.k, c.x.dtype, c.w13.dtype)
+    C = c.C or 0
+    ref = L(c.x, c.wg, c.w13, c.w2, C, c.bias, c.s13, c.s2)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    ev_some = [evs[0].cuda_event, None, evs[2].cuda_event, None, None, evs[5].cuda_event]
+    out_some = L(c.x, c.wg, c.w13, c.w2, C, c.bias, c.s13, c.s2, aux={"stage_events": ev_some})
+    torch.cuda.synchronize()
+    assert torch.equal(out_some.view(torch.int16), ref.view(torch.int16))
+    out = L(c.x, c.wg, c.w13, c.w2, C, c.bias, c.s13, c.s2, aux={"stage_events": [e.cuda_event for e in evs]})
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    steps = [evs[j].elapsed_time(evs[j + 1]) for j in range(5)]
+    total = evs[0].elapsed_time(evs[5])
+    assert all(t >= 0 for t in steps), steps
+    assert abs(sum(steps) - total) <= 1e-3 + 1e-3 * total, (steps, total)
+
+
 def test_empty_batch_is_a_noop():
     moe = _moe()
     x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
