@@ -4,11 +4,11 @@
 
 A step is one whole-layer call (moe_layer) over one batch of seeded synthetic
 inputs already resident in HBM.  The default workload is the Mixtral-8x7B
-shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  Each timed
-layer call records six events of the caller's around its five steps
-(moe_layer_aux.stage_events), which time every step inside the timed region;
-the dominant kernel's roofline is computed from its average there and its
-algorithmic flops/bytes.  After the K timed steps, K launches of each step
+shaped prefill layer (T=4096, H=4096, E=8, top-2, I=14336, bf16).  Right
+after the K timed steps, K more layer calls each record six events of the
+bench's around their five steps (moe_layer_aux.stage_events), which time
+every step inside a layer call; the dominant kernel's roofline is computed
+from its average there and its algorithmic flops/bytes.  Then K launches of each step
 (through its own entry point) are captured in a HIP graph and replayed
 between two HIP events, for each kernel's time launched back to back, and a
 cold pass (after a 1 GiB write) gives each step's time with its inputs in
@@ -358,22 +358,14 @@ def main() -> int:
     N, D = int(off[-1]), int((kept > 0).sum())
     log(f"dispatch: {dispatch}; N={N} D={D}")
 
-    # each timed layer call records six events of its own around its five
-    # steps (moe_layer_aux.stage_events), so every step is timed inside the
-    # timed region, in the layer's order and on the layer's stream
-    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for es in ev_sets:
-        for e in es:
-            e.record()                      # torch creates its events lazily, at the first record
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    handles = [[e.cuda_event for e in es] for es in ev_sets]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(args.steps):
-        step(events=handles[i])
+        step()
         evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -383,10 +375,24 @@ def main() -> int:
     log(f"layer: {ms_per_step:.3f} ms/step wall, {gpu_ms:.3f} ms/step on the stream "
         f"(p10 {np.percentile(per_step, 10):.3f}, median {np.median(per_step):.3f}, "
         f"p90 {np.percentile(per_step, 90):.3f})")
+    # the same layer calls again, K of them right after the timed ones, each
+    # recording six events of the bench's around its five steps
+    # (moe_layer_aux.stage_events): every step timed inside a layer call, in
+    # the layer's order and on the layer's stream.  The timed steps above
+    # carry no events: each record costs ~3.5 us on the GPU's timeline (+4%
+    # at the decode workload, +60% at the tiny one).
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for es in ev_sets:
+        for e in es:
+            e.record()                      # torch creates its events lazily, at the first record
+    torch.cuda.synchronize()
+    for es in ev_sets:
+        step(events=[e.cuda_event for e in es])
+    torch.cuda.synchronize()
     step_names = ("route", "align", "ffn_up", "ffn_down", "combine")
     in_layer = {n: float(np.mean([es[j].elapsed_time(es[j + 1]) for es in ev_sets]))
                 for j, n in enumerate(step_names)}
-    log("steps inside the timed layer calls (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in in_layer.items()))
+    log("steps inside layer calls (ms): " + ", ".join(f"{n}={v:.4f}" for n, v in in_layer.items()))
 
     # per-kernel durations: each step (entry point) launched back to back
     # `steps` times between two events on the library's stream
@@ -478,7 +484,7 @@ def main() -> int:
     align_bytes = 12 * T * k
     combine_bytes = N * H * by + T * H * bo + 4 * T * k
     dt = spec.w_dtype
-    # the dominant kernel's time: its average inside the timed layer calls
+    # the dominant kernel's time: its average inside the layer calls
     up_s = in_layer["ffn_up"] * 1e-3
     ai = up_flops / up_bytes
     if ai >= RIDGE[dt]:
@@ -490,7 +496,8 @@ def main() -> int:
     roof["kernel"] = "up GEMM: " + (dispatch.split("|")[2].strip().split("+")[0]
                                      if dispatch.count("|") >= 3 else "gg_kernel")
     roof["per_launch"] = {"flops": up_flops, "bytes": up_bytes, "ms": in_layer["ffn_up"],
-                          "timed": "average over the timed layer calls, between the layer's own events",
+                          "timed": "average inside K layer calls run right after the timed ones, between "
+                                   "events the layer records around its steps",
                           "ms_back_to_back": stage_ms["ffn_up"]}
     roof["traffic"] = traffic_for(spec.name, os.path.join(ROOT, "routing_dispatch_expert_gate_amd", "csrc",
                                                           "ffn.hip"))
