@@ -31,10 +31,11 @@
 //  * The down GEMM multiplies each output row by its route weight before the
 //    single bf16 rounding, so the combine only sums.
 //  * W8A8: the up epilogue dequantises with the token and channel scales,
-//    writes h in bf16 (the activation dtype of the layer) and folds the
-//    stored values' row max |h| in with an integer atomic max (non-negative
-//    floats order like their bit patterns); a row pass then quantises the
-//    stored h with the per-token rule, and the down GEMM runs int8 MFMA.
+//    writes h in bf16 (the activation dtype of the layer) and stores each
+//    workgroup's max |h| per row over its columns (one plain store per row
+//    and N block, no atomics); a row pass then takes the maximum over the N
+//    blocks, quantises the stored h with the per-token rule, and the down
+//    GEMM runs int8 MFMA.
 //  * W4A16 (LightOP page, section 4.3, INT4 weights with 16-bit
 //    activations): weights are int4 codes, two per byte along K (low nibble
 //    first), with one fp32 scale per output channel.  B tiles are copied to
