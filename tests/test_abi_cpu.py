@@ -292,3 +292,38 @@ def test_capacity_equals_oracle_over_a_grid(moe):
         for T, k, E in loads:
             want = oracle.capacity(T, k, E, f)
             assert L.moe_capacity(T, k, E, f) == want, (T, k, E, f, want)
+
+
+def test_binding_structs_match_the_header(moe, tmp_path):
+    """The ctypes mirrors of the header's structs (moe_layer_aux,
+    moe_layer_options) have the header's size and member offsets, as a C
+    compiler lays them out."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    structs = {"moe_layer_aux": moe.binding.MoeLayerAux, "moe_layer_options": moe.binding.MoeLayerOptions}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} sizeof %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    r = subprocess.run([cc, "-std=c11", f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            cname, what, val = line.split()
+            got[(cname, what)] = int(val)
+    for cname, py in structs.items():
+        assert got[(cname, "sizeof")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
