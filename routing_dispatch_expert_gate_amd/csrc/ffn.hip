@@ -699,23 +699,41 @@ void gg_kernel(const GemmArgs a) {
       }
     }
   } else {
-    uint16_t* y = reinterpret_cast<uint16_t*>(a.out);
+    // y = acc * channel scale * row scale, one bf16 rounding, stored two
+    // columns per 32-bit store as in the up epilogue (rows v and v + 1 of a
+    // fragment packed per lane, swapped with lane l ^ 1, byte-permuted)
+    uint8_t* const ybase = reinterpret_cast<uint8_t*>(a.out) + (int64_t)r0 * a.H * 2;
     float sc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f)
       sc[f] = (I8 || W4) ? a.wscale[(int64_t)e * a.H + nb * BN + wn * WCOLS + f * 32 + (lane & 31)] : 1.f;
+    const bool odd = (lane & 1) != 0;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       if (!fv[fm]) continue;
+      float wr[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WROWS + fm * 32 + acc_row(v, lane);
-        if (row >= rows) continue;
-        const float wr = row_scale[row];
+      for (int v = 0; v < 16; ++v) wr[v] = row_scale[wm * WROWS + fm * 32 + acc_row(v, lane)];
+      // this lane's store row for v = 0 (even lanes) or 1 (odd lanes)
+      const int rl = wm * WROWS + fm * 32 + 4 * (lane >> 5) + (odd ? 1 : 0);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const int col = nb * BN + wn * WCOLS + f * 32 + (lane & 31);
-          y[(int64_t)(r0 + row) * a.H + col] = (uint16_t)f32_to_bf16_bits((float)acc[fm][f][v] * sc[f] * wr);
+      for (int f = 0; f < NF; ++f) {
+        const int colp = (nb * BN + wn * WCOLS + f * 32 + (lane & 31)) & ~1;
+        uint32_t obase = (uint32_t)(rl * a.H + colp);
+        // (kept opaque so the compiler does not fold the row offsets back
+        // into one 32-bit multiply per store)
+        asm volatile("" : "+v"(obase));
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const float y0 = (float)acc[fm][f][v] * sc[f] * wr[v];
+          const float y1 = (float)acc[fm][f][v + 1] * sc[f] * wr[v + 1];
+          const uint32_t mine = pack_bf16x2(y0, y1);
+          const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp((int)mine, (int)mine, 0xB1, 0xF, 0xF, false);
+          const uint32_t pair = __builtin_amdgcn_perm(other, mine, sel);
+          const int dv = 8 * (v >> 2) + (v & 3);   // unrolled: a constant
+          if (rl + dv < rows)
+            *reinterpret_cast<uint32_t*>(ybase + (obase + (uint32_t)(dv * a.H)) * 2u) = pair;
         }
       }
     }
