@@ -945,15 +945,20 @@ constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4,
 // workgroups share a CU: at decode the K loop is latency-bound and more
 // independent workgroups stream faster than one deep pipeline (measured);
 // for BN = 256 three stages and raster groups over all N blocks measured 3-5%
-// faster per layer than two stages in groups of 8.
-constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 3, 128, 4}, {128, 256, 1, 4, 3, 128, 4},
+// faster per layer than two stages in groups of 8.  Prefill and mid tiles
+// take two stages (mid: two workgroups share a CU for W4A8, three for
+// W4A16), except the bf16 prefill down GEMM, which keeps three (measured per
+// layer: fine-grained W4A8 -15%, W4A16 -3.5%; skewed W4A8 -6%; Mixtral W4A16
+// up -1.5%, its down +4% with two).
+constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 2, 128, 4}, {128, 256, 1, 4, 2, 128, 4},
                                 {64, 256, 1, 4, 3, 128, 16}, {256, 128, 2, 2, 3, 128, 8},
                                 {128, 128, 1, 2, 3, 128, 8}, {64, 128, 1, 2, 3, 128, 8}};
-constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {128, 256, 1, 4, 3, 128, 2},
+constexpr Variant kDownVarW4[] = {{256, 256, 2, 4, 3, 128, 2}, {128, 256, 1, 4, 2, 128, 4},
                                   {64, 256, 1, 4, 3, 128, 16}, {256, 128, 2, 2, 3, 128, 8},
                                   {128, 128, 1, 2, 3, 128, 8}, {64, 128, 1, 2, 3, 128, 8},
                                   {256, 64, 2, 2, 3, 128, 8},  {128, 64, 1, 2, 3, 128, 8},
-                                  {64, 64, 1, 2, 3, 128, 8}};
+                                  {64, 64, 1, 2, 3, 128, 8},
+                                  {256, 256, 2, 4, 2, 128, 2}};   // W4A8 prefill (entry 9)
 
 // the up GEMM's N blocks (each writes one partial row maximum per row of h)
 int up_parts(int I, int w_dtype, int up_var) {
@@ -1024,8 +1029,8 @@ hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)a.max_tiles * (unsigned)a.n_blocks;
   if constexpr (UP) {
     switch (var) {
-      MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 4)
-      MOE_GG4_CASE(1, 128, 256, 1, 4, 3, 128, 4)
+      MOE_GG4_CASE(0, 256, 256, 2, 4, 2, 128, 4)
+      MOE_GG4_CASE(1, 128, 256, 1, 4, 2, 128, 4)
       MOE_GG4_CASE(2, 64, 256, 1, 4, 3, 128, 16)
       MOE_GG4_CASE(3, 256, 128, 2, 2, 3, 128, 8)
       MOE_GG4_CASE(4, 128, 128, 1, 2, 3, 128, 8)
@@ -1036,7 +1041,7 @@ hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
   } else {
     switch (var) {
       MOE_GG4_CASE(0, 256, 256, 2, 4, 3, 128, 2)
-      MOE_GG4_CASE(1, 128, 256, 1, 4, 3, 128, 2)
+      MOE_GG4_CASE(1, 128, 256, 1, 4, 2, 128, 4)
       MOE_GG4_CASE(2, 64, 256, 1, 4, 3, 128, 16)
       MOE_GG4_CASE(3, 256, 128, 2, 2, 3, 128, 8)
       MOE_GG4_CASE(4, 128, 128, 1, 2, 3, 128, 8)
@@ -1044,6 +1049,7 @@ hipError_t launch_gg_w4(int var, const GemmArgs& a, hipStream_t s) {
       MOE_GG4_CASE(6, 256, 64, 2, 2, 3, 128, 8)
       MOE_GG4_CASE(7, 128, 64, 1, 2, 3, 128, 8)
       MOE_GG4_CASE(8, 64, 64, 1, 2, 3, 128, 8)
+      MOE_GG4_CASE(9, 256, 256, 2, 4, 2, 128, 2)
       default:
         return hipErrorInvalidValue;
     }
@@ -1152,6 +1158,9 @@ FfnPlan plan_ffn(int64_t T, int H, int I, int E, int k, int w_dtype) {
     p.up_var = (I % 128 == 0 ? 0 : 3) + cls;
     p.down_var = (H % 256 == 0 ? 0 : (H % 128 == 0 ? 3 : 6)) + cls;
     p.block_m = cls == 2 ? 64 : (cls == 1 ? 128 : 256);
+    // the int8 prefill down GEMM measured faster with two stages, the bf16 one
+    // with three
+    if (w_dtype == kI4A8 && p.down_var == 0) p.down_var = 9;
     const Variant u = kUpVarW4[p.up_var], d = kDownVarW4[p.down_var];
     const char* t = w_dtype == kI4 ? "w4a16" : "w4a8";
     snprintf(p.up_name, sizeof p.up_name, "gg_kernel<%s,up,%dx%d,%dx%d,S%d,R%d,G%d>", t, u.bm, u.bn, u.wm,
