@@ -946,8 +946,9 @@ constexpr Variant kDownVar[] = {{256, 256, 4, 4, 2, 128, 2}, {256, 256, 4, 4, 4,
 // independent workgroups stream faster than one deep pipeline (measured);
 // for BN = 256 three stages and raster groups over all N blocks measured 3-5%
 // faster per layer than two stages in groups of 8.  Prefill and mid tiles
-// take two stages (mid: two workgroups share a CU for W4A8, three for
-// W4A16), except the bf16 prefill down GEMM, which keeps three (measured per
+// take two stages (with them two mid workgroups share a CU: the W4A8 one's
+// three stages held a CU alone), except the bf16 prefill down GEMM, which
+// keeps three (measured per
 // layer: fine-grained W4A8 -15%, W4A16 -3.5%; skewed W4A8 -6%; Mixtral W4A16
 // up -1.5%, its down +4% with two).
 constexpr Variant kUpVarW4[] = {{256, 256, 2, 4, 2, 128, 4}, {128, 256, 1, 4, 2, 128, 4},
