@@ -847,28 +847,45 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(
   const float* grow = UP ? wts + ((int64_t)e * 2 * I + n0 + lr) * K : wts + ((int64_t)e * H + n0 + lr) * K;
   const float* urow = UP ? wts + ((int64_t)e * 2 * I + I + n0 + lr) * K : grow;
   float ag[4] = {0, 0, 0, 0}, au[4] = {0, 0, 0, 0};
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const float4 av = lval ? *reinterpret_cast<const float4*>(arow + k0 + lc) : make_float4(0, 0, 0, 0);
-    const float4 gv = *reinterpret_cast<const float4*>(grow + k0 + lc);
-    As[lr][lc] = av.x; As[lr][lc + 1] = av.y; As[lr][lc + 2] = av.z; As[lr][lc + 3] = av.w;
-    Bg[lr][lc] = gv.x; Bg[lr][lc + 1] = gv.y; Bg[lr][lc + 2] = gv.z; Bg[lr][lc + 3] = gv.w;
-    if (UP) {
-      const float4 uv = *reinterpret_cast<const float4*>(urow + k0 + lc);
-      Bu[lr][lc] = uv.x; Bu[lr][lc + 1] = uv.y; Bu[lr][lc + 2] = uv.z; Bu[lr][lc + 3] = uv.w;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float b = Bg[tx][kk];
-      const float bu = UP ? Bu[tx][kk] : 0.f;
+  // P chunks of 32 K values in flight in registers: the chunk loads are
+  // latency-bound at these sizes, so each chunk is loaded P chunks ahead of
+  // its use (slot j of the ring is chunk c0 + j, a compile-time index)
+  constexpr int P = 4;
+  const int nk = K / 32;
+  float4 ra[P], rg[P], ru[P];
+  auto load = [&](int c, float4& va, float4& vg, float4& vu) {
+    va = lval ? *reinterpret_cast<const float4*>(arow + c * 32 + lc) : make_float4(0, 0, 0, 0);
+    vg = *reinterpret_cast<const float4*>(grow + c * 32 + lc);
+    if (UP) vu = *reinterpret_cast<const float4*>(urow + c * 32 + lc);
+  };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float av2 = As[ty * 4 + i][kk];
-        ag[i] = fmaf(av2, b, ag[i]);
-        if (UP) au[i] = fmaf(av2, bu, au[i]);
+  for (int j = 0; j < P; ++j)
+    if (j < nk) load(j, ra[j], rg[j], ru[j]);
+  for (int c0 = 0; c0 < nk; c0 += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int c = c0 + j;
+      if (c >= nk) break;
+      As[lr][lc] = ra[j].x; As[lr][lc + 1] = ra[j].y; As[lr][lc + 2] = ra[j].z; As[lr][lc + 3] = ra[j].w;
+      Bg[lr][lc] = rg[j].x; Bg[lr][lc + 1] = rg[j].y; Bg[lr][lc + 2] = rg[j].z; Bg[lr][lc + 3] = rg[j].w;
+      if (UP) {
+        Bu[lr][lc] = ru[j].x; Bu[lr][lc + 1] = ru[j].y; Bu[lr][lc + 2] = ru[j].z; Bu[lr][lc + 3] = ru[j].w;
       }
+      if (c + P < nk) load(c + P, ra[j], rg[j], ru[j]);
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < 32; ++kk) {
+        const float b = Bg[tx][kk];
+        const float bu = UP ? Bu[tx][kk] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float av2 = As[ty * 4 + i][kk];
+          ag[i] = fmaf(av2, b, ag[i]);
+          if (UP) au[i] = fmaf(av2, bu, au[i]);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
