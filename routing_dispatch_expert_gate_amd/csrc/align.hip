@@ -257,32 +257,38 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
 // kept counts into offsets; block 0 also writes counts, offsets, the tile
 // list and num_dropped.  Integer sums are exact in any order, so every
 // output is deterministic, and equal to the three-launch path's.
-// (E <= 64)
+// (E <= kMaxE = the block's 256 threads)
 __global__ __launch_bounds__(kAlignThreads) void align_route_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int ebits, const int32_t* __restrict__ whist, int64_t ng,
     int G, int spg, int64_t cap, int bm, int64_t max_tiles, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot, int32_t* __restrict__ pos,
     int32_t* __restrict__ tiles, int32_t* __restrict__ num_tiles, int32_t* __restrict__ num_dropped) {
+  static_assert(kMaxE <= kAlignThreads, "one thread per expert");
   __shared__ int32_t wh[4 * kMaxE];
   __shared__ int32_t pb[kAlignThreads], pt[kAlignThreads];   // per-thread partial base / total
-  __shared__ int32_t bb[kMaxE], off_s[kMaxE + 1], tb_s[kMaxE], tot_s[2];
-  const int tid = threadIdx.x;
+  __shared__ int32_t bb[kMaxE], off_s[kMaxE], wsum[8];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < 4 * kMaxE; i += kAlignThreads) wh[i] = 0;
   const int64_t g0 = (int64_t)blockIdx.x * G;
   const int64_t s0 = g0 * spg;
   const int64_t s1 = s0 + (int64_t)G * spg < n ? s0 + (int64_t)G * spg : n;
   WaveIds q = load_wave_ids(ids, s0, s1);   // in flight while the counts are summed
-  // thread (r, e), r < R = 256 / E: route workgroups g = r, r + R, ...
+  // thread (r, e), r < R = 256 / E: route workgroups g = r, r + R, ...,
+  // eight independent loads per step
   const int R = kAlignThreads / E;
   int sb = 0, st = 0;
   if (tid < R * E) {
     const int e = tid % E, r = tid / E;
     int64_t g = r;
-    for (; g + 3 * R < ng; g += 4 * R) {
-      const int a0 = whist[g * E + e], a1 = whist[(g + R) * E + e], a2 = whist[(g + 2 * R) * E + e],
-                a3 = whist[(g + 3 * R) * E + e];
-      st += (a0 + a1) + (a2 + a3);
-      sb += (g < g0 ? a0 : 0) + (g + R < g0 ? a1 : 0) + (g + 2 * R < g0 ? a2 : 0) + (g + 3 * R < g0 ? a3 : 0);
+    for (; g + 7 * R < ng; g += 8 * R) {
+      int a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = whist[(g + u * R) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        st += a[u];
+        sb += g + u * R < g0 ? a[u] : 0;
+      }
     }
     for (; g < ng; g += R) {
       const int a = whist[g * E + e];
@@ -293,53 +299,54 @@ __global__ __launch_bounds__(kAlignThreads) void align_route_kernel(
   pb[tid] = sb;
   pt[tid] = st;
   __syncthreads();
-  // wave 0 (E <= 64: lane e): totals, capacity, and the scans over experts
-  // of kept rows and row tiles (DPP wave scans); block 0 writes them out
-  if (tid < 64) {
-    int total = 0, b = 0;
-    if (tid < E)
-      for (int r = 0; r < R; ++r) {
-        b += pb[r * E + tid];
-        total += pt[r * E + tid];
-      }
-    const int kept = tid < E ? (cap > 0 && total > cap ? (int)cap : total) : 0;
-    const int ntile = (kept + bm - 1) / bm;
-    const int ik = wave_incl_scan(kept), it = wave_incl_scan(ntile);
-    const int off = ik - kept;
+  // thread e < E: its expert's base and total over the R partial sums, the
+  // capacity, and the scans over experts of kept rows and row tiles (DPP
+  // wave scans, then the four wave totals through LDS)
+  int total = 0, b = 0;
+  if (tid < E)
+    for (int r = 0; r < R; ++r) {
+      b += pb[r * E + tid];
+      total += pt[r * E + tid];
+    }
+  const int kept = tid < E ? (cap > 0 && total > cap ? (int)cap : total) : 0;
+  const int ntile = (kept + bm - 1) / bm;
+  const int ik = wave_incl_scan(kept), it = wave_incl_scan(ntile);
+  if (lane == 63) {
+    wsum[wv] = ik;
+    wsum[4 + wv] = it;
+  }
+  __syncthreads();
+  int pk = 0, ptl = 0, n_kept = 0, n_tiles = 0;
+#pragma unroll
+  for (int w = 0; w < kAlignThreads / 64; ++w) {
+    pk += w < wv ? wsum[w] : 0;
+    ptl += w < wv ? wsum[4 + w] : 0;
+    n_kept += wsum[w];
+    n_tiles += wsum[4 + w];
+  }
+  const int off = pk + ik - kept, tbase = ptl + it - ntile;
+  if (tid < E) {
+    bb[tid] = b;
+    off_s[tid] = off;
+  }
+  if (blockIdx.x == 0) {
     if (tid < E) {
-      bb[tid] = b;
-      off_s[tid] = off;
-      tb_s[tid] = it - ntile;
-    }
-    if (tid == 63) {
-      off_s[E] = ik;
-      tot_s[0] = ik;
-      tot_s[1] = it;
-    }
-    if (blockIdx.x == 0 && tid < E) {
       counts[tid] = total;
       offsets[tid] = off;
     }
-  }
-  __syncthreads();
-  const int n_kept = tot_s[0], n_tiles = tot_s[1];
-  if (blockIdx.x == 0) {
     if (tid == 0) {
       offsets[E] = n_kept;
       *num_dropped = (int32_t)(n - n_kept);
       *num_tiles = n_tiles;
     }
-    if (tid < E) {
-      const int kept = (tid + 1 < E ? off_s[tid + 1] : n_kept) - off_s[tid];
-      const int ntile = (kept + bm - 1) / bm;
-      for (int i = 0; i < ntile; ++i) {
-        const int rows = kept - i * bm < bm ? kept - i * bm : bm;
-        *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tb_s[tid] + i)) = make_int4(tid, off_s[tid] + i * bm, rows, 0);
-      }
+    for (int i = 0; i < ntile; ++i) {
+      const int rows = kept - i * bm < bm ? kept - i * bm : bm;
+      *reinterpret_cast<int4*>(tiles + 4 * (size_t)(tbase + i)) = make_int4(tid, off + i * bm, rows, 0);
     }
     for (int64_t i = n_tiles + tid; i < max_tiles; i += kAlignThreads)
       *reinterpret_cast<int4*>(tiles + 4 * i) = make_int4(-1, 0, 0, 0);
   }
+  __syncthreads();
   scatter_block(ids, n, E, ebits, s0, s1, q, [&](int e) { return bb[e]; }, [&](int e) { return off_s[e]; },
                 (int64_t)n_kept, cap, sorted_slot, pos, wh);
 }

@@ -186,9 +186,9 @@ LayerCarve carve_layer(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
   c.y = take(n * (size_t)H * (w_dtype == MOE_F32 ? 4 : 2));
   size_t scratch = c.rp.ws_bytes > rp2.ws_bytes ? c.rp.ws_bytes : rp2.ws_bytes;
   if (c.ap.ws_bytes > scratch) scratch = c.ap.ws_bytes;
-  // the route step's per-workgroup counts, read by the align step (route
-  // kinds that publish them use no other route or align workspace)
-  const size_t whist = (size_t)moe::route_hist_groups(c.rp, T, k) * (size_t)E * 4;
+  // the route step's per-workgroup counts, read by the align step (after
+  // the route step's own workspace, which the align step does not use)
+  const size_t whist = moe::route_hist_bytes(c.rp, T, k, E);
   if (whist > scratch) scratch = whist;
   if (c.fp.ws_bytes > scratch) scratch = c.fp.ws_bytes;
   c.scratch = take(scratch);
@@ -383,7 +383,7 @@ size_t moe_route_align_workspace_size(int64_t T, int32_t H, int32_t E, int32_t k
   for (int xd = MOE_F32; xd <= MOE_BF16; ++xd)
     for (int wd = MOE_F32; wd <= MOE_BF16; ++wd) {
       const moe::RoutePlan p = moe::plan_route(T, H, E, k, xd, wd);
-      const size_t h = (size_t)moe::route_hist_groups(p, T, k) * (size_t)(E > 0 ? E : 0) * 4;
+      const size_t h = E > 0 ? moe::route_hist_bytes(p, T, k, E) : 0;
       if (p.kind >= 0 && h > need) need = h;
     }
   return need;
@@ -425,11 +425,12 @@ moe_status moe_route_align(const void* x, int32_t x_dtype, const void* wg, int32
   if (moe::route_publishes_hist(plan, T, k)) {
     // the route step publishes each workgroup's counts; one align launch
     // takes them (the layer's path for these route kinds)
-    int32_t* whist = (int32_t*)workspace;
+    int32_t* whist = (int32_t*)((uint8_t*)workspace + moe::route_hist_offset(plan));
     e = moe::launch_route(plan, x, x_dtype, wg, wg_dtype, bias, T, H, E, k, topk_ids, topk_w, topk_p, xq, xs,
                           workspace, s, whist);
     if (e != hipSuccess) return hip_fail(e, "moe_route_align route launch");
-    e = moe::launch_align_from_route(topk_ids, whist, moe::route_hist_groups(plan, T, k), plan.bt, T, k, E, cap, block_m,
+    e = moe::launch_align_from_route(topk_ids, whist, moe::route_hist_groups(plan, T, k),
+                                     moe::route_hist_tokens(plan, k), T, k, E, cap, block_m,
                                      mt, counts, offsets, sorted_slot, pos, tiles, num_tiles, num_dropped, s);
     if (e != hipSuccess) return hip_fail(e, "moe_route_align align launch");
     return ok(route_name(plan) + " | align(from route counts, one launch)");
@@ -799,10 +800,10 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
     if (e != hipSuccess) return hip_fail(e, "moe_layer route+align launch");
     if ((e = mark(1)) != hipSuccess || (e = mark(2)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
   } else {
-    // route kinds that publish per-workgroup counts (E <= 64) let one align
-    // launch take them instead of histogramming the ids again
+    // a route step that publishes per-workgroup counts lets one align launch
+    // take them instead of histogramming the ids again
     const bool from_route = !grouped && moe::route_publishes_hist(c.rp, T, k);
-    int32_t* whist = from_route ? (int32_t*)scratch : nullptr;
+    int32_t* whist = from_route ? (int32_t*)((uint8_t*)scratch + moe::route_hist_offset(c.rp)) : nullptr;
     if (grouped)
       e = moe::launch_route_grouped(c.rp, x, wg, bias, T, H, E, k, o.n_group, o.topk_group, ids, w, p, xq, xs,
                                     scratch, s);
@@ -811,7 +812,7 @@ moe_status layer_impl(const void* x, int32_t x_dtype, const void* wg, int32_t wg
     if (e != hipSuccess) return hip_fail(e, "moe_layer route launch");
     if ((e = mark(1)) != hipSuccess) return hip_fail(e, "moe_layer stage event");
     if (from_route)
-      e = moe::launch_align_from_route(ids, whist, moe::route_hist_groups(c.rp, T, k), c.rp.bt, T, k, E,
+      e = moe::launch_align_from_route(ids, whist, moe::route_hist_groups(c.rp, T, k), moe::route_hist_tokens(c.rp, k), T, k, E,
                                        capacity > 0 ? capacity : 0, c.fp.block_m, c.fp.max_tiles, counts, offsets,
                                        sorted_slot, pos, tiles, num_tiles, num_dropped, s);
     else

@@ -213,18 +213,25 @@ struct RoutePlan {
 };
 // fused_ok = false: never kind 3 (the group-limited router runs on kind 2)
 RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, bool fused_ok = true);
-// whist (may be NULL): where route kinds 0 and 3 publish each workgroup's
+// whist (may be NULL): where the route step publishes each workgroup's
 // per-expert selection counts, [route_hist_groups(p, T)][E] int32, for
-// launch_align_from_route; other kinds ignore it
+// launch_align_from_route (kinds 0 and 3: the route workgroups; kind 2: its
+// top-k workgroups).  Kind 2 also uses ws for its partial logits, so whist
+// must start at ws + route_hist_offset(p) there.
 hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const void* wg, int wg_dtype,
                         const float* bias, int64_t T, int H, int E, int k, int32_t* ids, float* w,
                         float* prob, int8_t* xq, float* xs, void* ws, hipStream_t s, int32_t* whist = nullptr);
-// whether the route step publishes per-workgroup counts for this batch (route
-// kinds 0 and 3, at least kAlignFromRouteSlots slots)
+// whether the route step publishes per-workgroup counts for this batch (at
+// least kAlignFromRouteSlots slots)
 constexpr int64_t kAlignFromRouteSlots = 4096;
 bool route_publishes_hist(const RoutePlan& p, int64_t T, int k);
-// route workgroups (each over tokens [g bt, (g + 1) bt)) that publish counts
+// tokens per publishing workgroup (tg), the number of such workgroups (each
+// over tokens [g tg, (g + 1) tg)), where whist starts in the route workspace,
+// and the route workspace bytes including whist (0 when nothing is published)
+int route_hist_tokens(const RoutePlan& p, int k);
 int64_t route_hist_groups(const RoutePlan& p, int64_t T, int k);
+size_t route_hist_offset(const RoutePlan& p);
+size_t route_hist_bytes(const RoutePlan& p, int64_t T, int k, int E);
 // route and align in one launch where one workgroup can take every token
 // (route_align_fusable): the align outputs as in launch_align
 bool route_align_fusable(const RoutePlan& p, int64_t T, int k);

@@ -43,7 +43,7 @@ constexpr int kBF16 = 1;
 // token's largest logit and s its softmax denominator (used only for prob).
 __device__ void wave_topk_select_store(float v[4], int k, float m, float s, int64_t t,
                                        int32_t* __restrict__ ids, float* __restrict__ w,
-                                       float* __restrict__ prob) {
+                                       float* __restrict__ prob, int* hist = nullptr) {
   const int lane = threadIdx.x & 63;
   int my_id = 0;
   float my_l = -INFINITY;
@@ -72,6 +72,7 @@ __device__ void wave_topk_select_store(float v[4], int k, float m, float s, int6
     ids[t * k + lane] = my_id;
     w[t * k + lane] = ex / se;
     if (prob) prob[t * k + lane] = ex / s;
+    if (hist) atomicAdd(&hist[my_id], 1);   // counts only: their order is irrelevant
   }
 }
 
@@ -116,10 +117,10 @@ __device__ __forceinline__ float wave_softmax_denominator(const float v[4], int 
 }
 
 __device__ void wave_topk_store(float v[4], int E, int k, int64_t t, int32_t* __restrict__ ids,
-                                float* __restrict__ w, float* __restrict__ prob) {
+                                float* __restrict__ w, float* __restrict__ prob, int* hist = nullptr) {
   const float m = wave_logit_max(v);
   const float s = prob ? wave_softmax_denominator(v, E, m) : 0.f;
-  wave_topk_select_store(v, k, m, s, t, ids, w, prob);
+  wave_topk_select_store(v, k, m, s, t, ids, w, prob, hist);
 }
 
 // Group-limited top-k of one token (LightOP page, section 3.1, Moe Fuse Gate:
@@ -521,6 +522,12 @@ __global__ __launch_bounds__(WIDE ? 1024 : 512) void route_fma_kernel(
 // workgroup then reads half the bytes per output of a 64 x 64 tile, which is
 // what bounds the step (each CU's copy rate), for more partial logits.
 constexpr int kRT = 64;                        // tokens per tile (small batches)
+constexpr int kTopkHistTokens = 16;            // tokens per top-k workgroup that publishes counts
+// top-k workgroups per published count row: about 1024 slots, one align block
+inline int topk_hist_group(int k) {
+  const int g = 1024 / (kTopkHistTokens * k);
+  return g < 1 ? 1 : g;
+}
 constexpr int kRE = 64;                        // experts per tile (small batches)
 constexpr int kRRow = 128;                     // bytes of K per stage row
 constexpr int kRLds = 128 * 1024;              // bytes of stages
@@ -536,8 +543,15 @@ __global__ __launch_bounds__(WM* WN * 64) void route_gemm_kernel(const uint16_t*
                                                                 const uint16_t* __restrict__ wg, int64_t T,
                                                                 int H, int E, int kchunk,
                                                                 float* __restrict__ part,
-                                                                float* __restrict__ amax_part) {
+                                                                float* __restrict__ amax_part,
+                                                                int32_t* __restrict__ zero, int nzero) {
   constexpr int NW = WM * WN, NT = NW * 64;
+  // the top-k step's count rows, cleared here for its atomic adds
+  if (zero) {
+    const int64_t nthr = (int64_t)gridDim.x * gridDim.y * gridDim.z * NT;
+    const int64_t me = (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * NT + threadIdx.x;
+    for (int64_t i = me; i < nzero; i += nthr) zero[i] = 0;
+  }
   constexpr int STAGE = (RT + RE) * kRRow;
   constexpr int RS = kRLds / STAGE;              // stages
   constexpr int RL = STAGE / 1024 / NW;          // 1 KiB copies per wave per stage
@@ -680,7 +694,8 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
                            const float* __restrict__ bias, int64_t T, int E, int k, int H,
                            const uint16_t* __restrict__ x, int32_t* __restrict__ ids, float* __restrict__ w,
                            float* __restrict__ prob, int8_t* __restrict__ xq, float* __restrict__ xs,
-                           int n_group, int topk_group, float* lrow, float* grow, float* gscore) {
+                           int n_group, int topk_group, float* lrow, float* grow, float* gscore,
+                           int* hist = nullptr) {
   const int lane = threadIdx.x & 63;
   // W8A8, XPF > 0 (small batches, latency-bound): the token's x row (its
   // first XPF*512 values) and its per-split absmax are fetched before the
@@ -746,9 +761,9 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
   } else if (E <= 64) {
     lrow[lane] = v[0];
     __builtin_amdgcn_wave_barrier();
-    wave_topk_rank_store(lrow, E, k, t, ids, w, prob);
+    wave_topk_rank_store(lrow, E, k, t, ids, w, prob, hist);
   } else {
-    wave_topk_store(v, E, k, t, ids, w, prob);
+    wave_topk_store(v, E, k, t, ids, w, prob, hist);
   }
   if constexpr (QUANT) {
     if constexpr (QPF == 0) {
@@ -794,21 +809,43 @@ __device__ __forceinline__ void topk_token(int64_t t, const float* __restrict__ 
 // LAT: a batch small enough that the kernel is one dependent chain per token
 // (at most 256 workgroups): fetch all split partials at once and the x row
 // before the selection; otherwise keep registers for occupancy.
-template <bool QUANT, bool GROUPED, bool LAT>
-__global__ __launch_bounds__(256) void route_topk_kernel(
+// One wave per token, NWV tokens per workgroup.  With whist (NWV = 16 only),
+// the workgroup counts its selections per expert in LDS and adds the nonzero
+// counts to row blockIdx / hg of whist (integer atomics: the sums are exact
+// in any order), so each row holds the counts of hg consecutive workgroups,
+// about 1024 slots, the align step's block ([FA-MoE] fusion one: the gate's
+// tail does the histogram).  The logits kernel cleared the rows.
+template <bool QUANT, bool GROUPED, bool LAT, int NWV>
+__global__ __launch_bounds__(NWV * 64) void route_topk_kernel(
     const float* __restrict__ part, const float* __restrict__ amax_part, int ks,
     const float* __restrict__ bias, int64_t T, int E, int k, int H, const uint16_t* __restrict__ x,
     int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob, int8_t* __restrict__ xq,
-    float* __restrict__ xs, int n_group, int topk_group) {
-  __shared__ __attribute__((aligned(16))) float lrow[4][64];
-  __shared__ __attribute__((aligned(16))) float grow[GROUPED ? 4 : 1][256];
-  __shared__ float gscore[GROUPED ? 4 : 1][64];
+    float* __restrict__ xs, int n_group, int topk_group, int32_t* __restrict__ whist, int hg) {
+  static_assert(!GROUPED || NWV == 4, "the group-limited top-k publishes no counts");
+  constexpr bool HIST = NWV > 4;
+  __shared__ __attribute__((aligned(16))) float lrow[NWV][64];
+  __shared__ __attribute__((aligned(16))) float grow[GROUPED ? NWV : 1][256];
+  __shared__ float gscore[GROUPED ? NWV : 1][64];
+  __shared__ int hist[HIST ? kMaxE : 1];
   const int wv = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wv;
-  if (t >= T) return;
-  topk_token<QUANT, GROUPED, LAT ? 8 : 0, LAT ? 16 : 8>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob,
-                                                         xq, xs, n_group, topk_group, lrow[wv],
-                                                         grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0]);
+  const int64_t t = (int64_t)blockIdx.x * NWV + wv;
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < E; i += NWV * 64) hist[i] = 0;
+    __syncthreads();
+  } else {
+    if (t >= T) return;
+  }
+  if (t < T)
+    topk_token<QUANT, GROUPED, LAT ? 8 : 0, LAT ? 16 : 8>(t, part, amax_part, ks, bias, T, E, k, H, x, ids, w, prob,
+                                                           xq, xs, n_group, topk_group, lrow[wv],
+                                                           grow[GROUPED ? wv : 0], gscore[GROUPED ? wv : 0],
+                                                           HIST ? hist : nullptr);
+  if constexpr (HIST) {
+    __syncthreads();
+    int32_t* row = whist + (int64_t)(blockIdx.x / hg) * E;
+    for (int i = threadIdx.x; i < E; i += NWV * 64)
+      if (hist[i] != 0) atomicAdd(&row[i], hist[i]);
+  }
 }
 
 // ------------------------------------------------------------ kind 3 -----
@@ -1127,19 +1164,23 @@ template <bool GROUPED>
 hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const float* bias,
                        int64_t T, int H, int E, int k, int32_t* ids, float* w, float* prob,
                        int8_t* xq, float* xs, void* ws, int n_group, int topk_group, const AlignArgs* al,
-                       hipStream_t s) {
+                       hipStream_t s, int32_t* whist = nullptr) {
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* wb = (const uint16_t*)wg;
   float* part = (float*)ws;
   float* amax_part = (float*)((uint8_t*)ws + route_part_bytes(T, E, p.ks));
   const dim3 grid((unsigned)((T + p.bt - 1) / p.bt), (unsigned)((E + p.be - 1) / p.be), (unsigned)p.ks);
+  // with whist: the top-k workgroups add their counts into rows of
+  // topk_hist_group(k) workgroups each, which the logits kernel clears
+  const int hg = topk_hist_group(k);
+  const int nzero = whist ? (int)(((T + kTopkHistTokens - 1) / kTopkHistTokens + hg - 1) / hg) * E : 0;
 #define MOE_RG(RT, RE, WM, WN)                                                                                 \
   if (xq)                                                                                                      \
     route_gemm_kernel<true, RT, RE, WM, WN><<<grid, WM * WN * 64, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part,  \
-                                                                           amax_part);                          \
+                                                                           amax_part, whist, nzero);            \
   else                                                                                                         \
     route_gemm_kernel<false, RT, RE, WM, WN><<<grid, WM * WN * 64, 0, s>>>(xb, wb, T, H, E, 2 * H / p.ks, part, \
-                                                                            amax_part);
+                                                                            amax_part, whist, nzero);
   if (p.bt == 128 && p.nw == 16) {
     MOE_RG(128, 128, 4, 4)
   } else if (p.bt == 128 && p.nw == 8) {
@@ -1161,11 +1202,29 @@ hipError_t launch_mfma(const RoutePlan& p, const void* x, const void* wg, const 
                                                                  w, prob, xq, xs, n_group, topk_group, *al);
     return hipGetLastError();
   }
-  const dim3 g2((unsigned)((T + 3) / 4));
-#define MOE_TOPK(Q, LAT)                                                                                      \
-  route_topk_kernel<Q, GROUPED, LAT><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, \
-                                                        xq, xs, n_group, topk_group)
   const bool lat = T <= 4 * 256;
+  if constexpr (!GROUPED) {
+    if (whist) {
+      const dim3 g16((unsigned)((T + kTopkHistTokens - 1) / kTopkHistTokens));
+#define MOE_TOPKH(Q, LAT)                                                                                       \
+  route_topk_kernel<Q, false, LAT, kTopkHistTokens><<<g16, kTopkHistTokens * 64, 0, s>>>(                       \
+      part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, xq, xs, n_group, topk_group, whist, hg)
+      // (with codes the latency form needs more than the 128 VGPRs a wave of
+      // a 16-wave workgroup can hold, so it takes the other)
+      if (xq)
+        MOE_TOPKH(true, false);
+      else if (lat)
+        MOE_TOPKH(false, true);
+      else
+        MOE_TOPKH(false, false);
+#undef MOE_TOPKH
+      return hipGetLastError();
+    }
+  }
+  const dim3 g2((unsigned)((T + 3) / 4));
+#define MOE_TOPK(Q, LAT)                                                                                         \
+  route_topk_kernel<Q, GROUPED, LAT, 4><<<g2, 256, 0, s>>>(part, amax_part, p.ks, bias, T, E, k, H, xb, ids, w, prob, \
+                                                           xq, xs, n_group, topk_group, nullptr, 1)
   if (xq && lat)
     MOE_TOPK(true, true);
   else if (xq)
@@ -1269,7 +1328,7 @@ hipError_t route_any(const RoutePlan& p, const void* x, int x_dtype, const void*
     MOE_FMA_DT(16, false);
 #undef MOE_FMA_DT
   }
-  return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, al, s);
+  return launch_mfma<false>(p, x, wg, bias, T, H, E, k, ids, w, prob, xq, xs, ws, 1, 1, al, s, whist);
 }
 }  // namespace
 
@@ -1284,12 +1343,24 @@ hipError_t launch_route(const RoutePlan& p, const void* x, int x_dtype, const vo
 // (small batches keep the one-workgroup align, whose single wave is faster
 // than a workgroup summing the counts: 4.0 vs 5.3 us at 128 slots)
 bool route_publishes_hist(const RoutePlan& p, int64_t T, int k) {
-  return (p.kind == 0 || p.kind == 3) && T * k >= kAlignFromRouteSlots;
+  return (p.kind == 0 || p.kind == 2 || p.kind == 3) && T * k >= kAlignFromRouteSlots;
+}
+
+int route_hist_tokens(const RoutePlan& p, int k) {
+  return p.kind == 2 ? kTopkHistTokens * topk_hist_group(k) : p.bt;
 }
 
 int64_t route_hist_groups(const RoutePlan& p, int64_t T, int k) {
   if (!route_publishes_hist(p, T, k) || T <= 0) return 0;
-  return (T + p.bt - 1) / p.bt;
+  const int tg = route_hist_tokens(p, k);
+  return (T + tg - 1) / tg;
+}
+
+size_t route_hist_offset(const RoutePlan& p) { return (p.ws_bytes + 255) & ~(size_t)255; }
+
+size_t route_hist_bytes(const RoutePlan& p, int64_t T, int k, int E) {
+  const int64_t ng = route_hist_groups(p, T, k);
+  return ng > 0 ? route_hist_offset(p) + (size_t)ng * (size_t)E * 4 : 0;
 }
 
 bool route_align_fusable(const RoutePlan& p, int64_t T, int k) {

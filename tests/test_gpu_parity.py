@@ -299,6 +299,12 @@ ROUTE_ALIGN = [
     # counts and one align launch takes them (fused E <= 64 router, FMA router)
     (moe_synth.Spec("ra_e64_T8300_cap", 8300, 256, 64, 6, 64, zipf_s=1.1), 700, 128, True, False),
     (moe_synth.Spec("ra_e16_T20011_cap", 20011, 128, 16, 4, 64, zipf_s=1.1), 4000, 256, False, False),
+    # E > 64 (MFMA logits + top-k): the top-k workgroups publish the counts;
+    # T not a multiple of their 16 tokens, E = 80 (three count sums per
+    # expert per align thread), codes with the small-batch top-k
+    (moe_synth.Spec("ra_e256_T4100_cap", 4100, 256, 256, 8, 64, zipf_s=1.1), 150, 128, False, False),
+    (moe_synth.Spec("ra_e128_T700_q", 700, 512, 128, 6, 64), 0, 64, True, False),
+    (moe_synth.Spec("ra_e80_T1000_cap", 1000, 256, 80, 6, 64, zipf_s=1.1), 60, 32, False, False),
 ]
 
 
@@ -315,6 +321,9 @@ def test_route_align_equals_route_then_align(spec, C, bm, quant, fused):
     d = moe.last_dispatch()
     print(d)
     assert ("(one launch)" in d) == fused, d
+    # batches of at least 4096 slots take the align step from the route
+    # step's published counts
+    assert ("from route counts" in d) == (not fused and spec.T * spec.k >= 4096), d
     r = moe.route(x, wg, spec.k, bias=b, want_p=True, quant=quant)
     a = moe.align(r["ids"], spec.E, C, bm)
     torch.cuda.synchronize()
@@ -505,12 +514,15 @@ SMALL = [
     moe_synth.Spec("i4a8_mid_H384_cap1", 300, 384, 8, 2, 256, w_dtype="i4a8", capacity_factor=1.0, zipf_s=1.1),
     moe_synth.Spec("i4a8_decode_E64", 16, 512, 64, 6, 256, w_dtype="i4a8"),
     moe_synth.Spec("i4a8_decode_H384", 8, 384, 32, 4, 128, w_dtype="i4a8"),
-    # large batches whose route step publishes per-workgroup counts (E <= 64)
+    # large batches whose route step publishes per-workgroup counts
     # and whose align step is one launch over them, with capacity drops
     moe_synth.Spec("align_from_route_e64_cap", 8300, 256, 64, 6, 128, capacity_factor=1.0, zipf_s=1.1),
     moe_synth.Spec("align_from_route_e32_i8_cap", 9001, 128, 32, 3, 128, w_dtype="i8", capacity_factor=1.25,
                    zipf_s=1.1),
     moe_synth.Spec("align_from_route_e16_fma_cap", 20011, 128, 16, 4, 64, capacity_factor=1.25, zipf_s=1.1),
+    # E > 64: counts from the top-k workgroups of the MFMA router
+    moe_synth.Spec("align_from_route_e256_cap", 4100, 256, 256, 8, 128, capacity_factor=1.25, zipf_s=1.1),
+    moe_synth.Spec("align_from_route_e128_i8", 700, 256, 128, 6, 128, w_dtype="i8"),
 ]
 
 
