@@ -851,8 +851,8 @@ __global__ __launch_bounds__(NWV * 64) void route_topk_kernel(
 // ------------------------------------------------------------ kind 3 -----
 // E <= 64, bf16: gate, softmax and top-k (and, with quantisation, the int8
 // codes) in one kernel, with the logits on chip and x read from memory once.
-// A workgroup of 16 waves takes BM = 256 / KQ tokens and every expert over
-// all of H.  Wave (tb, q) owns tokens [16 tb, 16 tb + 16) of the block and
+// A workgroup of NW waves (16, or 8 so that two share a CU) takes
+// BM = 16 NW / KQ tokens and every expert over all of H.  Wave (tb, q) owns tokens [16 tb, 16 tb + 16) of the block and
 // the q-th of KQ contiguous parts of H.  It loads its whole x slice straight
 // into registers, all loads issued at once, laid out as the A operand of MFMA
 // 16x16x32 bf16 (row = lane % 16, eight K values at 8 (lane / 16) of each
@@ -891,23 +891,23 @@ inline int fused_parts(int H) {
   return 0;
 }
 
-template <bool QUANT, int KQ, int NSUB>
-__global__ __launch_bounds__(1024) void route_fused_kernel(
+template <bool QUANT, int KQ, int NSUB, int NW, int LDSB>
+__global__ __launch_bounds__(NW * 64) void route_fused_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, const float* __restrict__ bias, int64_t T,
     int H, int E, int k, int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ prob,
     int8_t* __restrict__ xq, float* __restrict__ xs, int32_t* __restrict__ whist) {
-  constexpr int BM = 256 / KQ;                     // tokens per workgroup
+  constexpr int BM = 16 * NW / KQ;                 // tokens per workgroup
   constexpr int RB = KQ >= 8 ? 64 : 128;           // stage row bytes
   constexpr int SPS = RB / 64;                     // substeps per stage
   constexpr int NST = NSUB / SPS;                  // stages per K loop
   constexpr int BROWS = kFE * KQ;                  // stage rows: (part, expert)
   constexpr int STAGE = BROWS * RB;
-  constexpr int SMAX = 128 * 1024 / STAGE;
+  constexpr int SMAX = LDSB / STAGE;
   // short loops issue every stage before the first wait
   constexpr int S = NST + 1 < SMAX ? (NST + 1 < 2 ? 2 : NST + 1) : SMAX;
-  constexpr int L = STAGE / 1024 / 16;             // 1 KiB copies per wave per stage
+  constexpr int L = STAGE / 1024 / NW;             // 1 KiB copies per wave per stage
   constexpr int CPR = RB / 16, RPB = 1024 / RB;
-  static_assert(L >= 1 && L * 16 * 1024 == STAGE, "copies split evenly over the 16 waves");
+  static_assert(L >= 1 && L * NW * 1024 == STAGE, "copies split evenly over the waves");
   static_assert(NST * SPS == NSUB && S >= 2, "stages");
   // One LDS allocation (with a second LDS object the compiler can no longer
   // tell the stage reads from the in-flight copies and drains every copy
@@ -1062,7 +1062,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(
   __syncthreads();
   // logits = the parts summed in order, plus the bias, in place over the
   // first part's plane (each thread reads and writes its own entries)
-  for (int i = tid; i < BM * kFE; i += 1024) {
+  for (int i = tid; i < BM * kFE; i += NW * 64) {
     const int e = i % kFE;
     float v = 0.f;
 #pragma unroll
@@ -1071,7 +1071,7 @@ __global__ __launch_bounds__(1024) void route_fused_kernel(
   }
   __syncthreads();
   const int ntok = (int)(T - t0 < BM ? T - t0 : BM);
-  for (int t = wv; t < ntok; t += 16)
+  for (int t = wv; t < ntok; t += NW)
     wave_topk64_store(pl[t * kFE + lane], E, k, t0 + t, ids, w, prob, whist ? hist : nullptr);
   if (whist) {
     // publish the workgroup's per-expert selection counts for the align step
@@ -1257,7 +1257,13 @@ RoutePlan plan_route(int64_t T, int H, int E, int k, int x_dtype, int wg_dtype, 
   const int kq = E <= kFE ? fused_parts(H) : 0;
   if (fused_ok && kq > 0 && (T + 256 / kq - 1) / (256 / kq) >= 64) {
     p.kind = 3;
-    p.bt = 256 / kq;
+    // 8 waves (two workgroups per CU, so one's x stream overlaps the
+    // other's top-k) for parts of H up to a quarter; measured, T = 16384,
+    // H = 2048, E = 64: 26.0 -> 25.0 us, with codes 43.1 -> 40.0 us; T = 4096,
+    // H = 2048, E = 32: 19.7 -> 14.1 us; at eight parts (H = 4096) 16 waves
+    // stay (28.8 against 31.1 us)
+    p.nw = kq <= 4 ? 8 : 16;
+    p.bt = 16 * p.nw / kq;
     p.be = kFE;
     p.ks = kq;
     return p;
@@ -1290,12 +1296,23 @@ hipError_t launch_fused_n(const RoutePlan& p, const void* x, const void* wg, con
                           int E, int k, int32_t* ids, float* w, float* prob, int8_t* xq, float* xs, int32_t* whist,
                           hipStream_t s) {
   const dim3 grid((unsigned)((T + p.bt - 1) / p.bt));
-  if (xq)
-    route_fused_kernel<true, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H, E,
-                                                             k, ids, w, prob, xq, xs, whist);
-  else
-    route_fused_kernel<false, KQ, NSUB><<<grid, 1024, 0, s>>>((const uint16_t*)x, (const uint16_t*)wg, bias, T, H,
-                                                              E, k, ids, w, prob, xq, xs, whist);
+  const uint16_t *xb = (const uint16_t*)x, *wb = (const uint16_t*)wg;
+  if (p.nw == 8) {
+    // two workgroups per CU: at most 64 KiB of stages each
+    if (xq)
+      route_fused_kernel<true, KQ, NSUB, 8, 64 * 1024><<<grid, 512, 0, s>>>(xb, wb, bias, T, H, E, k, ids, w, prob,
+                                                                           xq, xs, whist);
+    else
+      route_fused_kernel<false, KQ, NSUB, 8, 64 * 1024><<<grid, 512, 0, s>>>(xb, wb, bias, T, H, E, k, ids, w, prob,
+                                                                            xq, xs, whist);
+  } else {
+    if (xq)
+      route_fused_kernel<true, KQ, NSUB, 16, 128 * 1024><<<grid, 1024, 0, s>>>(xb, wb, bias, T, H, E, k, ids, w,
+                                                                              prob, xq, xs, whist);
+    else
+      route_fused_kernel<false, KQ, NSUB, 16, 128 * 1024><<<grid, 1024, 0, s>>>(xb, wb, bias, T, H, E, k, ids, w,
+                                                                               prob, xq, xs, whist);
+  }
   return hipGetLastError();
 }
 

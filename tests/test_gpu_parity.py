@@ -155,14 +155,16 @@ ROUTE_PATHS = [
     (moe_synth.Spec("fma_tb16_many", 16411, 256, 8, 2, 64), True, "tokens/wg=16,"),
     # E <= 64, large batches: the fused kernel (logits on chip, x read once),
     # two parts of H (H <= 1024: 2, 4, 8 or 16 substeps per wave), four
-    # (H = 2048) and eight (H = 4096), ragged last token block, bias, codes
+    # (H = 2048) and eight (H = 4096), ragged last token block, bias, codes;
+    # 8-wave workgroups (64 or 32 tokens) for two or four parts, 16 waves (32
+    # tokens) for eight
     (moe_synth.Spec("e64_ragged_bias", 130 * 64 + 37, 256, 64, 6, 64, zipf_s=1.1), True,
-     "route_fused_kernel(tokens/wg=128,parts=2)"),
+     "route_fused_kernel(tokens/wg=64,parts=2)"),
     (moe_synth.Spec("e32_many_tokens", 128 * 64 + 1, 128, 32, 3, 64), False,
-     "route_fused_kernel(tokens/wg=128,parts=2)"),
-    (moe_synth.Spec("fused_e32_h512", 8200, 512, 32, 3, 64), False, "route_fused_kernel(tokens/wg=128,parts=2)"),
+     "route_fused_kernel(tokens/wg=64,parts=2)"),
+    (moe_synth.Spec("fused_e32_h512", 8200, 512, 32, 3, 64), False, "route_fused_kernel(tokens/wg=64,parts=2)"),
     (moe_synth.Spec("fused_e64_h2048_codes", 16384 + 77, 2048, 64, 6, 64, zipf_s=1.1), True,
-     "route_fused_kernel(tokens/wg=64,parts=4)"),
+     "route_fused_kernel(tokens/wg=32,parts=4)"),
     (moe_synth.Spec("fused_e48_h4096_codes", 2085, 4096, 48, 4, 64), True,
      "route_fused_kernel(tokens/wg=32,parts=8)"),
     (moe_synth.Spec("fused_e64_h4096", 2048, 4096, 64, 8, 64), False, "route_fused_kernel(tokens/wg=32,parts=8)"),
@@ -180,7 +182,7 @@ ROUTE_PATHS = [
     (moe_synth.Spec("big_e256_codes", 4096 + 37, 512, 256, 8, 64), True,
      "tokens/wg=128,experts/wg=128,ksplit=4)"),
     (moe_synth.Spec("big_e64_codes", 16384 + 5, 1024, 64, 6, 64, zipf_s=1.1), True,
-     "route_fused_kernel(tokens/wg=128,parts=2)"),
+     "route_fused_kernel(tokens/wg=64,parts=2)"),
     (moe_synth.Spec("big_e80", 8300, 256, 80, 4, 64), False, "tokens/wg=64,experts/wg=64,ksplit=1)"),
 ]
 
