@@ -852,8 +852,9 @@ __global__ __launch_bounds__(NWV * 64) void route_topk_kernel(
 // E <= 64, bf16: gate, softmax and top-k (and, with quantisation, the int8
 // codes) in one kernel, with the logits on chip and x read from memory once.
 // A workgroup of NW waves (16, or 8 so that two share a CU) takes
-// BM = 16 NW / KQ tokens and every expert over all of H.  Wave (tb, q) owns tokens [16 tb, 16 tb + 16) of the block and
-// the q-th of KQ contiguous parts of H.  It loads its whole x slice straight
+// BM = 16 NW / KQ tokens and every expert over all of H.  Wave (tb, q) owns
+// tokens [16 tb, 16 tb + 16) of the block and the q-th of KQ contiguous parts
+// of H.  It loads its whole x slice straight
 // into registers, all loads issued at once, laid out as the A operand of MFMA
 // 16x16x32 bf16 (row = lane % 16, eight K values at 8 (lane / 16) of each
 // 32-value substep); the same registers give the int8 codes, made a few
