@@ -106,16 +106,31 @@ def test_fused_router_loop_never_drains_all_copies(tmp_path):
     assert r.returncode == 0, r.stderr[-3000:]
     text = out.read_text()
     names = re.findall(r"^(_ZN3moe12_GLOBAL__N_118route_fused_kernel\w+):", text, re.M)
-    assert len(names) == 12, names
+    # six (parts, substeps) shapes, with and without codes, in 8- and 16-wave workgroups
+    assert len(names) == 24, names
     for name in names:
         a = text.index(name + ":")
         b = text.index(".Lfunc_end", a)
         body = text[a:b]
+        # the kernel's stage count S, from its template arguments as the kernel
+        # derives it (<QUANT, KQ, NSUB, NW, LDSB>)
+        kq, nsub, nw, ldsb = map(int, re.search(r"route_fused_kernelILb[01]ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E",
+                                                name).groups())
+        rb = 64 if kq >= 8 else 128
+        nst = nsub // (rb // 64)
+        smax = ldsb // (64 * kq * rb)
+        stages = max(nst + 1, 2) if nst + 1 < smax else smax
         # the loop is unrolled: every wait from the first barrier to the last
         # MFMA, except the final stage's, leaves later copies in flight (before
         # the first barrier the codes variants publish the row maxima to LDS,
-        # and the compiler drains the prefetched stages once for that write)
+        # and the compiler drains the prefetched stages once for that write).
+        # With two stages the copy in flight at a stage's wait is that stage's
+        # own, so every wait is vmcnt(0) by design: there, no more than one
+        # wait per stage.
         first = body.index("s_barrier")
         last = body.rindex("v_mfma")
         waits = re.findall(r"s_waitcnt vmcnt\((\d+)\)", body[first:last])
-        assert all(int(w) > 0 for w in waits[:-1]), (name, waits)
+        if stages == 2:
+            assert len(waits) <= nst, (name, waits)
+        else:
+            assert all(int(w) > 0 for w in waits[:-1]), (name, waits)
